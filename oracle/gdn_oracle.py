@@ -1,0 +1,396 @@
+"""Plain, slow fp64 definition of tree-structured GDN speculative verification.
+
+TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.  It shares no code
+with the HIP library and imports nothing from it.
+
+What is computed, and where it is defined
+-----------------------------------------
+* The gated delta rule, one decode step (GDN's update, as TreeWY's abstract and
+  "Background" describe GDN layers: a fixed-size recurrent state per head)::
+
+      alpha = exp(g);   u = beta * (v - alpha * S k);   S' = alpha * S + u k^T;   o = S' q
+
+  S is the d_v x d_k state in math orientation; the device stores it
+  transposed, H = S^T, as [d_k][d_v].  ``u`` is the pseudo-value with beta
+  folded in: the new value minus what the decayed preceding state already
+  predicts for this key (TreeWY, "Method").
+* Tree semantics (GDN Tree-Scan, English abstract): every draft node's row
+  must see the recurrent state that plain sequential decode produces along its
+  root-to-node path.  The oracle therefore walks nodes in parent-before-child
+  order (TreeWY, "Method") and applies the step to the parent's state; a node
+  with parent -1 starts from the committed state S0.  Nothing is shared between
+  branches except common ancestors (TreeWY, "Method": a branch refers to its
+  common ancestors, never to the other branch).
+* Commit (TreeWY, "Method" and "Novelty"; Tree-Scan: accepted-chain-only state
+  publication): the next committed state is the sequential state at the last
+  node of the accepted root-first path; an empty path keeps S0.
+* storeall (TreeWY, "Prior work": vLLM's default keeps the committed state and
+  one state per candidate position and selects the accepted one): node_state[t]
+  is the state after node t, and its commit copies the accepted node's state.
+
+There is no blocking, reordering or algebraic rewrite here: the tree-WY
+identities that the HIP kernels use are checked against this file, not used
+by it.
+
+Parity status of each function: see the module-level ``PINS`` table.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "STATUS_OK", "STATUS_BAD_OFFSETS", "STATUS_TOO_MANY_NODES", "STATUS_BAD_PARENT",
+    "STATUS_BAD_PATH", "STATUS_BAD_ACCEPT", "MAX_NODES",
+    "parents_valid", "ancestry", "depths", "root_to_node", "accepted_path", "gated_delta_step",
+    "verify_unit", "commit_unit", "replay_commit_unit", "verify_request", "verify_batch",
+    "commit_batch", "accepted_path_batch", "verify_storeall_batch", "commit_storeall_batch",
+    "state_bytes", "PINS",
+]
+
+# Status codes written per request.  These numbers are part of the C-ABI's
+# interface (its header lists the same values), not shared code.
+STATUS_OK = 0
+STATUS_BAD_OFFSETS = 1      # node_offset not monotone or beyond T
+STATUS_TOO_MANY_NODES = 2   # N_b > max_nodes (or > 64)
+STATUS_BAD_PARENT = 3       # parent[t] >= t or < -1
+STATUS_BAD_PATH = 4         # path is not a root-first chain of the request's tree
+STATUS_BAD_ACCEPT = 5       # accept_node outside [-1, N_b)
+
+MAX_NODES = 64
+
+# Which independent check pins each function (tests/test_oracle_pins.py).
+PINS = {
+    "ancestry": "brute-force parent walk; chain closed form; pages' two-branch example",
+    "depths": "equals popcount of ancestry; chain closed form",
+    "accepted_path": "chain structure (root parent -1, consecutive parents, ends at node)",
+    "gated_delta_step": "finite-difference gradient of the least-squares loss; delta-rule "
+                        "write property; orthogonal-complement decay; alpha=0 and beta=0 "
+                        "closed forms; storage-layout definition",
+    "verify_unit": "brute-force replay of every root-to-node path; sibling invariance; "
+                   "relabelling; independent tree-WY triangular-solve formulation",
+    "commit_unit": "equals the accepted node's sequential state; empty path keeps S0; "
+                   "verify-then-commit composition",
+    "verify_storeall_batch": "node states equal the per-path sequential states; state count "
+                             "of a depth-3 chain is 4 including S0 (TreeWY, Prior work)",
+}
+
+
+# ----------------------------------------------------------------------------
+# tree structure
+# ----------------------------------------------------------------------------
+
+def parents_valid(parent: Sequence[int]) -> bool:
+    """Parent-before-child order: every parent index is -1 or an earlier node."""
+    return all(-1 <= int(p) < i for i, p in enumerate(parent))
+
+
+def ancestry(parent: Sequence[int]) -> List[int]:
+    """Inclusive ancestor set of each node as a bitmask (bit j = node j).
+
+    anc(t) = anc(parent(t)) | {t}, with anc(-1) empty (TreeWY, "Method";
+    Tree-Scan's ancestry mask).  Requires a valid parent array.
+    """
+    anc: List[int] = []
+    for t, p in enumerate(parent):
+        p = int(p)
+        anc.append((anc[p] if p >= 0 else 0) | (1 << t))
+    return anc
+
+
+def depths(parent: Sequence[int]) -> List[int]:
+    """Depth of each node; a node attached to S0 has depth 1."""
+    out: List[int] = []
+    for p in parent:
+        p = int(p)
+        out.append(1 if p < 0 else out[p] + 1)
+    return out
+
+
+def root_to_node(parent: Sequence[int], t: int) -> List[int]:
+    """The node indices from the S0-attached root down to t, inclusive."""
+    path = []
+    while t >= 0:
+        path.append(t)
+        t = int(parent[t])
+    return path[::-1]
+
+
+def accepted_path(parent: Sequence[int], accept_node: int) -> List[int]:
+    """Root-first accepted path ending at accept_node; [] when none is accepted."""
+    if accept_node < 0:
+        return []
+    return root_to_node(parent, accept_node)
+
+
+# ----------------------------------------------------------------------------
+# the sequential rule
+# ----------------------------------------------------------------------------
+
+def gated_delta_step(S: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                     g: float, beta: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One gated-delta-rule decode step in fp64.
+
+    S is d_v x d_k (math orientation).  Returns (S_new, u, o) where u is the
+    pseudo-value (beta folded in) and o the output read from the updated state.
+    """
+    alpha = math.exp(float(g))
+    u = float(beta) * (v - alpha * (S @ k))
+    S_new = alpha * S + np.outer(u, k)
+    o = S_new @ q
+    return S_new, u, o
+
+
+def verify_unit(H0: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                g: np.ndarray, beta: np.ndarray, parent: Sequence[int]):
+    """One (request, v-head) unit.
+
+    H0: [d_k][d_v] stored state.  q, k: [N][d_k]; v: [N][d_v]; g, beta: [N].
+    Returns (O [N][d_v], U [N][d_v], states) where states[t] is the math-
+    orientation state after node t.
+    """
+    S_root = np.ascontiguousarray(np.asarray(H0, np.float64).T)
+    N = len(parent)
+    dv = S_root.shape[0]
+    O = np.zeros((N, dv))
+    U = np.zeros((N, dv))
+    states: List[np.ndarray] = []
+    for t in range(N):
+        p = int(parent[t])
+        P = S_root if p < 0 else states[p]
+        S_t, u_t, o_t = gated_delta_step(P, q[t], k[t], v[t], g[t], beta[t])
+        states.append(S_t)
+        U[t] = u_t
+        O[t] = o_t
+    return O, U, states
+
+
+def commit_unit(H0: np.ndarray, states: List[np.ndarray], path: Sequence[int]) -> np.ndarray:
+    """Next committed state in storage orientation: the accepted node's state,
+    or S0 unchanged when the path is empty."""
+    if len(path) == 0:
+        return np.asarray(H0, np.float64).copy()
+    return states[int(path[-1])].T.copy()
+
+
+def replay_commit_unit(H0, q, k, v, g, beta, path: Sequence[int]) -> np.ndarray:
+    """Committed state by replaying the accepted path from S0 with the
+    sequential rule (ReplaySSM / Tree-Scan's branch replay).  Storage orientation."""
+    S = np.ascontiguousarray(np.asarray(H0, np.float64).T)
+    for t in path:
+        S, _, _ = gated_delta_step(S, q[t], k[t], v[t], g[t], beta[t])
+    return S.T.copy()
+
+
+# ----------------------------------------------------------------------------
+# batch wrappers mirroring the C-ABI layouts
+# ----------------------------------------------------------------------------
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def _request_status(node_offset, b, T, max_nodes, parent) -> int:
+    lo, hi = int(node_offset[b]), int(node_offset[b + 1])
+    if lo < 0 or hi < lo or hi > T:
+        return STATUS_BAD_OFFSETS
+    if hi - lo > min(max_nodes, MAX_NODES):
+        return STATUS_TOO_MANY_NODES
+    if not parents_valid(parent[lo:hi]):
+        return STATUS_BAD_PARENT
+    return STATUS_OK
+
+
+def verify_request(S0, q, k, v, g, beta, node_offset, parent, b: int, Hv: int, Hk: int,
+                   max_nodes: int = MAX_NODES, state_slot=None, heads=None):
+    """All v-heads (or the listed ones) of request b.
+
+    Returns (status, O [N][Hv][d], U [N][Hv][d], anc list, states) where
+    states[h] is the list of node states of head h (math orientation).
+    Arrays are float64 views of the device inputs (q, k, v already widened).
+    """
+    T = len(parent)
+    st = _request_status(node_offset, b, T, max_nodes, parent)
+    lo, hi = int(node_offset[b]), int(node_offset[b + 1])
+    if st != STATUS_OK:
+        return st, None, None, None, None
+    par = [int(p) for p in parent[lo:hi]]
+    N = hi - lo
+    d_v = S0.shape[-1]
+    r = Hv // Hk
+    slot = b if state_slot is None else int(state_slot[b])
+    O = np.zeros((N, Hv, d_v))
+    U = np.zeros((N, Hv, d_v))
+    states = {}
+    for h in (range(Hv) if heads is None else heads):
+        hk = h // r
+        o, u, s = verify_unit(_f64(S0[slot, h]), q[lo:hi, hk], k[lo:hi, hk], v[lo:hi, h],
+                              _f64(g[lo:hi, h]), _f64(beta[lo:hi, h]), par)
+        O[:, h] = o
+        U[:, h] = u
+        states[h] = s
+    return st, O, U, ancestry(par), states
+
+
+def verify_batch(S0, q, k, v, g, beta, node_offset, parent, Hv: int, Hk: int,
+                 max_nodes: int = MAX_NODES, state_slot=None):
+    """Whole batch: (O [T][Hv][d], U [T][Hv][d], anc uint64 [T], status int32 [B]).
+
+    A request whose status is nonzero gets NaN rows in O and U and zero
+    ancestry masks (when its rows are addressable at all).
+    """
+    T = len(parent)
+    B = len(node_offset) - 1
+    d_v = S0.shape[-1]
+    O = np.zeros((T, Hv, d_v))
+    U = np.zeros((T, Hv, d_v))
+    anc = np.zeros(T, dtype=np.uint64)
+    status = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        st, Ob, Ub, ab, _ = verify_request(S0, q, k, v, g, beta, node_offset, parent, b, Hv, Hk,
+                                           max_nodes, state_slot)
+        status[b] = st
+        lo, hi = int(node_offset[b]), int(node_offset[b + 1])
+        if st == STATUS_OK:
+            O[lo:hi] = Ob
+            U[lo:hi] = Ub
+            anc[lo:hi] = np.array(ab, dtype=np.uint64)
+        elif st != STATUS_BAD_OFFSETS:
+            O[lo:hi] = np.nan
+            U[lo:hi] = np.nan
+    return O, U, anc, status
+
+
+def _path_status(parent_local: Sequence[int], path: Sequence[int]) -> int:
+    N = len(parent_local)
+    if len(path) > N:
+        return STATUS_BAD_PATH
+    prev = -1
+    for t in path:
+        t = int(t)
+        if t < 0 or t >= N or int(parent_local[t]) != prev:
+            return STATUS_BAD_PATH
+        prev = t
+    return STATUS_OK
+
+
+def commit_batch(S0, q, k, v, g, beta, node_offset, parent, path, path_len, Hv: int, Hk: int,
+                 max_nodes: int = MAX_NODES, state_slot=None, requests=None):
+    """Committed states by definition: the sequential state at each request's
+    accepted node, S0 for an empty path or an invalid request.
+
+    path: int32 [B][max_nodes] root-first; path_len: int32 [B].
+    Returns (S_out [B or len(requests)][Hv][d_k][d_v] in storage orientation,
+    status [same]).  S_out is indexed by request, not by slot.
+    """
+    B = len(node_offset) - 1
+    reqs = range(B) if requests is None else list(requests)
+    d = S0.shape[-1]
+    out = np.zeros((len(reqs), Hv, d, d))
+    status = np.zeros(len(reqs), dtype=np.int32)
+    T = len(parent)
+    for i, b in enumerate(reqs):
+        slot = b if state_slot is None else int(state_slot[b])
+        st = _request_status(node_offset, b, T, max_nodes, parent)
+        L = int(path_len[b])
+        lo, hi = int(node_offset[b]), int(node_offset[b + 1])
+        if st == STATUS_OK:
+            if L < 0 or L > max_nodes:
+                st = STATUS_BAD_PATH
+            else:
+                st = _path_status(parent[lo:hi], path[b][:L])
+        status[i] = st
+        if st != STATUS_OK or L == 0:
+            out[i] = _f64(S0[slot])
+            continue
+        pth = [int(t) for t in path[b][:L]]
+        r = Hv // Hk
+        for h in range(Hv):
+            hk = h // r
+            out[i, h] = replay_commit_unit(_f64(S0[slot, h]), q[lo:hi, hk], k[lo:hi, hk],
+                                           v[lo:hi, h], _f64(g[lo:hi, h]), _f64(beta[lo:hi, h]), pth)
+    return out, status
+
+
+def accepted_path_batch(node_offset, parent, accept_node, max_nodes: int = MAX_NODES):
+    """(path int32 [B][max_nodes] root-first, zero-filled; path_len [B]; status [B])."""
+    B = len(node_offset) - 1
+    T = len(parent)
+    path = np.zeros((B, max_nodes), dtype=np.int32)
+    plen = np.zeros(B, dtype=np.int32)
+    status = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        st = _request_status(node_offset, b, T, max_nodes, parent)
+        lo, hi = int(node_offset[b]), int(node_offset[b + 1])
+        a = int(accept_node[b])
+        if st == STATUS_OK and not (-1 <= a < hi - lo):
+            st = STATUS_BAD_ACCEPT
+        status[b] = st
+        if st != STATUS_OK:
+            continue
+        p = accepted_path(parent[lo:hi], a)
+        plen[b] = len(p)
+        path[b, :len(p)] = p
+    return path, plen, status
+
+
+def verify_storeall_batch(S0, q, k, v, g, beta, node_offset, parent, Hv: int, Hk: int,
+                          max_nodes: int = MAX_NODES, state_slot=None, requests=None):
+    """storeall: (O, node_state [T][Hv][d_k][d_v] storage orientation, status).
+
+    With ``requests`` only those requests are evaluated (others left zero).
+    """
+    T = len(parent)
+    B = len(node_offset) - 1
+    d = S0.shape[-1]
+    O = np.zeros((T, Hv, d))
+    NS = np.zeros((T, Hv, d, d))
+    status = np.zeros(B, dtype=np.int32)
+    for b in (range(B) if requests is None else requests):
+        st, Ob, _, _, states = verify_request(S0, q, k, v, g, beta, node_offset, parent, b, Hv, Hk,
+                                              max_nodes, state_slot)
+        status[b] = st
+        lo, hi = int(node_offset[b]), int(node_offset[b + 1])
+        if st == STATUS_OK:
+            O[lo:hi] = Ob
+            for h, sl in states.items():
+                for t, S in enumerate(sl):
+                    NS[lo + t, h] = S.T
+        elif st != STATUS_BAD_OFFSETS:
+            O[lo:hi] = np.nan
+    return O, NS, status
+
+
+def commit_storeall_batch(S0, node_state, node_offset, parent, accept_node, max_nodes: int = MAX_NODES,
+                          state_slot=None):
+    """storeall commit: copy the accepted node's stored state (S0 when none)."""
+    B = len(node_offset) - 1
+    T = len(parent)
+    out = np.zeros((B,) + S0.shape[1:])
+    status = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        slot = b if state_slot is None else int(state_slot[b])
+        st = _request_status(node_offset, b, T, max_nodes, parent)
+        lo, hi = int(node_offset[b]), int(node_offset[b + 1])
+        a = int(accept_node[b])
+        if st == STATUS_OK and not (-1 <= a < hi - lo):
+            st = STATUS_BAD_ACCEPT
+        status[b] = st
+        out[b] = _f64(S0[slot]) if (st != STATUS_OK or a < 0) else _f64(node_state[lo + a])
+    return out, status
+
+
+def state_bytes(B: int, Hv: int, d_k: int, d_v: int, T: int, storeall: bool) -> int:
+    """Speculative recurrent-state memory of one layer, excluding S0.
+
+    storeall keeps one fp32 d_k x d_v state per (node, head) (TreeWY, "Prior
+    work"); the tree-WY path keeps the fp32 pseudo-value matrix U, one d_v row
+    per (node, head) (TreeWY, "Novelty": a small pseudo-value matrix instead of
+    per-node states).
+    """
+    if storeall:
+        return T * Hv * d_k * d_v * 4
+    return T * Hv * d_v * 4
