@@ -1,0 +1,204 @@
+/*
+ * gdn_tree.h -- C ABI of the tree-structured Gated DeltaNet speculative
+ * verification library (libgdn_tree.so, gfx950 / MI355X).
+ *
+ * What the library computes
+ * -------------------------
+ * A Gated DeltaNet layer keeps, per value head, a fixed-size recurrent state
+ * S (d_v x d_k) and advances it one token at a time with the gated delta rule
+ *
+ *     alpha_t = exp(g_t)
+ *     u_t     = beta_t * (v_t - alpha_t * S_{t-1} k_t)      (pseudo-value)
+ *     S_t     = alpha_t * S_{t-1} + u_t k_t^T,    o_t = S_t q_t
+ *
+ * (TreeWY, arXiv 2608.20961: "Background" and "Method"; the pseudo-value is
+ * the new value minus what the decayed preceding state already predicts).
+ * For tree speculative decoding, every draft node must see the state that
+ * sequential decode would produce along its root-to-node path (GDN Tree-Scan,
+ * arXiv 2609.23900, abstract).  gdn_tree_verify computes every node's output
+ * and pseudo-value at once from the committed state S0 with an ancestor-masked
+ * unit-lower-triangular solve (TreeWY, "Method" and "Novelty": tree-structured
+ * WY transform, one triangular system, parent-before-child order).
+ * gdn_tree_commit rebuilds only the accepted path's state from the same
+ * pseudo-values (TreeWY, "Novelty": one full state is restored for the
+ * accepted path; Tree-Scan: accepted-chain-only state publication).  The
+ * *_storeall entry points are the snapshot-per-node scheme kept for
+ * comparison (TreeWY, "Prior work": vLLM's storeall saves the committed state
+ * plus one state per candidate position and selects the accepted one).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer except `dims` is a DEVICE pointer (HIP device memory of the
+ *   current device) unless stated otherwise.  The caller owns all buffers;
+ *   the library never allocates, frees or synchronises.  Each call enqueues
+ *   kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ * - Only d_k = d_v = 128 is compiled.  Smaller heads run zero-padded to 128,
+ *   which is exact (padded coordinates never interact).
+ * - Layouts are dense row-major:
+ *     S0, S_out   float32 [n_slots][Hv][d_k][d_v]: the state stored transposed
+ *                 (H = S^T): row i holds what the state returns for key e_i.
+ *     state_slot  int32 [B]: slot of request b in S0/S_out; NULL = slot b.
+ *     q, k        bfloat16 bit patterns (uint16) [T][Hk][d_k]
+ *     v           bfloat16 bit patterns [T][Hv][d_v]
+ *     g, beta     float32 [T][Hv]: log-decay g <= 0 (alpha = exp(g)) and beta
+ *     node_offset int32 [B+1]: request b owns node rows node_offset[b] ..
+ *                 node_offset[b+1]-1; node_offset[B] must equal T
+ *     parent      int32 [T]: request-local parent index, -1 = attached to S0;
+ *                 parent[t] < t (parent-before-child; a forest is allowed)
+ *     out, U      float32 [T][Hv][d_v]: node outputs and pseudo-values
+ *                 (beta folded into U)
+ *     anc_mask    uint64 [T]: inclusive ancestor bitset, bit j = request-local
+ *                 node j
+ *     path        int32 [B][max_nodes]: root-first request-local node indices
+ *     path_len    int32 [B]: 0 = nothing accepted
+ *     accept_node int32 [B]: last accepted node, -1 = none
+ *     node_state  float32 [T][Hv][d_k][d_v] (storeall only)
+ *     status      int32 [B] (optional, may be NULL): per-request device status
+ * - S0, S_out, q, k, v, out, U and node_state must be 16-byte aligned (the
+ *   kernels move them in 16-byte vectors); other arrays need natural alignment.
+ * - v-head h reads key head h / (Hv / Hk) (grouped-query heads).
+ * - Return value: 0 = enqueued; a negative GDN_TREE_E_* code = rejected on
+ *   the host and NOTHING was enqueued.  Problems only visible on the device
+ *   are reported per request in status[b] (GDN_TREE_S_*); the documented
+ *   fallback output is written for that request instead.
+ */
+#ifndef GDN_TREE_H
+#define GDN_TREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_TREE_ABI_VERSION 1
+#define GDN_TREE_MAX_NODES 64   /* per request: one wave64 lane and one uint64 bit per node */
+#define GDN_TREE_HEAD_DIM 128
+
+/* host-side return codes (nothing enqueued) */
+#define GDN_TREE_OK 0
+#define GDN_TREE_E_NULL (-1)      /* a required pointer is NULL */
+#define GDN_TREE_E_DIMS (-2)      /* B, T, Hv, Hk, n_slots out of range or Hv % Hk != 0 */
+#define GDN_TREE_E_HEAD_DIM (-3)  /* d_k or d_v is not 128 */
+#define GDN_TREE_E_MAX_NODES (-4) /* max_nodes < 1 or > 64 */
+#define GDN_TREE_E_LAUNCH (-5)    /* the HIP runtime refused the launch */
+#define GDN_TREE_E_SIZE (-6)      /* a buffer would exceed 2^62 bytes */
+#define GDN_TREE_E_ALIGN (-7)     /* a state / q / k / v / out / U / node_state pointer is not 16-byte aligned */
+
+/* device-side per-request status codes (status[b]) */
+#define GDN_TREE_S_OK 0
+#define GDN_TREE_S_BAD_OFFSETS 1  /* node_offset[b] < 0, decreasing, or node_offset[b+1] > T */
+#define GDN_TREE_S_TOO_MANY 2     /* request has more than max_nodes nodes */
+#define GDN_TREE_S_BAD_PARENT 3   /* some parent[t] >= t or < -1 */
+#define GDN_TREE_S_BAD_PATH 4     /* path is not a root-first chain of the tree, or path_len out of range */
+#define GDN_TREE_S_BAD_ACCEPT 5   /* accept_node outside [-1, N_b) */
+#define GDN_TREE_S_BAD_SLOT 6     /* state_slot[b] outside [0, n_slots) */
+
+typedef struct gdn_tree_dims {
+    int32_t B;         /* requests in the batch (>= 0) */
+    int32_t Hv;        /* value heads (>= 1) */
+    int32_t Hk;        /* key heads (>= 1, divides Hv) */
+    int32_t d_k;       /* key head dim, must be 128 */
+    int32_t d_v;       /* value head dim, must be 128 */
+    int32_t T;         /* total draft nodes = node_offset[B] (>= 0) */
+    int32_t max_nodes; /* per-request node cap and row stride of path[] (1..64) */
+    int32_t n_slots;   /* slots in S0 / S_out (>= 1 when B > 0) */
+} gdn_tree_dims;
+
+/*
+ * gdn_tree_verify -- outputs and pseudo-values of every draft node.
+ *
+ * For each request b and v-head h, with anc*(t) the inclusive ancestors of t,
+ * G_t the sum of g over anc*(t), gamma_t = exp(G_t) and D_tj = exp(G_t - G_j):
+ *   U solves  u_t + beta_t * sum_{j in anc(t)} D_tj (k_t.k_j) u_j
+ *                 = beta_t * (v_t - gamma_t * S0 k_t)
+ *   out_t = gamma_t * S0 q_t + sum_{j in anc*(t)} D_tj (q_t.k_j) u_j
+ * which equals sequential decode along each root-to-node path (TreeWY,
+ * "Method"; Tree-Scan, abstract).  No per-node state is materialised.
+ *
+ * Reads S0, state_slot, q, k, v, g, beta, node_offset, parent; writes out, U,
+ * anc_mask (if non-NULL) and status (if non-NULL).  state_slot, anc_mask and
+ * status may be NULL; q, k, v, g, beta, parent, out, U may be NULL when T == 0.
+ * Device errors: a request with bad offsets is skipped (status 1); a request
+ * with too many nodes or a bad parent array gets NaN rows in out and U and
+ * zero ancestry masks (status 2 / 3); a bad slot gives NaN rows (status 6).
+ */
+int gdn_tree_verify(const gdn_tree_dims *dims, const float *S0, const int32_t *state_slot,
+                    const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                    const float *beta, const int32_t *node_offset, const int32_t *parent,
+                    float *out, float *U, uint64_t *anc_mask, int32_t *status, void *stream);
+
+/*
+ * gdn_tree_commit -- the next committed state from the accepted path only.
+ *
+ * For the root-first path p_1..p_L ending at node a (L = path_len[b]):
+ *   S_out = gamma_a * S0 + sum_{j in path} D_aj u_j k_j^T     (stored transposed)
+ * i.e. the sequential state at node a (TreeWY, "Method": only the accepted
+ * path's pseudo-values are composed into the next committed state).  L = 0
+ * copies S0 bit-exactly.  S_out may alias S0 (in-place commit).  U must be the
+ * pseudo-values gdn_tree_verify produced for the same inputs.
+ * Device errors: an invalid path (status 4) or an invalid request (1..3) makes
+ * S_out[slot] a copy of S0[slot]; a bad slot (6) writes nothing.
+ */
+int gdn_tree_commit(const gdn_tree_dims *dims, const float *S0, float *S_out,
+                    const int32_t *state_slot, const float *U, const uint16_t *k, const float *g,
+                    const int32_t *node_offset, const int32_t *parent, const int32_t *path,
+                    const int32_t *path_len, int32_t *status, void *stream);
+
+/*
+ * gdn_tree_accepted_path -- root-first path from each request's accepted node.
+ *
+ * path[b][0..L) = the nodes from the S0-attached root down to accept_node[b]
+ * (Tree-Scan: accepted chain), path_len[b] = L; the rest of the row is zeroed.
+ * accept_node[b] = -1 gives L = 0.  Device errors (status 1..3, 5) give L = 0.
+ */
+int gdn_tree_accepted_path(const gdn_tree_dims *dims, const int32_t *node_offset,
+                           const int32_t *parent, const int32_t *accept_node, int32_t *path,
+                           int32_t *path_len, int32_t *status, void *stream);
+
+/*
+ * gdn_tree_verify_storeall -- the snapshot-per-node comparison scheme.
+ *
+ * Walks each request's nodes in order with the sequential rule and writes
+ * every node's full state (TreeWY, "Prior work": storeall keeps one state per
+ * candidate position; a tree needs one per node):
+ *   node_state[t] = (alpha_t S_parent + u_t k_t^T)^T,   out_t = S_t q_t.
+ * Same inputs and error behaviour as gdn_tree_verify (NaN rows in out; the
+ * node states of a failed request are left unwritten).
+ */
+int gdn_tree_verify_storeall(const gdn_tree_dims *dims, const float *S0, const int32_t *state_slot,
+                             const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const float *g, const float *beta, const int32_t *node_offset,
+                             const int32_t *parent, float *out, float *node_state,
+                             int32_t *status, void *stream);
+
+/*
+ * gdn_tree_commit_storeall -- copy the accepted node's snapshot into S_out
+ * (S0 when accept_node[b] == -1).  S_out may alias S0.  Device errors (1..3,
+ * 5) copy S0; a bad slot (6) writes nothing.
+ */
+int gdn_tree_commit_storeall(const gdn_tree_dims *dims, const float *S0, float *S_out,
+                             const int32_t *state_slot, const float *node_state,
+                             const int32_t *node_offset, const int32_t *parent,
+                             const int32_t *accept_node, int32_t *status, void *stream);
+
+/*
+ * gdn_tree_state_bytes -- speculative recurrent-state bytes one layer holds
+ * beyond S0: storeall != 0 gives T*Hv*d_k*d_v*4 (one state per node and head),
+ * storeall == 0 gives the pseudo-value matrix U, T*Hv*d_v*4.  Host only; 0 on
+ * invalid dims.
+ */
+size_t gdn_tree_state_bytes(const gdn_tree_dims *dims, int storeall);
+
+/* Static description of a return or status code (host only, never NULL). */
+const char *gdn_tree_strerror(int code);
+
+/* GDN_TREE_ABI_VERSION of the built library (host only). */
+int gdn_tree_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_TREE_H */

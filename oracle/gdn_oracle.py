@@ -44,7 +44,7 @@ import numpy as np
 
 __all__ = [
     "STATUS_OK", "STATUS_BAD_OFFSETS", "STATUS_TOO_MANY_NODES", "STATUS_BAD_PARENT",
-    "STATUS_BAD_PATH", "STATUS_BAD_ACCEPT", "MAX_NODES",
+    "STATUS_BAD_PATH", "STATUS_BAD_ACCEPT", "STATUS_BAD_SLOT", "MAX_NODES",
     "parents_valid", "ancestry", "depths", "root_to_node", "accepted_path", "gated_delta_step",
     "verify_unit", "commit_unit", "replay_commit_unit", "verify_request", "verify_batch",
     "commit_batch", "accepted_path_batch", "verify_storeall_batch", "commit_storeall_batch",
@@ -59,6 +59,7 @@ STATUS_TOO_MANY_NODES = 2   # N_b > max_nodes (or > 64)
 STATUS_BAD_PARENT = 3       # parent[t] >= t or < -1
 STATUS_BAD_PATH = 4         # path is not a root-first chain of the request's tree
 STATUS_BAD_ACCEPT = 5       # accept_node outside [-1, N_b)
+STATUS_BAD_SLOT = 6         # state_slot[b] outside [0, n_slots)
 
 MAX_NODES = 64
 
@@ -193,7 +194,8 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _request_status(node_offset, b, T, max_nodes, parent) -> int:
+def _request_status(node_offset, b, T, max_nodes, parent, slot=0, n_slots=1) -> int:
+    """Checks in a fixed order: offsets, node count, parent order, state slot."""
     lo, hi = int(node_offset[b]), int(node_offset[b + 1])
     if lo < 0 or hi < lo or hi > T:
         return STATUS_BAD_OFFSETS
@@ -201,7 +203,13 @@ def _request_status(node_offset, b, T, max_nodes, parent) -> int:
         return STATUS_TOO_MANY_NODES
     if not parents_valid(parent[lo:hi]):
         return STATUS_BAD_PARENT
+    if not 0 <= slot < n_slots:
+        return STATUS_BAD_SLOT
     return STATUS_OK
+
+
+def _slot(state_slot, b):
+    return b if state_slot is None else int(state_slot[b])
 
 
 def verify_request(S0, q, k, v, g, beta, node_offset, parent, b: int, Hv: int, Hk: int,
@@ -213,7 +221,8 @@ def verify_request(S0, q, k, v, g, beta, node_offset, parent, b: int, Hv: int, H
     Arrays are float64 views of the device inputs (q, k, v already widened).
     """
     T = len(parent)
-    st = _request_status(node_offset, b, T, max_nodes, parent)
+    slot = _slot(state_slot, b)
+    st = _request_status(node_offset, b, T, max_nodes, parent, slot, S0.shape[0])
     lo, hi = int(node_offset[b]), int(node_offset[b + 1])
     if st != STATUS_OK:
         return st, None, None, None, None
@@ -221,7 +230,6 @@ def verify_request(S0, q, k, v, g, beta, node_offset, parent, b: int, Hv: int, H
     N = hi - lo
     d_v = S0.shape[-1]
     r = Hv // Hk
-    slot = b if state_slot is None else int(state_slot[b])
     O = np.zeros((N, Hv, d_v))
     U = np.zeros((N, Hv, d_v))
     states = {}
@@ -278,40 +286,42 @@ def _path_status(parent_local: Sequence[int], path: Sequence[int]) -> int:
 
 
 def commit_batch(S0, q, k, v, g, beta, node_offset, parent, path, path_len, Hv: int, Hk: int,
-                 max_nodes: int = MAX_NODES, state_slot=None, requests=None):
+                 max_nodes: int = MAX_NODES, state_slot=None, S_out_init=None, requests=None):
     """Committed states by definition: the sequential state at each request's
-    accepted node, S0 for an empty path or an invalid request.
+    accepted node, replayed from S0 along the accepted root-first path.
 
-    path: int32 [B][max_nodes] root-first; path_len: int32 [B].
-    Returns (S_out [B or len(requests)][Hv][d_k][d_v] in storage orientation,
-    status [same]).  S_out is indexed by request, not by slot.
+    path: int32 [B][max_nodes] root-first; path_len: int32 [B].  Returns
+    (S_out [n_slots][Hv][d_k][d_v] storage orientation, status [B]).  S_out
+    starts as a copy of S_out_init (default S0); an invalid request or path
+    writes a copy of S0 into its slot, a bad slot writes nothing.  With
+    ``requests``, only those requests are evaluated (others keep status 0).
     """
     B = len(node_offset) - 1
-    reqs = range(B) if requests is None else list(requests)
-    d = S0.shape[-1]
-    out = np.zeros((len(reqs), Hv, d, d))
-    status = np.zeros(len(reqs), dtype=np.int32)
+    out = np.array(S0 if S_out_init is None else S_out_init, dtype=np.float64, copy=True)
+    status = np.zeros(B, dtype=np.int32)
     T = len(parent)
-    for i, b in enumerate(reqs):
-        slot = b if state_slot is None else int(state_slot[b])
-        st = _request_status(node_offset, b, T, max_nodes, parent)
-        L = int(path_len[b])
+    r = Hv // Hk
+    for b in (range(B) if requests is None else requests):
+        slot = _slot(state_slot, b)
+        st = _request_status(node_offset, b, T, max_nodes, parent, slot, S0.shape[0])
+        L = int(path_len[b]) if st == STATUS_OK else 0
         lo, hi = int(node_offset[b]), int(node_offset[b + 1])
         if st == STATUS_OK:
             if L < 0 or L > max_nodes:
                 st = STATUS_BAD_PATH
             else:
                 st = _path_status(parent[lo:hi], path[b][:L])
-        status[i] = st
+        status[b] = st
+        if not 0 <= slot < S0.shape[0]:
+            continue
         if st != STATUS_OK or L == 0:
-            out[i] = _f64(S0[slot])
+            out[slot] = _f64(S0[slot])
             continue
         pth = [int(t) for t in path[b][:L]]
-        r = Hv // Hk
         for h in range(Hv):
             hk = h // r
-            out[i, h] = replay_commit_unit(_f64(S0[slot, h]), q[lo:hi, hk], k[lo:hi, hk],
-                                           v[lo:hi, h], _f64(g[lo:hi, h]), _f64(beta[lo:hi, h]), pth)
+            out[slot, h] = replay_commit_unit(_f64(S0[slot, h]), q[lo:hi, hk], k[lo:hi, hk],
+                                              v[lo:hi, h], _f64(g[lo:hi, h]), _f64(beta[lo:hi, h]), pth)
     return out, status
 
 
@@ -365,21 +375,25 @@ def verify_storeall_batch(S0, q, k, v, g, beta, node_offset, parent, Hv: int, Hk
 
 
 def commit_storeall_batch(S0, node_state, node_offset, parent, accept_node, max_nodes: int = MAX_NODES,
-                          state_slot=None):
-    """storeall commit: copy the accepted node's stored state (S0 when none)."""
+                          state_slot=None, S_out_init=None):
+    """storeall commit: copy the accepted node's stored state into the request's
+    slot (S0 when none is accepted or the request is invalid; nothing on a bad
+    slot).  Returns (S_out [n_slots]..., status [B])."""
     B = len(node_offset) - 1
     T = len(parent)
-    out = np.zeros((B,) + S0.shape[1:])
+    out = np.array(S0 if S_out_init is None else S_out_init, dtype=np.float64, copy=True)
     status = np.zeros(B, dtype=np.int32)
     for b in range(B):
-        slot = b if state_slot is None else int(state_slot[b])
-        st = _request_status(node_offset, b, T, max_nodes, parent)
+        slot = _slot(state_slot, b)
+        st = _request_status(node_offset, b, T, max_nodes, parent, slot, S0.shape[0])
         lo, hi = int(node_offset[b]), int(node_offset[b + 1])
         a = int(accept_node[b])
         if st == STATUS_OK and not (-1 <= a < hi - lo):
             st = STATUS_BAD_ACCEPT
         status[b] = st
-        out[b] = _f64(S0[slot]) if (st != STATUS_OK or a < 0) else _f64(node_state[lo + a])
+        if not 0 <= slot < S0.shape[0]:
+            continue
+        out[slot] = _f64(S0[slot]) if (st != STATUS_OK or a < 0) else _f64(node_state[lo + a])
     return out, status
 
 

@@ -1,0 +1,206 @@
+// Host side of the C ABI declared in include/gdn_tree.h: argument checks
+// (nothing is enqueued when one fails), then one launch per entry point on
+// the caller's stream.  The library holds no state, allocates nothing and
+// never synchronises.
+#include <limits.h>
+
+#include "common.h"
+#include "launch.h"
+
+using gdn::Args;
+
+namespace {
+
+// Dims shared by every entry point.  need_T: whether T > 0 is meaningful.
+int check_dims(const gdn_tree_dims *d) {
+    if (!d) return GDN_TREE_E_NULL;
+    if (d->B < 0 || d->T < 0) return GDN_TREE_E_DIMS;
+    if (d->B == 0) return GDN_TREE_OK;
+    if (d->Hv < 1 || d->Hk < 1 || d->Hv % d->Hk != 0 || d->n_slots < 1) return GDN_TREE_E_DIMS;
+    if (d->d_k != GDN_TREE_HEAD_DIM || d->d_v != GDN_TREE_HEAD_DIM) return GDN_TREE_E_HEAD_DIM;
+    if (d->max_nodes < 1 || d->max_nodes > GDN_TREE_MAX_NODES) return GDN_TREE_E_MAX_NODES;
+    // one workgroup per (request, v-head); indices are computed in 64-bit
+    const long long units = (long long)d->B * d->Hv;
+    if (units > (long long)INT_MAX - 8) return GDN_TREE_E_SIZE;
+    const long long state = (long long)GDN_TREE_HEAD_DIM * GDN_TREE_HEAD_DIM * 4;
+    if ((long long)d->n_slots * d->Hv > (1ll << 62) / state) return GDN_TREE_E_SIZE;
+    if ((long long)d->T * d->Hv > (1ll << 62) / state) return GDN_TREE_E_SIZE;
+    return GDN_TREE_OK;
+}
+
+Args base_args(const gdn_tree_dims *d) {
+    Args a = {};
+    a.B = d->B;
+    a.Hv = d->Hv;
+    a.Hk = d->Hk;
+    a.T = d->T;
+    a.max_nodes = d->max_nodes;
+    a.n_slots = d->n_slots;
+    return a;
+}
+
+bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+template <typename... Ps>
+bool any_misaligned(Ps... ps) {
+    return (misaligned((const void *)ps) || ...);
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? GDN_TREE_OK : GDN_TREE_E_LAUNCH; }
+
+// Clear an error left by earlier, unrelated work so that the check after our
+// launch reports our launch only.
+void clear_pending() { (void)hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+int gdn_tree_abi_version(void) { return GDN_TREE_ABI_VERSION; }
+
+const char *gdn_tree_strerror(int code) {
+    switch (code) {
+        case GDN_TREE_OK: return "ok";
+        case GDN_TREE_E_NULL: return "a required pointer is NULL";
+        case GDN_TREE_E_DIMS: return "dimensions out of range (B, T, Hv, Hk, n_slots; Hv must be a multiple of Hk)";
+        case GDN_TREE_E_HEAD_DIM: return "unsupported head dimension (only d_k = d_v = 128 is built)";
+        case GDN_TREE_E_MAX_NODES: return "max_nodes must be in 1..64";
+        case GDN_TREE_E_LAUNCH: return "kernel launch failed";
+        case GDN_TREE_E_SIZE: return "buffer or grid size out of range";
+        case GDN_TREE_E_ALIGN: return "state, q, k, v, out, U and node_state pointers must be 16-byte aligned";
+        case GDN_TREE_S_BAD_OFFSETS: return "status: node_offset out of order or beyond T";
+        case GDN_TREE_S_TOO_MANY: return "status: request has more than max_nodes nodes";
+        case GDN_TREE_S_BAD_PARENT: return "status: parent[t] must satisfy -1 <= parent[t] < t";
+        case GDN_TREE_S_BAD_PATH: return "status: path is not a root-first chain of the request's tree";
+        case GDN_TREE_S_BAD_ACCEPT: return "status: accept_node outside [-1, N_b)";
+        case GDN_TREE_S_BAD_SLOT: return "status: state_slot outside [0, n_slots)";
+        default: return "unknown gdn_tree code";
+    }
+}
+
+size_t gdn_tree_state_bytes(const gdn_tree_dims *dims, int storeall) {
+    if (check_dims(dims) != GDN_TREE_OK) return 0;
+    const size_t rows = (size_t)dims->T * (size_t)dims->Hv;
+    return storeall ? rows * (size_t)dims->d_k * (size_t)dims->d_v * 4u : rows * (size_t)dims->d_v * 4u;
+}
+
+int gdn_tree_verify(const gdn_tree_dims *dims, const float *S0, const int32_t *state_slot,
+                    const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                    const float *beta, const int32_t *node_offset, const int32_t *parent, float *out,
+                    float *U, uint64_t *anc_mask, int32_t *status, void *stream) {
+    int rc = check_dims(dims);
+    if (rc != GDN_TREE_OK || dims->B == 0) return rc;
+    if (!S0 || !node_offset) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && (!q || !k || !v || !g || !beta || !parent || !out || !U)) return GDN_TREE_E_NULL;
+    if (any_misaligned(S0, q, k, v, out, U)) return GDN_TREE_E_ALIGN;
+    Args a = base_args(dims);
+    a.S0 = S0;
+    a.state_slot = state_slot;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.node_offset = node_offset;
+    a.parent = parent;
+    a.out = out;
+    a.U = U;
+    a.anc_mask = anc_mask;
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_verify(a, (hipStream_t)stream));
+}
+
+int gdn_tree_commit(const gdn_tree_dims *dims, const float *S0, float *S_out, const int32_t *state_slot,
+                    const float *U, const uint16_t *k, const float *g, const int32_t *node_offset,
+                    const int32_t *parent, const int32_t *path, const int32_t *path_len, int32_t *status,
+                    void *stream) {
+    int rc = check_dims(dims);
+    if (rc != GDN_TREE_OK || dims->B == 0) return rc;
+    if (!S0 || !S_out || !node_offset || !path || !path_len) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && (!U || !k || !g || !parent)) return GDN_TREE_E_NULL;
+    if (any_misaligned(S0, S_out, U, k)) return GDN_TREE_E_ALIGN;
+    Args a = base_args(dims);
+    a.S0 = S0;
+    a.S_out = S_out;
+    a.state_slot = state_slot;
+    a.U = const_cast<float *>(U);
+    a.k = k;
+    a.g = g;
+    a.node_offset = node_offset;
+    a.parent = parent;
+    a.path = path;
+    a.path_len = path_len;
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_commit(a, (hipStream_t)stream));
+}
+
+int gdn_tree_accepted_path(const gdn_tree_dims *dims, const int32_t *node_offset, const int32_t *parent,
+                           const int32_t *accept_node, int32_t *path, int32_t *path_len, int32_t *status,
+                           void *stream) {
+    int rc = check_dims(dims);
+    if (rc != GDN_TREE_OK || dims->B == 0) return rc;
+    if (!node_offset || !accept_node || !path || !path_len) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && !parent) return GDN_TREE_E_NULL;
+    Args a = base_args(dims);
+    a.node_offset = node_offset;
+    a.parent = parent;
+    a.accept_node = accept_node;
+    a.path_out = path;
+    a.path_len_out = path_len;
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_accepted_path(a, (hipStream_t)stream));
+}
+
+int gdn_tree_verify_storeall(const gdn_tree_dims *dims, const float *S0, const int32_t *state_slot,
+                             const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                             const float *beta, const int32_t *node_offset, const int32_t *parent,
+                             float *out, float *node_state, int32_t *status, void *stream) {
+    int rc = check_dims(dims);
+    if (rc != GDN_TREE_OK || dims->B == 0) return rc;
+    if (!S0 || !node_offset) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && (!q || !k || !v || !g || !beta || !parent || !out || !node_state))
+        return GDN_TREE_E_NULL;
+    if (any_misaligned(S0, q, k, v, out, node_state)) return GDN_TREE_E_ALIGN;
+    Args a = base_args(dims);
+    a.S0 = S0;
+    a.state_slot = state_slot;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.node_offset = node_offset;
+    a.parent = parent;
+    a.out = out;
+    a.node_state = node_state;
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_verify_storeall(a, (hipStream_t)stream));
+}
+
+int gdn_tree_commit_storeall(const gdn_tree_dims *dims, const float *S0, float *S_out,
+                             const int32_t *state_slot, const float *node_state, const int32_t *node_offset,
+                             const int32_t *parent, const int32_t *accept_node, int32_t *status,
+                             void *stream) {
+    int rc = check_dims(dims);
+    if (rc != GDN_TREE_OK || dims->B == 0) return rc;
+    if (!S0 || !S_out || !node_offset || !accept_node) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && (!parent || !node_state)) return GDN_TREE_E_NULL;
+    if (any_misaligned(S0, S_out, node_state)) return GDN_TREE_E_ALIGN;
+    Args a = base_args(dims);
+    a.S0 = S0;
+    a.S_out = S_out;
+    a.state_slot = state_slot;
+    a.node_state_in = node_state;
+    a.node_offset = node_offset;
+    a.parent = parent;
+    a.accept_node = accept_node;
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_commit_storeall(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

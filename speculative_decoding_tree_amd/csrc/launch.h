@@ -1,0 +1,17 @@
+// Host-side launchers, one per kernel family.  Each enqueues on `stream`
+// and returns the hipError_t of the launch.  Arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace gdn {
+
+hipError_t launch_verify(const Args &a, hipStream_t stream);
+hipError_t launch_commit(const Args &a, hipStream_t stream);
+hipError_t launch_accepted_path(const Args &a, hipStream_t stream);
+hipError_t launch_verify_storeall(const Args &a, hipStream_t stream);
+hipError_t launch_commit_storeall(const Args &a, hipStream_t stream);
+
+}  // namespace gdn

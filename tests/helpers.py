@@ -1,0 +1,66 @@
+"""Shared helpers for the GPU parity tests: device upload of a workload and the
+error metrics the parity bar is stated in."""
+from __future__ import annotations
+
+import numpy as np
+
+# Row-normwise relative error bar for float outputs (fp32 accumulation with
+# bf16 q/k/v inputs): max over rows of ||x - ref||_inf / ||ref||_inf.
+TOL = 2e-3
+
+
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X visible to torch"
+    return torch.device("cuda:0")
+
+
+def upload(wl, S0=None):
+    """Device tensors of a workload in the C-ABI formats."""
+    import torch
+    d = dev()
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(d).view(torch.bfloat16)
+    return dict(
+        S0=torch.from_numpy(np.ascontiguousarray(wl.S0 if S0 is None else S0, dtype=np.float32)).to(d),
+        q=bf(wl.q), k=bf(wl.k), v=bf(wl.v),
+        g=torch.from_numpy(np.ascontiguousarray(wl.g, np.float32)).to(d),
+        beta=torch.from_numpy(np.ascontiguousarray(wl.beta, np.float32)).to(d),
+        node_offset=torch.from_numpy(np.ascontiguousarray(wl.node_offset, np.int32)).to(d),
+        parent=torch.from_numpy(np.ascontiguousarray(wl.parent, np.int32)).to(d),
+        accept_node=torch.from_numpy(np.ascontiguousarray(wl.accept_node, np.int32)).to(d),
+    )
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def anc_u64(t):
+    return host(t).view(np.uint64)
+
+
+def rowwise_rel_err(x, ref):
+    """max over rows (last axis) of ||x - ref||_inf / ||ref||_inf."""
+    x = np.asarray(x, np.float64).reshape(-1, np.shape(x)[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, np.shape(ref)[-1])
+    num = np.abs(x - ref).max(axis=1)
+    den = np.abs(ref).max(axis=1)
+    assert np.all(np.isfinite(num)), "non-finite values where the oracle has finite ones"
+    zero = den == 0
+    if zero.any():
+        assert np.all(num[zero] == 0), "nonzero output where the oracle row is exactly zero"
+    return float((num[~zero] / den[~zero]).max()) if (~zero).any() else 0.0
+
+
+def matwise_rel_err(x, ref):
+    """max over leading index of ||X - REF||_max / ||REF||_max (matrices in the last two axes)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    lead = x.shape[:-2]
+    x = x.reshape(-1, x.shape[-2] * x.shape[-1])
+    ref = ref.reshape(-1, ref.shape[-2] * ref.shape[-1])
+    return rowwise_rel_err(x, ref)
+
+
+def oracle_inputs(wl):
+    return (wl.S0, wl.q64(), wl.k64(), wl.v64(), wl.g, wl.beta, wl.node_offset, wl.parent)

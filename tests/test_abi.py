@@ -1,0 +1,111 @@
+"""CPU checks of the C ABI: the built library loads, exports every function the
+header declares, and rejects bad arguments on the host (returning a negative
+code before any kernel is enqueued).  No compute call is made here."""
+import ctypes
+import os
+
+import pytest
+
+import speculative_decoding_tree_amd.gdn_tree as G
+
+
+def test_library_exports_every_declared_symbol():
+    L = G.lib()
+    names = G.declared_symbols()
+    assert {"gdn_tree_verify", "gdn_tree_commit", "gdn_tree_accepted_path", "gdn_tree_verify_storeall",
+            "gdn_tree_commit_storeall", "gdn_tree_state_bytes", "gdn_tree_strerror",
+            "gdn_tree_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert G.abi_version() == 1
+
+
+def test_header_constants_match_binding():
+    text = open(G.HEADER).read()
+    for name, val in [("GDN_TREE_S_BAD_OFFSETS", G.S_BAD_OFFSETS), ("GDN_TREE_S_TOO_MANY", G.S_TOO_MANY),
+                      ("GDN_TREE_S_BAD_PARENT", G.S_BAD_PARENT), ("GDN_TREE_S_BAD_PATH", G.S_BAD_PATH),
+                      ("GDN_TREE_S_BAD_ACCEPT", G.S_BAD_ACCEPT), ("GDN_TREE_S_BAD_SLOT", G.S_BAD_SLOT)]:
+        assert f"#define {name} {val}" in text
+
+
+def test_status_codes_agree_with_oracle_numbers():
+    import oracle as O
+    assert (O.STATUS_BAD_OFFSETS, O.STATUS_TOO_MANY_NODES, O.STATUS_BAD_PARENT, O.STATUS_BAD_PATH,
+            O.STATUS_BAD_ACCEPT, O.STATUS_BAD_SLOT) == (1, 2, 3, 4, 5, 6)
+
+
+def test_strerror_never_null():
+    for c in range(-8, 9):
+        assert isinstance(G.strerror(c), str) and G.strerror(c)
+
+
+NULLS15 = [None] * 14
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("Hv", 0, -2), ("Hk", 3, -2), ("n_slots", 0, -2), ("T", -1, -2), ("B", -1, -2),
+    ("d_k", 64, -3), ("d_v", 256, -3), ("max_nodes", 0, -4), ("max_nodes", 65, -4),
+])
+def test_host_validation_rejects_dims(field, value, code):
+    L = G.lib()
+    d = G.make_dims(4, 32, 16, 20, 8, 4)
+    setattr(d, field, value)
+    assert L.gdn_tree_verify(ctypes.byref(d), *NULLS15) == code
+    assert L.gdn_tree_commit(ctypes.byref(d), *([None] * 12)) == code
+    assert L.gdn_tree_accepted_path(ctypes.byref(d), *([None] * 7)) == code
+    assert L.gdn_tree_verify_storeall(ctypes.byref(d), *([None] * 13)) == code
+    assert L.gdn_tree_commit_storeall(ctypes.byref(d), *([None] * 9)) == code
+
+
+def test_host_validation_rejects_null_pointers():
+    L = G.lib()
+    d = G.make_dims(4, 32, 16, 20, 8, 4)
+    assert L.gdn_tree_verify(None, *NULLS15) == -1
+    assert L.gdn_tree_verify(ctypes.byref(d), *NULLS15) == -1
+    assert L.gdn_tree_commit(ctypes.byref(d), *([None] * 12)) == -1
+    assert L.gdn_tree_accepted_path(ctypes.byref(d), *([None] * 7)) == -1
+    # non-null S0/node_offset but null per-node arrays with T > 0
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake, None] + [None] * 6 + [fake] + [None] * 5
+    assert L.gdn_tree_verify(ctypes.byref(d), *args) == -1
+
+
+def test_empty_batch_is_a_no_op():
+    L = G.lib()
+    d = G.make_dims(0, 32, 16, 0, 8, 1)
+    assert L.gdn_tree_verify(ctypes.byref(d), *NULLS15) == 0
+    assert L.gdn_tree_commit(ctypes.byref(d), *([None] * 12)) == 0
+
+
+def test_size_overflow_rejected():
+    L = G.lib()
+    d = G.make_dims(1, 1 << 20, 1, 1 << 30, 8, 1)
+    assert L.gdn_tree_verify(ctypes.byref(d), *NULLS15) == -6
+
+
+def test_state_bytes_accounting():
+    d = G.make_dims(256, 32, 16, 8192, 32, 256)
+    assert G.state_bytes(d, True) == 8192 * 32 * 128 * 128 * 4          # 16 GiB: one state per node-head
+    assert G.state_bytes(d, False) == 8192 * 32 * 128 * 4               # 128 MiB: U rows
+    bad = G.make_dims(1, 3, 2, 1, 8, 1)
+    assert G.state_bytes(bad, True) == 0
+
+
+def test_oracle_not_imported_by_product_path():
+    import speculative_decoding_tree_amd
+    root = os.path.dirname(speculative_decoding_tree_amd.__file__)
+    for dirpath, _, files in os.walk(root):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_misaligned_pointer_rejected():
+    L = G.lib()
+    d = G.make_dims(1, 2, 1, 3, 4, 1)
+    ok = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10004)
+    args = [odd, None, ok, ok, ok, ok, ok, ok, ok, ok, ok, None, None, None]
+    assert L.gdn_tree_verify(ctypes.byref(d), *args) == -7
+    assert "16-byte" in G.strerror(-7)

@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bar: bit-exact ancestry masks, accepted paths and statuses; row-normwise
+relative error <= 2e-3 on node outputs, pseudo-values and committed states.
+Small configurations are compared in full; the batch-256 configurations are
+run whole, in the launch configuration the benchmark times, and compared on a
+sample of requests that the oracle evaluates one by one, plus properties that
+hold at any size (statuses, masks and paths in full).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from helpers import TOL, anc_u64, host, matwise_rel_err, oracle_inputs, rowwise_rel_err, upload
+
+import speculative_decoding_tree_amd.gdn_tree as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _mn(wl):
+    return max(1, wl.max_nodes)
+
+
+def run_gpu(wl, S0=None, state_slot=None, max_nodes=None, inplace=False):
+    mn = max_nodes or _mn(wl)
+    d = upload(wl, S0)
+    ss = None if state_slot is None else torch.from_numpy(np.asarray(state_slot, np.int32)).cuda()
+    out, U, anc, st = G.verify(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"],
+                               d["parent"], max_nodes=mn, state_slot=ss)
+    path, plen, pst = G.accepted_path(d["node_offset"], d["parent"], d["accept_node"], max_nodes=mn)
+    S_in = d["S0"].clone() if inplace else d["S0"]
+    S1, cst = G.commit(S_in, U, d["k"], d["g"], d["node_offset"], d["parent"], path, plen, max_nodes=mn,
+                       S_out=S_in if inplace else None, state_slot=ss)
+    torch.cuda.synchronize()
+    return dict(out=host(out), U=host(U), anc=anc_u64(anc), status=host(st), path=host(path),
+                plen=host(plen), pstatus=host(pst), S1=host(S1), cstatus=host(cst), dev=d)
+
+
+def check_full(wl, res, state_slot=None, mn=None):
+    mn = mn or _mn(wl)
+    Oo, Uo, anco, sto = O.verify_batch(*oracle_inputs(wl), wl.Hv, wl.Hk, max_nodes=mn, state_slot=state_slot)
+    assert np.array_equal(res["status"], sto)
+    assert np.array_equal(res["anc"], anco)
+    ok = np.concatenate([np.arange(wl.node_offset[b], wl.node_offset[b + 1])
+                         for b in range(wl.B) if sto[b] == 0] + [np.zeros(0, int)]).astype(int)
+    eo = rowwise_rel_err(res["out"][ok], Oo[ok])
+    eu = rowwise_rel_err(res["U"][ok], Uo[ok])
+    assert eo <= TOL and eu <= TOL, (eo, eu)
+    po, plo, pso = O.accepted_path_batch(wl.node_offset, wl.parent, wl.accept_node, max_nodes=mn)
+    assert np.array_equal(res["path"], po) and np.array_equal(res["plen"], plo)
+    assert np.array_equal(res["pstatus"], pso)
+    So, cso = O.commit_batch(*oracle_inputs(wl), po, plo, wl.Hv, wl.Hk, max_nodes=mn, state_slot=state_slot)
+    assert np.array_equal(res["cstatus"], cso)
+    es = matwise_rel_err(res["S1"], So)
+    assert es <= TOL, es
+    for b in range(wl.B):   # nothing accepted: S0 kept bit-exactly
+        slot = b if state_slot is None else state_slot[b]
+        if plo[b] == 0 and cso[b] == 0:
+            assert np.array_equal(res["S1"][slot], wl.S0[slot])
+    return eo, eu, es
+
+
+SMALL = {
+    "c1_chain_pad": lambda: W.zero_pad(W.make_c1("chain")),
+    "c1_tree_pad": lambda: W.zero_pad(W.make_c1("tree")),
+    "c2": W.make_c2,
+    "c3_b1": lambda: W.make_c3(B=1),
+    "c3_b16": lambda: W.make_c3(B=16),
+    "c3_b16_bfs": lambda: W.make_c3(B=16, bfs=True),
+    "mixed_small": lambda: W.make_c5(per_kind=3, Hv=6, Hk=2),
+    "deep_chain64": lambda: W.make_custom([W.chain(64), W.chain(64)], [63, 20], Hv=4, Hk=2),
+    "forest_empty_single": lambda: W.make_custom(
+        [np.zeros(0, np.int32), np.array([-1], np.int32), np.full(8, -1, np.int32),
+         np.zeros(0, np.int32), W.random_tree(np.random.default_rng(3), 40)],
+        [-1, 0, 5, -1, 7], Hv=4, Hk=4),
+    "ragged_tail_max": lambda: W.make_custom(
+        [W.random_tree(np.random.default_rng(s), n) for s, n in enumerate([64, 17, 33, 5, 63, 1])],
+        [3, 0, -1, 4, 10, 0], Hv=6, Hk=3),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_configs_full_parity(name):
+    wl = SMALL[name]()
+    res = run_gpu(wl)
+    check_full(wl, res)
+
+
+def test_zero_padding_is_exact():
+    wl = W.zero_pad(W.make_c1("tree"))
+    res = run_gpu(wl)
+    assert np.all(res["out"][..., 16:] == 0) and np.all(res["U"][..., 16:] == 0)
+    assert np.all(res["S1"][..., 16:, :] == 0) and np.all(res["S1"][..., :, 16:] == 0)
+
+
+def test_state_slot_permutation_and_inplace_commit():
+    wl = W.make_c5(per_kind=2, Hv=4, Hk=2, seed=5)
+    slots = list(range(wl.B))[::-1]
+    res = run_gpu(wl, state_slot=slots, inplace=True)
+    check_full(wl, res, state_slot=slots)
+
+
+def test_deterministic_bitwise():
+    wl = W.make_c5(per_kind=2, Hv=6, Hk=2, seed=7)
+    a, b = run_gpu(wl), run_gpu(wl)
+    for key in ("out", "U", "S1", "anc", "path"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_sibling_perturbation_leaves_other_branches_bit_identical():
+    rng = np.random.default_rng(11)
+    par = W.random_tree(rng, 24)
+    wl = W.make_custom([par], [5], Hv=4, Hk=2, seed=2)
+    base = run_gpu(wl)
+    j = 4
+    sub = {t for t in range(24) if (O.ancestry(par)[t] >> j) & 1}
+    wl2 = W.make_custom([par], [5], Hv=4, Hk=2, seed=2)
+    wl2.v[j] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(wl2.v[j]) * 2 + 1)
+    wl2.k[j] = W.f32_to_bf16_bits(-W.bf16_bits_to_f32(wl2.k[j]))
+    wl2.q[j] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(wl2.q[j]) + 1)
+    wl2.g[j] -= 0.5
+    wl2.beta[j] = 0.9
+    pert = run_gpu(wl2)
+    for t in range(24):
+        same = np.array_equal(base["out"][t], pert["out"][t]) and np.array_equal(base["U"][t], pert["U"][t])
+        assert same == (t not in sub), t
+
+
+def test_gqa_twin_heads_bit_identical():
+    wl = W.make_custom([W.random_tree(np.random.default_rng(4), 20), W.chain(5)], [3, 4], Hv=4, Hk=2)
+    wl.S0[:, 1] = wl.S0[:, 0]
+    wl.v[:, 1] = wl.v[:, 0]
+    wl.g[:, 1] = wl.g[:, 0]
+    wl.beta[:, 1] = wl.beta[:, 0]
+    res = run_gpu(wl)
+    assert np.array_equal(res["out"][:, 0], res["out"][:, 1])
+    assert np.array_equal(res["U"][:, 0], res["U"][:, 1])
+    assert np.array_equal(res["S1"][:, 0], res["S1"][:, 1])
+
+
+# ----------------------------------------------------------------------------
+# device-detected errors
+# ----------------------------------------------------------------------------
+
+def test_device_errors():
+    wl = W.make_custom([W.chain(3), W.root_branch(), W.chain(4), W.chain(2)], [2, 4, 1, -1], Hv=4, Hk=2)
+    clean = run_gpu(wl)
+    bad = W.make_custom([W.chain(3), W.root_branch(), W.chain(4), W.chain(2)], [2, 4, 1, -1], Hv=4, Hk=2)
+    bad.parent[3 + 2] = 2                      # request 1: node 2 -> parent 2 (not < 2)
+    bad.accept_node[2] = 4                     # request 2: accept beyond N
+    res = run_gpu(bad)
+    assert list(res["status"]) == [0, O.STATUS_BAD_PARENT, 0, 0]
+    assert np.isnan(res["out"][3:9]).all() and np.isnan(res["U"][3:9]).all()
+    assert np.all(res["anc"][3:9] == 0)
+    for r in (slice(0, 3), slice(9, 15)):       # other requests untouched, bit-exact
+        assert np.array_equal(res["out"][r], clean["out"][r])
+    assert list(res["pstatus"]) == [0, O.STATUS_BAD_PARENT, O.STATUS_BAD_ACCEPT, 0]
+    assert res["plen"][1] == 0 and res["plen"][2] == 0
+    # commit: invalid request keeps S0; path problems give status 4 and S0
+    assert np.array_equal(res["S1"][1], bad.S0[1]) and np.array_equal(res["S1"][2], bad.S0[2])
+    check_full(bad, res)
+
+
+def test_device_errors_paths_offsets_slots_and_node_cap():
+    wl = W.make_custom([W.chain(3), W.root_branch(), W.chain(5)], [2, 4, 1], Hv=2, Hk=1)
+    d = upload(wl)
+    mn = 6
+    # too many nodes: max_nodes 4 with requests of 6 and 5 nodes
+    out, U, anc, st = G.verify(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"],
+                               d["parent"], max_nodes=4)
+    torch.cuda.synchronize()
+    assert list(host(st)) == [0, O.STATUS_TOO_MANY_NODES, O.STATUS_TOO_MANY_NODES]
+    assert np.isnan(host(out)[3:]).all()
+    # bad slot
+    ss = torch.tensor([0, 9, 2], dtype=torch.int32, device="cuda")
+    out, U, anc, st = G.verify(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"],
+                               d["parent"], max_nodes=mn, state_slot=ss)
+    torch.cuda.synchronize()
+    assert list(host(st)) == [0, O.STATUS_BAD_SLOT, 0]
+    # bad offsets (request 1 ends before it starts)
+    off = torch.tensor([0, 3, 2, 14], dtype=torch.int32, device="cuda")
+    out, U, anc, st = G.verify(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], off, d["parent"],
+                               max_nodes=mn)
+    torch.cuda.synchronize()
+    assert host(st)[1] == O.STATUS_BAD_OFFSETS
+    # bad paths: not a chain / too long / negative length
+    out, U, anc, st = G.verify(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"],
+                               d["parent"], max_nodes=mn)
+    path = torch.zeros((3, mn), dtype=torch.int32, device="cuda")
+    path[0, :2] = torch.tensor([0, 2])
+    path[1, :3] = torch.tensor([3, 4, 5])
+    plen = torch.tensor([2, 3, 7], dtype=torch.int32, device="cuda")
+    S_out = torch.zeros_like(d["S0"])
+    S1, cst = G.commit(d["S0"], U, d["k"], d["g"], d["node_offset"], d["parent"], path, plen, max_nodes=mn,
+                       S_out=S_out)
+    torch.cuda.synchronize()
+    assert list(host(cst)) == [O.STATUS_BAD_PATH, 0, O.STATUS_BAD_PATH]
+    S1 = host(S1)
+    assert np.array_equal(S1[0], wl.S0[0]) and np.array_equal(S1[2], wl.S0[2])
+    So, cso = O.commit_batch(*oracle_inputs(wl), host(path), host(plen), wl.Hv, wl.Hk, max_nodes=mn,
+                             S_out_init=np.zeros_like(wl.S0))
+    assert list(cso) == list(host(cst))
+    assert matwise_rel_err(S1, So) <= TOL
+
+
+# ----------------------------------------------------------------------------
+# storeall comparison variant
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c2", "c3_b16", "mixed_small", "forest_empty_single"])
+def test_storeall_parity(name):
+    wl = SMALL[name]()
+    if name == "c2":
+        wl = W.subset(wl, range(16))
+    mn = _mn(wl)
+    d = upload(wl)
+    out, NS, st = G.verify_storeall(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"],
+                                    d["parent"], max_nodes=mn)
+    S1, cst = G.commit_storeall(d["S0"], NS, d["node_offset"], d["parent"], d["accept_node"], max_nodes=mn)
+    torch.cuda.synchronize()
+    Oo, NSo, sto = O.verify_storeall_batch(*oracle_inputs(wl), wl.Hv, wl.Hk, max_nodes=mn)
+    assert np.array_equal(host(st), sto)
+    assert rowwise_rel_err(host(out), Oo) <= TOL
+    assert matwise_rel_err(host(NS), NSo) <= TOL
+    So, cso = O.commit_storeall_batch(wl.S0, NSo, wl.node_offset, wl.parent, wl.accept_node, max_nodes=mn)
+    assert np.array_equal(host(cst), cso)
+    assert matwise_rel_err(host(S1), So) <= TOL
+
+
+# ----------------------------------------------------------------------------
+# batch-256 configurations, whole batch on the GPU, sampled oracle
+# ----------------------------------------------------------------------------
+
+def sampled_check(wl, res, n_sample=24, seed=0):
+    mn = _mn(wl)
+    assert np.all(res["status"] == 0) and np.all(res["cstatus"] == 0) and np.all(res["pstatus"] == 0)
+    anc = np.concatenate([np.array(O.ancestry(wl.parents_of(b)), dtype=np.uint64) for b in range(wl.B)])
+    assert np.array_equal(res["anc"], anc)
+    po, plo, _ = O.accepted_path_batch(wl.node_offset, wl.parent, wl.accept_node, max_nodes=mn)
+    assert np.array_equal(res["path"], po) and np.array_equal(res["plen"], plo)
+    rng = np.random.default_rng(seed)
+    reqs = sorted(rng.choice(wl.B, size=min(n_sample, wl.B), replace=False).tolist())
+    # always include the largest trees
+    reqs = sorted(set(reqs) | {int(np.argmax(np.diff(wl.node_offset)))})
+    q, k, v = wl.q64(), wl.k64(), wl.v64()
+    worst = [0.0, 0.0, 0.0]
+    for b in reqs:
+        st, Ob, Ub, ab, states = O.verify_request(wl.S0, q, k, v, wl.g, wl.beta, wl.node_offset, wl.parent,
+                                                  b, wl.Hv, wl.Hk, max_nodes=mn)
+        lo, hi = wl.node_offset[b], wl.node_offset[b + 1]
+        worst[0] = max(worst[0], rowwise_rel_err(res["out"][lo:hi], Ob))
+        worst[1] = max(worst[1], rowwise_rel_err(res["U"][lo:hi], Ub))
+        a = int(wl.accept_node[b])
+        for h in range(wl.Hv):
+            want = O.commit_unit(wl.S0[b, h], states[h], O.accepted_path(wl.parents_of(b), a))
+            worst[2] = max(worst[2], matwise_rel_err(res["S1"][b, h][None], want[None]))
+    assert max(worst) <= TOL, worst
+    return worst
+
+
+def test_c4_full_batch_sampled():
+    wl = W.make_c4()
+    res = run_gpu(wl)
+    print("c4 worst rel err out/U/S':", sampled_check(wl, res))
+
+
+def test_c5_full_batch_sampled():
+    wl = W.make_c5()
+    res = run_gpu(wl)
+    print("c5 worst rel err out/U/S':", sampled_check(wl, res))
+
+
+def test_commit_alone_from_oracle_pseudo_values():
+    """commit fed with the oracle's U (cast to fp32): isolates the commit kernel."""
+    wl = SMALL["mixed_small"]()
+    mn = _mn(wl)
+    Oo, Uo, _, _ = O.verify_batch(*oracle_inputs(wl), wl.Hv, wl.Hk, max_nodes=mn)
+    d = upload(wl)
+    U = torch.from_numpy(Uo.astype(np.float32)).cuda()
+    po, plo, _ = O.accepted_path_batch(wl.node_offset, wl.parent, wl.accept_node, max_nodes=mn)
+    S1, cst = G.commit(d["S0"], U, d["k"], d["g"], d["node_offset"], d["parent"],
+                       torch.from_numpy(po).cuda(), torch.from_numpy(plo).cuda(), max_nodes=mn)
+    torch.cuda.synchronize()
+    So, _ = O.commit_batch(*oracle_inputs(wl), po, plo, wl.Hv, wl.Hk, max_nodes=mn)
+    assert matwise_rel_err(host(S1), So) <= 1e-5
