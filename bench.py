@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Throughput of tree-structured GDN speculative verify + commit on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c4]
+
+One step = the whole hot path over one batch: gdn_tree_verify (outputs and
+pseudo-values of every draft node), gdn_tree_accepted_path and gdn_tree_commit
+(the accepted path's state, out of place so every step is identical).  Inputs
+are seeded synthetic tensors already resident in HBM; three independent copies
+of every buffer are rotated so that no step finds the previous step's data in
+the 256 MB Infinity Cache.  Prints ONE JSON line on stdout.
+
+The default workload is the ragged batch-256 mix (64 each of depth-3 chains,
+6-node root-branch trees, random 16- and 64-node trees; 48 v-heads, 16 k-heads,
+d = 128).  ``value`` is verified tree-nodes per second (a node counts once all
+48 heads have verified it; commits/s and node-heads/s ride along).  Per-kernel
+durations come from HIP events recorded on the launch stream around every
+launch of the timed steps.  The snapshot-per-node (storeall) pair is timed
+after the main loop for comparison, and the fp64 oracle is timed on a bounded
+sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "verified tree-nodes/s (all heads) + commits/s at batch 256; % HBM peak"
+D = 128
+
+
+# ----------------------------------------------------------------------------
+# algorithmic bytes (what the method must move, each byte once)
+# ----------------------------------------------------------------------------
+
+def verify_bytes(wl) -> int:
+    """H0 once per (request, v-head); per node and v-head v (256 B), g and beta
+    (8 B), out and U (512 B each); per node and key head q and k (512 B);
+    ancestry masks, parents, offsets and statuses."""
+    import numpy as np
+    n = np.diff(wl.node_offset).astype(np.int64)
+    per_req = wl.Hv * (D * D * 4 + n * (2 * D + 8 + 4 * D + 4 * D)) + wl.Hk * n * (4 * D)
+    return int(per_req.sum() + wl.T * (8 + 4) + 4 * (wl.B + 1) + 4 * wl.B)
+
+
+def commit_bytes(wl, path_len) -> int:
+    """H0 in and H' out once per (request, v-head); per path node and v-head
+    its U row (512 B) and g (4 B); per path node and key head its k row (256 B);
+    the path rows."""
+    import numpy as np
+    L = np.asarray(path_len, np.int64)
+    per_req = wl.Hv * (2 * D * D * 4 + L * (4 * D + 4)) + wl.Hk * L * (2 * D)
+    return int(per_req.sum() + 4 * L.sum() + 4 * wl.B + 4 * (wl.B + 1))
+
+
+def verify_flops(wl) -> int:
+    """State products 4 N d^2 per unit plus the masked grams and solve/output terms."""
+    total = 0
+    for b in range(wl.B):
+        par = wl.parents_of(b)
+        dep = [0] * len(par)
+        for i, p in enumerate(par):
+            dep[i] = 1 if p < 0 else dep[p] + 1
+        n = len(par)
+        total += wl.Hv * (4 * n * D * D + 4 * D * sum(2 * x - 1 for x in dep))
+    return total
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample, one process per core
+# ----------------------------------------------------------------------------
+
+def _oracle_request(args):
+    """Worker: verify one request (all heads) and commit its accepted path."""
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    import numpy as np
+    import oracle as O
+    S0, q, k, v, g, beta, parent, accept, Hv, Hk = args
+    off = np.array([0, len(parent)], np.int32)
+    st, Ob, Ub, anc, states = O.verify_request(S0[None], q, k, v, g, beta, off, parent, 0, Hv, Hk)
+    path = O.accepted_path(parent, int(accept))
+    for h in range(Hv):
+        O.commit_unit(S0[h], states[h], path)
+    return len(parent)
+
+
+def cpu_baseline(wl, n_req: int):
+    import multiprocessing as mp
+    import numpy as np
+    cores = min(16, len(os.sched_getaffinity(0)))
+    q, k, v = wl.q64(), wl.k64(), wl.v64()
+    jobs = []
+    for b in range(min(n_req, wl.B)):
+        lo, hi = wl.node_offset[b], wl.node_offset[b + 1]
+        jobs.append((wl.S0[b], q[lo:hi], k[lo:hi], v[lo:hi], wl.g[lo:hi], wl.beta[lo:hi],
+                     wl.parent[lo:hi].copy(), wl.accept_node[b], wl.Hv, wl.Hk))
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_request, jobs[:cores])        # warm the workers
+        t0 = time.perf_counter()
+        nodes = sum(pool.map(_oracle_request, jobs, chunksize=1))
+        dt = time.perf_counter() - t0
+    return {"value": nodes / dt, "unit": "nodes/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {len(jobs)} of {wl.B} requests of the {wl.name} batch ({nodes} nodes, "
+                      f"all {wl.Hv} heads), fp64 verify + commit, one process per core",
+            "seconds": dt}
+
+
+# ----------------------------------------------------------------------------
+# GPU timing
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c5", choices=["c5", "c4"])
+    ap.add_argument("--pools", type=int, default=3, help="rotated copies of every buffer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-storeall", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=128, help="requests in the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (reference kernel for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the verify/commit path has no cross-GPU step and this "
+              "build runs on a single MI355X; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from speculative_decoding_tree_amd import gdn_tree as G
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X visible to torch", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    t0 = time.time()
+    wl = W.make_c5() if args.workload == "c5" else W.make_c4()
+    log(f"[bench] generated {wl.name}: B={wl.B} Hv={wl.Hv} Hk={wl.Hk} T={wl.T} "
+        f"max_nodes={wl.max_nodes} in {time.time() - t0:.1f}s")
+    mn = wl.max_nodes
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def make_pool():
+        p = dict(S0=torch.from_numpy(wl.S0).to(dev), q=bf(wl.q), k=bf(wl.k), v=bf(wl.v),
+                 g=torch.from_numpy(wl.g).to(dev), beta=torch.from_numpy(wl.beta).to(dev),
+                 off=torch.from_numpy(wl.node_offset).to(dev), par=torch.from_numpy(wl.parent).to(dev),
+                 acc=torch.from_numpy(wl.accept_node).to(dev))
+        p["S_out"] = torch.empty_like(p["S0"])
+        p["out"] = torch.empty((wl.T, wl.Hv, D), dtype=torch.float32, device=dev)
+        p["U"] = torch.empty_like(p["out"])
+        p["anc"] = torch.empty((wl.T,), dtype=torch.int64, device=dev)
+        p["status"] = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+        p["path"] = torch.empty((wl.B, mn), dtype=torch.int32, device=dev)
+        p["plen"] = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+        p["pst"] = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+        p["cst"] = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+        return p
+
+    pools = [make_pool() for _ in range(max(1, args.pools))]
+    stream = torch.cuda.current_stream()
+
+    def step(p, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        G.verify(p["S0"], p["q"], p["k"], p["v"], p["g"], p["beta"], p["off"], p["par"], max_nodes=mn,
+                 out=p["out"], U=p["U"], anc_mask=p["anc"], status=p["status"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        G.accepted_path(p["off"], p["par"], p["acc"], max_nodes=mn, path=p["path"], path_len=p["plen"],
+                        status=p["pst"], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        G.commit(p["S0"], p["U"], p["k"], p["g"], p["off"], p["par"], p["path"], p["plen"], max_nodes=mn,
+                 S_out=p["S_out"], status=p["cst"], stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(pools[i % len(pools)])
+    torch.cuda.synchronize()
+    st = pools[0]["status"].cpu().numpy()
+    if not (np.all(st == 0) and np.all(pools[0]["cst"].cpu().numpy() == 0)):
+        raise RuntimeError(f"device status nonzero: {st}")
+    path_len = pools[0]["plen"].cpu().numpy()
+
+    # timed region: whole steps only
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(pools[i % len(pools)])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+
+    # per-kernel durations: events around each launch (separate pass, same steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(pools[i % len(pools)], evs[i])
+    torch.cuda.synchronize()
+    t_ver = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3     # us
+    t_path = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    t_com = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+
+    vb, cb = verify_bytes(wl), commit_bytes(wl, path_len)
+    vf = verify_flops(wl)
+
+    def kstats(t, nbytes, flops=None):
+        d = {"avg_us": float(t.mean()), "p10_us": float(np.percentile(t, 10)),
+             "p50_us": float(np.percentile(t, 50)), "p90_us": float(np.percentile(t, 90)),
+             "alg_bytes": nbytes, "alg_GBps": nbytes / (t.mean() * 1e-6) / 1e9,
+             "hbm_frac": nbytes / (t.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        if flops:
+            d["alg_flops"] = flops
+            d["TFLOPs"] = flops / (t.mean() * 1e-6) / 1e12
+        return d
+
+    kernels = {"gdn_tree_verify": kstats(t_ver, vb, vf), "gdn_tree_accepted_path": kstats(t_path, 0),
+               "gdn_tree_commit": kstats(t_com, cb)}
+    kernels["gdn_tree_accepted_path"].pop("hbm_frac")
+    dom = max(("gdn_tree_verify", "gdn_tree_commit"), key=lambda k: kernels[k]["avg_us"])
+    ach = kernels[dom]["alg_GBps"]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                "alg_bytes_per_launch": kernels[dom]["alg_bytes"]}
+
+    nodes_per_s = wl.T / (ms_step * 1e-3)
+    result = {
+        "metric": METRIC, "value": nodes_per_s, "unit": "nodes/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "Hv": wl.Hv, "Hk": wl.Hk, "d_k": D, "d_v": D, "T": wl.T,
+                   "max_nodes": mn, "trees": ("64 each of chain-3, root-branch-6, random-16, random-64"
+                                              if args.workload == "c5" else "random-32, depth <= 6"),
+                   "inputs": "q/k/v bf16, S0/g/beta fp32, seed 0", "parallelism": "single-gpu"},
+        "commits_per_s": wl.B / (ms_step * 1e-3),
+        "node_heads_per_s": wl.T * wl.Hv / (ms_step * 1e-3),
+        "hbm_frac_step": (vb + cb) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": roofline, "kernels": kernels,
+    }
+
+    if not args.no_storeall:
+        p = pools[0]
+        node_state = torch.empty((wl.T, wl.Hv, D, D), dtype=torch.float32, device=dev)
+        sa_out = torch.empty_like(p["out"])
+        sa_S = torch.empty_like(p["S0"])
+        sa_st = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+
+        def sa_step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            G.verify_storeall(p["S0"], p["q"], p["k"], p["v"], p["g"], p["beta"], p["off"], p["par"],
+                              max_nodes=mn, out=sa_out, node_state=node_state, status=sa_st, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            G.commit_storeall(p["S0"], node_state, p["off"], p["par"], p["acc"], max_nodes=mn, S_out=sa_S,
+                              status=sa_st, stream=stream)
+            if ev is not None:
+                ev[2].record(stream)
+
+        for _ in range(3):
+            sa_step()
+        n_sa = max(5, args.steps // 5)
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_sa)]
+        torch.cuda.synchronize()
+        for i in range(n_sa):
+            sa_step(sev[i])
+        torch.cuda.synchronize()
+        sv = np.array([e[0].elapsed_time(e[1]) for e in sev]) * 1e3
+        sc = np.array([e[1].elapsed_time(e[2]) for e in sev]) * 1e3
+        dims = G.make_dims(wl.B, wl.Hv, wl.Hk, wl.T, mn, wl.B)
+        result["storeall"] = {
+            "verify_avg_us": float(sv.mean()), "commit_avg_us": float(sc.mean()),
+            "ms_per_step": float((sv.mean() + sc.mean()) * 1e-3),
+            "speculative_state_bytes": G.state_bytes(dims, True),
+            "treewy_speculative_state_bytes": G.state_bytes(dims, False),
+            "node_state_write_GBps": wl.T * wl.Hv * D * D * 4 / (sv.mean() * 1e-6) / 1e9,
+            "treewy_ms_per_step": ms_step,
+        }
+        del node_state
+        torch.cuda.empty_cache()
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = 2 * a.numel() * 4
+
+    if not args.no_cpu_baseline:
+        log(f"[bench] oracle sample: {args.cpu_sample} requests on host cores")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,12 +8,23 @@
 // with anc*(t) the inclusive ancestors, G_t = sum of g over anc*(t),
 // gamma_t = exp(G_t), D_tj = exp(G_t - G_j) and H0 = S0^T ([d_k][d_v]):
 //
-//   W = K H0,  Z = Q H0                                  (state products)
+//   [W; Z] = [K; Q] H0,   [KK; QK] = [K; Q] K^T                (one MFMA pass)
 //   R_t = beta_t (v_t - gamma_t W_t)
-//   u_t = R_t - sum_{j in anc(t)} beta_t D_tj (k_t.k_j) u_j    (level by level)
-//   o_t = gamma_t Z_t + sum_{j in anc*(t)} D_tj (q_t.k_j) u_j
+//   u_t = R_t - sum_{j in anc(t)} beta_t D_tj KK_tj u_j           (level by level)
+//   o_t = gamma_t Z_t + sum_{j in anc*(t)} D_tj QK_tj u_j
 //
-// One workgroup (256 lanes, 4 wave64) owns one (request, v-head) unit.
+// gfx950 layout.  One workgroup (4 wave64) owns one (request, v-head) unit.
+// Wave w keeps its 128 x 32 column slab of H0 in registers as the B operand
+// of v_mfma_f32_16x16x32_bf16, split into bf16 hi + lo parts (q and k are
+// exact bf16, so two MFMAs with fp32 accumulation carry ~16 mantissa bits of
+// H0).  Lane (n, grp) of the wave loads float2 columns 32w + 2n, 2n+1 of rows
+// 32s + 8grp .. +7; the even columns form n-tile 0 and the odd ones n-tile 1,
+// so every load instruction reads whole 128-byte row segments.  The K and Q
+// rows of the unit are stacked (K rows 0..N-1, Q rows N..2N-1) in LDS as the A
+// operand; wave w also multiplies them by K^T for node columns 16w .. 16w+15,
+// which gives the masked grams.  The LDS block that held K/Q is reused for
+// R and then U.  H0, q/k, v and the per-node scalars are all requested before
+// the first barrier; barriers are LDS-only so those loads stay in flight.
 #include "common.h"
 #include "launch.h"
 
@@ -22,49 +33,60 @@ namespace {
 
 constexpr int NT = 256;
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier that orders LDS only: outstanding global loads are not
+// waited for (HIP's __syncthreads fences global memory as well).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Two floats to a packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2_t r;
+    r.x = (__bf16)a;
+    r.y = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// x = hi + lo + O(2^-16 |x|): hi = bf16(x), lo = bf16(x - hi) (x - hi is exact).
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = pack_bf16x2(a, b);
+    const float ha = __uint_as_float(hi << 16);
+    const float hb = __uint_as_float(hi & 0xffff0000u);
+    lo = pack_bf16x2(a - ha, b - hb);
+}
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 template <int NM>
 struct VerifySmem {
-    uint16_t K[NM][D];      // key rows of the unit's key head (bf16)
-    uint16_t Q[NM][D];      // query rows (bf16)
-    float W[NM][D];         // K.H0, then R, then U
-    float Z[NM][D];         // Q.H0
-    float A[NM][NM + 1];    // beta_t D_tj (k_t.k_j) for strict ancestors j
-    float P[NM][NM + 1];    // D_tj (q_t.k_j) for inclusive ancestors j
+    union {
+        uint16_t kq[2 * NM][D + 8];   // A operand: K rows then Q rows (bf16)
+        float ru[NM][D + 4];          // R, then U after the solve
+    } u;
+    float A[NM][NM + 1];   // beta_t D_tj KK_tj for strict ancestors j
+    float P[NM][NM + 1];   // D_tj QK_tj for inclusive ancestors j
     uint64_t anc[NM];
     float gam[NM], beta[NM], gl[NM];
-    int par[NM], dep[NM];
-    int lvl_nodes[NM];
-    int lvl_start[NM + 2];
+    int par[NM], dep[NM], lvl_nodes[NM], lvl_start[NM + 2];
     int bad, maxdep;
 };
 
-__device__ __forceinline__ float dot8_bf16(uint4 x, uint4 y, float acc) {
-    acc = fmaf(bf16_lo(x.x), bf16_lo(y.x), acc);
-    acc = fmaf(bf16_hi(x.x), bf16_hi(y.x), acc);
-    acc = fmaf(bf16_lo(x.y), bf16_lo(y.y), acc);
-    acc = fmaf(bf16_hi(x.y), bf16_hi(y.y), acc);
-    acc = fmaf(bf16_lo(x.z), bf16_lo(y.z), acc);
-    acc = fmaf(bf16_hi(x.z), bf16_hi(y.z), acc);
-    acc = fmaf(bf16_lo(x.w), bf16_lo(y.w), acc);
-    acc = fmaf(bf16_hi(x.w), bf16_hi(y.w), acc);
-    return acc;
-}
-
-__device__ __forceinline__ float axpy8_bf16(uint4 x, const float *hv, float acc) {
-    acc = fmaf(bf16_lo(x.x), hv[0], acc);
-    acc = fmaf(bf16_hi(x.x), hv[1], acc);
-    acc = fmaf(bf16_lo(x.y), hv[2], acc);
-    acc = fmaf(bf16_hi(x.y), hv[3], acc);
-    acc = fmaf(bf16_lo(x.z), hv[4], acc);
-    acc = fmaf(bf16_hi(x.z), hv[5], acc);
-    acc = fmaf(bf16_lo(x.w), hv[6], acc);
-    acc = fmaf(bf16_hi(x.w), hv[7], acc);
-    return acc;
-}
-
 template <int NM>
 __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
+    constexpr int MT = NM / 8;    // max M-tiles of 16 rows over 2N stacked rows
+    constexpr int KT = NM / 16;   // max M-tiles that can hold K rows
     __shared__ VerifySmem<NM> sm;
+
     const int n_units = a.B * a.Hv;
     const int unit = xcd_unit(blockIdx.x, n_units);
     if (unit >= n_units) return;
@@ -72,6 +94,8 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
     const int h = unit - b * a.Hv;
     const int hk = h / (a.Hv / a.Hk);
     const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int n = lane & 15, grp = lane >> 4;
 
     int lo, N;
     int st = check_offsets(a, b, lo, N);
@@ -79,21 +103,73 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
         if (h == 0 && tid == 0 && a.status) a.status[b] = st;
         return;
     }
-    if (st == GDN_TREE_S_OK) {
-        if (tid == 0) sm.bad = 0;
-        __syncthreads();
-        for (int t = tid; t < N; t += NT) {
-            const int p = a.parent[lo + t];
-            sm.par[t] = p;
-            if (p < -1 || p >= t) sm.bad = 1;
+    const int slot = resolve_slot(a, b);
+    const int nmt = (2 * N + 15) >> 4;
+
+    // ---- issue every global read of the unit (nodes first, then H0 and v) ----
+    int p_mine = -1;
+    float g_mine = 0.f, b_mine = 0.f;
+    constexpr int KQ_PER_T = (2 * NM * 16 + NT - 1) / NT;   // 16-byte pieces per lane
+    uint4 kq_stage[KQ_PER_T];
+    float2 hraw[4][8];
+    uint32_t vv[KT][4];
+    const bool ok = (st == GDN_TREE_S_OK);
+    if (ok) {
+        if (tid < N) {
+            const size_t gi = (size_t)(lo + tid) * a.Hv + h;
+            p_mine = a.parent[lo + tid];
+            g_mine = a.g[gi];
+            b_mine = a.beta[gi];
         }
-        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < KQ_PER_T; ++e) {
+            const int idx = tid + e * NT;
+            const int r = idx >> 4, c8 = idx & 15;
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (r < N)
+                val = reinterpret_cast<const uint4 *>(a.k + ((size_t)(lo + r) * a.Hk + hk) * D)[c8];
+            else if (r < 2 * N)
+                val = reinterpret_cast<const uint4 *>(a.q + ((size_t)(lo + r - N) * a.Hk + hk) * D)[c8];
+            kq_stage[e] = val;
+        }
+        if (slot >= 0) {
+            const float *H = a.S0 + ((size_t)slot * a.Hv + h) * D * D + 32 * w + 2 * n;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    hraw[s][e] = *reinterpret_cast<const float2 *>(H + (32 * s + 8 * grp + e) * D);
+        }
+#pragma unroll
+        for (int tau = 0; tau < KT; ++tau)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * tau + 4 * grp + i;
+                vv[tau][i] = 0;
+                if (r < N)
+                    vv[tau][i] = *reinterpret_cast<const uint32_t *>(
+                        a.v + ((size_t)(lo + r) * a.Hv + h) * D + 32 * w + 2 * n);
+            }
+        // parents, gates and K/Q rows into LDS
+        if (tid < N) {
+            sm.par[tid] = p_mine;
+            sm.gl[tid] = g_mine;
+            sm.beta[tid] = b_mine;
+        }
+        if (w == 0) {
+            const bool bad = (tid < N) && (p_mine < -1 || p_mine >= tid);
+            const unsigned long long any = __ballot(bad);
+            if (lane == 0) sm.bad = any != 0ull;
+        }
+#pragma unroll
+        for (int e = 0; e < KQ_PER_T; ++e) {
+            const int idx = tid + e * NT;
+            const int r = idx >> 4, c8 = idx & 15;
+            if (r < 16 * nmt) *reinterpret_cast<uint4 *>(&sm.u.kq[r][c8 * 8]) = kq_stage[e];
+        }
+        lds_barrier();
         if (sm.bad) st = GDN_TREE_S_BAD_PARENT;
-    }
-    int slot = -1;
-    if (st == GDN_TREE_S_OK) {
-        slot = resolve_slot(a, b);
-        if (slot < 0) st = GDN_TREE_S_BAD_SLOT;
+        else if (slot < 0) st = GDN_TREE_S_BAD_SLOT;
     }
     if (st != GDN_TREE_S_OK) {
         const float qnan = __int_as_float(0x7fc00000);
@@ -112,26 +188,15 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
     if (h == 0 && tid == 0 && a.status) a.status[b] = GDN_TREE_S_OK;
     if (N == 0) return;
 
-    // ---- tree pre-pass: ancestry bitsets, depths, per-node gate and beta ----
+    // ---- tree pre-pass: ancestry bitsets and depths ----
     if (tid < N) {
-        const int t = tid;
         uint64_t m = 0;
-        for (int j = t; j >= 0; j = sm.par[j]) m |= 1ull << j;
-        sm.anc[t] = m;
-        sm.dep[t] = __popcll(m);
-        const size_t gi = (size_t)(lo + t) * a.Hv + h;
-        sm.gl[t] = a.g[gi];
-        sm.beta[t] = a.beta[gi];
-        if (h == 0 && a.anc_mask) a.anc_mask[lo + t] = m;
+        for (int j = tid; j >= 0; j = sm.par[j]) m |= 1ull << j;
+        sm.anc[tid] = m;
+        sm.dep[tid] = __popcll(m);
+        if (h == 0 && a.anc_mask) a.anc_mask[lo + tid] = m;
     }
-    // stage the key head's q and k rows (bf16, 256 B each)
-    for (int idx = tid; idx < N * (D / 8); idx += NT) {
-        const int t = idx >> 4, c8 = idx & 15;
-        const size_t row = ((size_t)(lo + t) * a.Hk + hk) * D;
-        *reinterpret_cast<uint4 *>(&sm.K[t][c8 * 8]) = reinterpret_cast<const uint4 *>(a.k + row)[c8];
-        *reinterpret_cast<uint4 *>(&sm.Q[t][c8 * 8]) = reinterpret_cast<const uint4 *>(a.q + row)[c8];
-    }
-    __syncthreads();
+    lds_barrier();
     if (tid < N) {
         uint64_t m = sm.anc[tid];
         float G = 0.f;
@@ -153,100 +218,150 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
         sm.lvl_start[maxd + 1] = pos;
         sm.maxdep = maxd;
     }
-    // ---- masked grams and decay ratios (ancestor pairs only) ----
-    for (int idx = tid; idx < N * N; idx += NT) {
-        const int t = idx / N, j = idx - t * N;
-        if (!((sm.anc[t] >> j) & 1)) continue;
-        float kk = 0.f, qk = 0.f;
-#pragma unroll 4
-        for (int c8 = 0; c8 < D / 8; ++c8) {
-            const uint4 kj = *reinterpret_cast<const uint4 *>(&sm.K[j][c8 * 8]);
-            const uint4 kt = *reinterpret_cast<const uint4 *>(&sm.K[t][c8 * 8]);
-            const uint4 qt = *reinterpret_cast<const uint4 *>(&sm.Q[t][c8 * 8]);
-            kk = dot8_bf16(kt, kj, kk);
-            qk = dot8_bf16(qt, kj, qk);
+
+    // ---- B operands: H0 slab (hi, lo) and K^T for node columns 16w.. ----
+    u32x4 bhi[4][2], blo[4][2], bg[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+            uint32_t h0, l0, h1, l1;
+            split_bf16x2(hraw[s][2 * pr].x, hraw[s][2 * pr + 1].x, h0, l0);
+            split_bf16x2(hraw[s][2 * pr].y, hraw[s][2 * pr + 1].y, h1, l1);
+            bhi[s][0][pr] = h0;
+            blo[s][0][pr] = l0;
+            bhi[s][1][pr] = h1;
+            blo[s][1][pr] = l1;
         }
-        uint64_t seg = sm.anc[t] & ~sm.anc[j];   // nodes on the path strictly below j
-        float s = 0.f;
-        while (seg) {
-            s += sm.gl[__builtin_ctzll(seg)];
-            seg &= seg - 1;
-        }
-        const float dtj = expf(s);
-        sm.P[t][j] = dtj * qk;
-        if (j != t) sm.A[t][j] = sm.beta[t] * dtj * kk;
+    }
+    const bool gram = 16 * w < N;
+    if (gram) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            bg[s] = *reinterpret_cast<const u32x4 *>(&sm.u.kq[16 * w + n][32 * s + 8 * grp]);
     }
 
-    // ---- state products W = K.H0, Z = Q.H0 (fp32 VALU) ----
-    {
-        constexpr int RM = NM / 2;
-        const int c = tid & (D - 1), rg = tid >> 7;
-        float aw[RM], az[RM];
+    // ---- one MFMA pass: [K;Q] x [H0 | K^T] ----
+    f32x4 acc[MT][2], gacc[MT];
 #pragma unroll
-        for (int m = 0; m < RM; ++m) aw[m] = az[m] = 0.f;
-        const float *H = a.S0 + ((size_t)slot * a.Hv + h) * D * D;
-        for (int i0 = 0; i0 < D; i0 += 8) {
-            float hv[8];
+    for (int tau = 0; tau < MT; ++tau) {
+        acc[tau][0] = acc[tau][1] = gacc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tau < nmt) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) hv[e] = H[(i0 + e) * D + c];
+            for (int s = 0; s < 4; ++s) {
+                const u32x4 av = *reinterpret_cast<const u32x4 *>(&sm.u.kq[16 * tau + n][32 * s + 8 * grp]);
+                acc[tau][0] = mfma(av, bhi[s][0], acc[tau][0]);
+                acc[tau][1] = mfma(av, bhi[s][1], acc[tau][1]);
+                acc[tau][0] = mfma(av, blo[s][0], acc[tau][0]);
+                acc[tau][1] = mfma(av, blo[s][1], acc[tau][1]);
+                if (gram) gacc[tau] = mfma(av, bg[s], gacc[tau]);
+            }
+        }
+    }
+    lds_barrier();   // K/Q rows are dead from here; ru reuses their space
+
+    // ---- masked coefficient tables from the grams ----
+    if (gram) {
+        const int j = 16 * w + n;
 #pragma unroll
-            for (int m = 0; m < RM; ++m) {
-                const int t = rg + 2 * m;
-                if (t < N) {
-                    aw[m] = axpy8_bf16(*reinterpret_cast<const uint4 *>(&sm.K[t][i0]), hv, aw[m]);
-                    az[m] = axpy8_bf16(*reinterpret_cast<const uint4 *>(&sm.Q[t][i0]), hv, az[m]);
+        for (int tau = 0; tau < MT; ++tau) {
+            if (tau < nmt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * tau + 4 * grp + i;
+                    if (j < N && r < 2 * N) {
+                        const bool krow = r < N;
+                        const int t = krow ? r : r - N;
+                        const uint64_t at = sm.anc[t];
+                        if (((at >> j) & 1) && !(krow && j == t)) {
+                            uint64_t seg = at & ~sm.anc[j];
+                            float sg = 0.f;
+                            while (seg) {
+                                sg += sm.gl[__builtin_ctzll(seg)];
+                                seg &= seg - 1;
+                            }
+                            const float dtj = expf(sg);
+                            if (krow)
+                                sm.A[t][j] = sm.beta[t] * dtj * gacc[tau][i];
+                            else
+                                sm.P[t][j] = dtj * gacc[tau][i];
+                        }
+                    }
                 }
             }
         }
+    }
+    // ---- right-hand side R_t = beta_t (v_t - gamma_t W_t) ----
 #pragma unroll
-        for (int m = 0; m < RM; ++m) {
-            const int t = rg + 2 * m;
-            if (t < N) {
-                sm.W[t][c] = aw[m];
-                sm.Z[t][c] = az[m];
+    for (int tau = 0; tau < KT; ++tau) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * tau + 4 * grp + i;
+            if (r < N) {
+                const float bt = sm.beta[r], gm = sm.gam[r];
+                float2 rr;
+                rr.x = bt * (bf16_lo(vv[tau][i]) - gm * acc[tau][0][i]);
+                rr.y = bt * (bf16_hi(vv[tau][i]) - gm * acc[tau][1][i]);
+                *reinterpret_cast<float2 *>(&sm.u.ru[r][32 * w + 2 * n]) = rr;
             }
         }
     }
-    __syncthreads();
 
-    // ---- right-hand side R_t = beta_t (v_t - gamma_t W_t) ----
-    for (int idx = tid; idx < N * D; idx += NT) {
-        const int t = idx >> 7, c = idx & (D - 1);
-        const float vv = bf16_to_f32(a.v[((size_t)(lo + t) * a.Hv + h) * D + c]);
-        sm.W[t][c] = sm.beta[t] * (vv - sm.gam[t] * sm.W[t][c]);
-    }
     // ---- forward substitution over depth levels ----
     const int maxdep = sm.maxdep;
     for (int L = 2; L <= maxdep; ++L) {
-        __syncthreads();
+        lds_barrier();
         const int s0 = sm.lvl_start[L], cnt = sm.lvl_start[L + 1] - s0;
-        for (int idx = tid; idx < cnt * D; idx += NT) {
-            const int t = sm.lvl_nodes[s0 + (idx >> 7)], c = idx & (D - 1);
+        for (int idx = tid; idx < cnt * (D / 2); idx += NT) {
+            const int t = sm.lvl_nodes[s0 + (idx >> 6)], c = 2 * (idx & 63);
             uint64_t m = sm.anc[t] & ~(1ull << t);
-            float acc = sm.W[t][c];
+            float2 acc2 = *reinterpret_cast<const float2 *>(&sm.u.ru[t][c]);
             while (m) {
                 const int j = __builtin_ctzll(m);
-                acc = fmaf(-sm.A[t][j], sm.W[j][c], acc);
+                const float aj = sm.A[t][j];
+                const float2 uj = *reinterpret_cast<const float2 *>(&sm.u.ru[j][c]);
+                acc2.x = fmaf(-aj, uj.x, acc2.x);
+                acc2.y = fmaf(-aj, uj.y, acc2.y);
                 m &= m - 1;
             }
-            sm.W[t][c] = acc;
+            *reinterpret_cast<float2 *>(&sm.u.ru[t][c]) = acc2;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- outputs and pseudo-values ----
-    for (int idx = tid; idx < N * D; idx += NT) {
-        const int t = idx >> 7, c = idx & (D - 1);
-        const size_t o = ((size_t)(lo + t) * a.Hv + h) * D + c;
-        a.U[o] = sm.W[t][c];
-        float acc = sm.gam[t] * sm.Z[t][c];
-        uint64_t m = sm.anc[t];
-        while (m) {
-            const int j = __builtin_ctzll(m);
-            acc = fmaf(sm.P[t][j], sm.W[j][c], acc);
-            m &= m - 1;
+    // ---- pseudo-values out (coalesced rows) ----
+    for (int idx = tid; idx < N * (D / 4); idx += NT) {
+        const int t = idx >> 5, c4 = idx & 31;
+        reinterpret_cast<float4 *>(a.U + ((size_t)(lo + t) * a.Hv + h) * D)[c4] =
+            *reinterpret_cast<const float4 *>(&sm.u.ru[t][4 * c4]);
+    }
+    // ---- outputs o_t = gamma_t Z_t + sum_j D_tj QK_tj u_j, from the Z tiles ----
+#pragma unroll
+    for (int tau = 0; tau < MT; ++tau) {
+        if (tau < nmt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * tau + 4 * grp + i;
+                if (r >= N && r < 2 * N) {
+                    const int t = r - N;
+                    const int c = 32 * w + 2 * n;
+                    const float gm = sm.gam[t];
+                    float2 o;
+                    o.x = gm * acc[tau][0][i];
+                    o.y = gm * acc[tau][1][i];
+                    uint64_t m = sm.anc[t];
+                    while (m) {
+                        const int j = __builtin_ctzll(m);
+                        const float pj = sm.P[t][j];
+                        const float2 uj = *reinterpret_cast<const float2 *>(&sm.u.ru[j][c]);
+                        o.x = fmaf(pj, uj.x, o.x);
+                        o.y = fmaf(pj, uj.y, o.y);
+                        m &= m - 1;
+                    }
+                    *reinterpret_cast<float2 *>(a.out + ((size_t)(lo + t) * a.Hv + h) * D + c) = o;
+                }
+            }
         }
-        a.out[o] = acc;
     }
 }
 
