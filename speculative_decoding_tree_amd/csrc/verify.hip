@@ -13,18 +13,25 @@
 //   u_t = R_t - sum_{j in anc(t)} beta_t D_tj KK_tj u_j           (level by level)
 //   o_t = gamma_t Z_t + sum_{j in anc*(t)} D_tj QK_tj u_j
 //
+// The tree pre-pass (ancestry bitsets, G, depth levels) runs in wave 0 on
+// registers with pointer doubling and ballots while the other waves start
+// their MFMAs.
+//
 // gfx950 layout.  One workgroup (4 wave64) owns one (request, v-head) unit.
 // Wave w keeps its 128 x 32 column slab of H0 in registers as the B operand
 // of v_mfma_f32_16x16x32_bf16, split into bf16 hi + lo parts (q and k are
 // exact bf16, so two MFMAs with fp32 accumulation carry ~16 mantissa bits of
 // H0).  Lane (n, grp) of the wave loads float2 columns 32w + 2n, 2n+1 of rows
 // 32s + 8grp .. +7; the even columns form n-tile 0 and the odd ones n-tile 1,
-// so every load instruction reads whole 128-byte row segments.  The K and Q
-// rows of the unit are stacked (K rows 0..N-1, Q rows N..2N-1) in LDS as the A
-// operand; wave w also multiplies them by K^T for node columns 16w .. 16w+15,
-// which gives the masked grams.  The LDS block that held K/Q is reused for
-// R and then U.  H0, q/k, v and the per-node scalars are all requested before
-// the first barrier; barriers are LDS-only so those loads stay in flight.
+// so every load instruction reads whole 128-byte row segments.  A operands
+// (16-node tiles of K or Q rows) come straight from L2.  Pass 1 runs the K
+// tiles: W = K H0 becomes R in LDS, and wave w also multiplies K and Q tiles
+// by K^T for node columns 16w .. 16w+15 (the grams).  After the solve, pass 2
+// runs the Q tiles and turns each Z tile into outputs directly, so only one
+// tile of accumulators is ever live.  The grams share one LDS table: A_tj in
+// the strict lower triangle, P_tj stored transposed in the upper triangle.
+// H0, v and the per-node scalars are all requested before the first barrier;
+// barriers are LDS-only so those loads stay in flight.
 #include "common.h"
 #include "launch.h"
 
@@ -69,22 +76,31 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 
 template <int NM>
 struct VerifySmem {
-    union {
-        uint16_t kq[2 * NM][D + 8];   // A operand: K rows then Q rows (bf16)
-        float ru[NM][D + 4];          // R, then U after the solve
-    } u;
-    float A[NM][NM + 1];   // beta_t D_tj KK_tj for strict ancestors j
-    float P[NM][NM + 1];   // D_tj QK_tj for inclusive ancestors j
+    float ru[NM][D + 4];   // R, then U after the solve
+    float T[NM][NM + 1];   // [t][j], j < t: beta_t D_tj KK_tj;  [j][t], j <= t: D_tj QK_tj
     uint64_t anc[NM];
-    float gam[NM], beta[NM], gl[NM];
-    int par[NM], dep[NM], lvl_nodes[NM], lvl_start[NM + 2];
+    float gam[NM], beta[NM], G[NM];
+    int lvl_nodes[NM], lvl_start[NM + 2];
     int bad, maxdep;
 };
 
+// A or B fragment of a 16-node tile: lane (n, grp) gets row `row`, elements
+// 32 s + 8 grp .. +7 for s = 0..3 (16 bytes each); zero past the last node.
+__device__ __forceinline__ void load_rows(const uint16_t *base, size_t row_stride, int row, int nrows,
+                                          int grp, u32x4 (&f)[4]) {
+    if (row < nrows) {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(base + (size_t)row * row_stride + 8 * grp);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) f[s] = p[4 * s];
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) f[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
 template <int NM>
 __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
-    constexpr int MT = NM / 8;    // max M-tiles of 16 rows over 2N stacked rows
-    constexpr int KT = NM / 16;   // max M-tiles that can hold K rows
+    constexpr int KT = NM / 16;   // max 16-node tiles
     __shared__ VerifySmem<NM> sm;
 
     const int n_units = a.B * a.Hv;
@@ -96,6 +112,7 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int n = lane & 15, grp = lane >> 4;
+    const int c = 32 * w + 2 * n;   // this lane's column pair
 
     int lo, N;
     int st = check_offsets(a, b, lo, N);
@@ -104,41 +121,30 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
         return;
     }
     const int slot = resolve_slot(a, b);
-    const int nmt = (2 * N + 15) >> 4;
+    const int nkt = (N + 15) >> 4;
+    const size_t krow = (size_t)a.Hk * D;            // q/k row stride (elements)
+    const uint16_t *kbase = a.k + ((size_t)lo * a.Hk + hk) * D;
+    const uint16_t *qbase = a.q + ((size_t)lo * a.Hk + hk) * D;
 
-    // ---- issue every global read of the unit (nodes first, then H0 and v) ----
+    // ---- issue the unit's global reads: per-node scalars, H0, v ----
     int p_mine = -1;
     float g_mine = 0.f, b_mine = 0.f;
-    constexpr int KQ_PER_T = (2 * NM * 16 + NT - 1) / NT;   // 16-byte pieces per lane
-    uint4 kq_stage[KQ_PER_T];
     float2 hraw[4][8];
     uint32_t vv[KT][4];
-    const bool ok = (st == GDN_TREE_S_OK);
-    if (ok) {
+    if (st == GDN_TREE_S_OK) {
         if (tid < N) {
             const size_t gi = (size_t)(lo + tid) * a.Hv + h;
             p_mine = a.parent[lo + tid];
             g_mine = a.g[gi];
             b_mine = a.beta[gi];
         }
-#pragma unroll
-        for (int e = 0; e < KQ_PER_T; ++e) {
-            const int idx = tid + e * NT;
-            const int r = idx >> 4, c8 = idx & 15;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (r < N)
-                val = reinterpret_cast<const uint4 *>(a.k + ((size_t)(lo + r) * a.Hk + hk) * D)[c8];
-            else if (r < 2 * N)
-                val = reinterpret_cast<const uint4 *>(a.q + ((size_t)(lo + r - N) * a.Hk + hk) * D)[c8];
-            kq_stage[e] = val;
-        }
         if (slot >= 0) {
-            const float *H = a.S0 + ((size_t)slot * a.Hv + h) * D * D + 32 * w + 2 * n;
+            const float *H = a.S0 + ((size_t)slot * a.Hv + h) * D * D + 8 * grp * D + c;
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    hraw[s][e] = *reinterpret_cast<const float2 *>(H + (32 * s + 8 * grp + e) * D);
+                    hraw[s][e] = *reinterpret_cast<const float2 *>(H + (32 * s + e) * D);
         }
 #pragma unroll
         for (int tau = 0; tau < KT; ++tau)
@@ -147,25 +153,13 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
                 const int r = 16 * tau + 4 * grp + i;
                 vv[tau][i] = 0;
                 if (r < N)
-                    vv[tau][i] = *reinterpret_cast<const uint32_t *>(
-                        a.v + ((size_t)(lo + r) * a.Hv + h) * D + 32 * w + 2 * n);
+                    vv[tau][i] = *reinterpret_cast<const uint32_t *>(a.v + ((size_t)(lo + r) * a.Hv + h) * D + c);
             }
-        // parents, gates and K/Q rows into LDS
-        if (tid < N) {
-            sm.par[tid] = p_mine;
-            sm.gl[tid] = g_mine;
-            sm.beta[tid] = b_mine;
-        }
+        if (tid < N) sm.beta[tid] = b_mine;
         if (w == 0) {
             const bool bad = (tid < N) && (p_mine < -1 || p_mine >= tid);
             const unsigned long long any = __ballot(bad);
             if (lane == 0) sm.bad = any != 0ull;
-        }
-#pragma unroll
-        for (int e = 0; e < KQ_PER_T; ++e) {
-            const int idx = tid + e * NT;
-            const int r = idx >> 4, c8 = idx & 15;
-            if (r < 16 * nmt) *reinterpret_cast<uint4 *>(&sm.u.kq[r][c8 * 8]) = kq_stage[e];
         }
         lds_barrier();
         if (sm.bad) st = GDN_TREE_S_BAD_PARENT;
@@ -188,38 +182,52 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
     if (h == 0 && tid == 0 && a.status) a.status[b] = GDN_TREE_S_OK;
     if (N == 0) return;
 
-    // ---- tree pre-pass: ancestry bitsets and depths ----
-    if (tid < N) {
-        uint64_t m = 0;
-        for (int j = tid; j >= 0; j = sm.par[j]) m |= 1ull << j;
-        sm.anc[tid] = m;
-        sm.dep[tid] = __popcll(m);
-        if (h == 0 && a.anc_mask) a.anc_mask[lo + tid] = m;
-    }
-    lds_barrier();
-    if (tid < N) {
-        uint64_t m = sm.anc[tid];
-        float G = 0.f;
-        while (m) {
-            G += sm.gl[__builtin_ctzll(m)];
-            m &= m - 1;
+    // ---- tree pre-pass in wave 0, lane t = node t, registers only ----
+    // Pointer doubling: m is the set of nodes from t up to (excluding) jp and
+    // G the sum of their gates; each round joins the segment above, so
+    // ceil(log2(depth)) + 1 rounds give the inclusive ancestor set and the
+    // path-cumulative log-decay G_t.
+    if (w == 0) {
+        const bool live = lane < N;
+        int jp = live ? p_mine : -1;
+        uint64_t m = live ? (1ull << lane) : 0ull;
+        float G = live ? g_mine : 0.f;
+        while (__ballot(jp >= 0)) {
+            const int src = jp >= 0 ? jp : lane;
+            const uint64_t m_up = __shfl(m, src);
+            const float G_up = __shfl(G, src);
+            const int jp_up = __shfl(jp, src);
+            if (jp >= 0) {
+                m |= m_up;
+                G += G_up;
+                jp = jp_up;
+            }
         }
-        sm.gam[tid] = expf(G);
-    }
-    if (tid == 0) {  // nodes grouped by depth (counting sort, N <= 64)
-        int maxd = 0;
-        for (int t = 0; t < N; ++t) maxd = max(maxd, sm.dep[t]);
-        int pos = 0;
-        for (int d = 1; d <= maxd; ++d) {
-            sm.lvl_start[d] = pos;
-            for (int t = 0; t < N; ++t)
-                if (sm.dep[t] == d) sm.lvl_nodes[pos++] = t;
+        const int dep = live ? __popcll(m) : 0;
+        int maxd = dep;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) maxd = max(maxd, __shfl_xor(maxd, off));
+        int base = 0, pos = 0;
+        for (int d = 1; d <= maxd; ++d) {   // nodes grouped by depth, index order inside
+            const uint64_t mk = __ballot(dep == d);
+            if (dep == d) pos = base + __popcll(mk & ((1ull << lane) - 1ull));
+            if (lane == 0) sm.lvl_start[d] = base;
+            base += __popcll(mk);
         }
-        sm.lvl_start[maxd + 1] = pos;
-        sm.maxdep = maxd;
+        if (lane == 0) {
+            sm.lvl_start[maxd + 1] = base;
+            sm.maxdep = maxd;
+        }
+        if (live) {
+            sm.anc[lane] = m;
+            sm.G[lane] = G;
+            sm.gam[lane] = expf(G);
+            sm.lvl_nodes[pos] = lane;
+            if (h == 0 && a.anc_mask) a.anc_mask[lo + lane] = m;
+        }
     }
 
-    // ---- B operands: H0 slab (hi, lo) and K^T for node columns 16w.. ----
+    // ---- B operands: H0 slab (hi, lo); K^T for node columns 16w .. 16w+15 ----
     u32x4 bhi[4][2], blo[4][2], bg[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -235,74 +243,76 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
         }
     }
     const bool gram = 16 * w < N;
-    if (gram) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            bg[s] = *reinterpret_cast<const u32x4 *>(&sm.u.kq[16 * w + n][32 * s + 8 * grp]);
-    }
+    const int jcol = 16 * w + n;   // gram column (node) of this lane
+    if (gram) load_rows(kbase, krow, jcol, N, grp, bg);
+    lds_barrier();   // ancestry, G, gamma, levels visible
 
-    // ---- one MFMA pass: [K;Q] x [H0 | K^T] ----
-    f32x4 acc[MT][2], gacc[MT];
+    // ---- pass 1: K tiles -> R rows and raw K.K^T; Q tiles -> raw Q.K^T ----
 #pragma unroll
-    for (int tau = 0; tau < MT; ++tau) {
-        acc[tau][0] = acc[tau][1] = gacc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (tau < nmt) {
+    for (int tau = 0; tau < KT; ++tau) {
+        if (tau < nkt) {
+            u32x4 af[4];
+            load_rows(kbase, krow, 16 * tau + n, N, grp, af);
+            f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0, gk = w0;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const u32x4 av = *reinterpret_cast<const u32x4 *>(&sm.u.kq[16 * tau + n][32 * s + 8 * grp]);
-                acc[tau][0] = mfma(av, bhi[s][0], acc[tau][0]);
-                acc[tau][1] = mfma(av, bhi[s][1], acc[tau][1]);
-                acc[tau][0] = mfma(av, blo[s][0], acc[tau][0]);
-                acc[tau][1] = mfma(av, blo[s][1], acc[tau][1]);
-                if (gram) gacc[tau] = mfma(av, bg[s], gacc[tau]);
+                w0 = mfma(af[s], bhi[s][0], w0);
+                w1 = mfma(af[s], bhi[s][1], w1);
+                w0 = mfma(af[s], blo[s][0], w0);
+                w1 = mfma(af[s], blo[s][1], w1);
+                if (gram) gk = mfma(af[s], bg[s], gk);
             }
-        }
-    }
-    lds_barrier();   // K/Q rows are dead from here; ru reuses their space
-
-    // ---- masked coefficient tables from the grams ----
-    if (gram) {
-        const int j = 16 * w + n;
 #pragma unroll
-        for (int tau = 0; tau < MT; ++tau) {
-            if (tau < nmt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * tau + 4 * grp + i;
-                    if (j < N && r < 2 * N) {
-                        const bool krow = r < N;
-                        const int t = krow ? r : r - N;
-                        const uint64_t at = sm.anc[t];
-                        if (((at >> j) & 1) && !(krow && j == t)) {
-                            uint64_t seg = at & ~sm.anc[j];
-                            float sg = 0.f;
-                            while (seg) {
-                                sg += sm.gl[__builtin_ctzll(seg)];
-                                seg &= seg - 1;
-                            }
-                            const float dtj = expf(sg);
-                            if (krow)
-                                sm.A[t][j] = sm.beta[t] * dtj * gacc[tau][i];
-                            else
-                                sm.P[t][j] = dtj * gacc[tau][i];
-                        }
-                    }
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * tau + 4 * grp + i;
+                if (r < N) {
+                    const float bt = sm.beta[r], gm = sm.gam[r];
+                    float2 rr;
+                    rr.x = bt * (bf16_lo(vv[tau][i]) - gm * w0[i]);
+                    rr.y = bt * (bf16_hi(vv[tau][i]) - gm * w1[i]);
+                    *reinterpret_cast<float2 *>(&sm.ru[r][c]) = rr;
+                    if (gram && jcol < r) sm.T[r][jcol] = gk[i];
                 }
             }
         }
     }
-    // ---- right-hand side R_t = beta_t (v_t - gamma_t W_t) ----
+    if (gram) {
 #pragma unroll
-    for (int tau = 0; tau < KT; ++tau) {
+        for (int tau = 0; tau < KT; ++tau) {
+            if (tau < nkt) {
+                u32x4 af[4];
+                load_rows(qbase, krow, 16 * tau + n, N, grp, af);
+                f32x4 gq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * tau + 4 * grp + i;
-            if (r < N) {
-                const float bt = sm.beta[r], gm = sm.gam[r];
-                float2 rr;
-                rr.x = bt * (bf16_lo(vv[tau][i]) - gm * acc[tau][0][i]);
-                rr.y = bt * (bf16_hi(vv[tau][i]) - gm * acc[tau][1][i]);
-                *reinterpret_cast<float2 *>(&sm.u.ru[r][32 * w + 2 * n]) = rr;
+                for (int s = 0; s < 4; ++s) gq = mfma(af[s], bg[s], gq);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * tau + 4 * grp + i;
+                    if (t < N && jcol <= t) sm.T[jcol][t] = gq[i];
+                }
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- decay and beta factors on the ancestor entries only ----
+    if (w < 2 && lane < N) {
+        const int t = lane;
+        const float Gt = sm.G[t];
+        uint64_t m = sm.anc[t];
+        if (w == 0) {
+            const float bt = sm.beta[t];
+            m &= ~(1ull << t);
+            while (m) {
+                const int j = __builtin_ctzll(m);
+                sm.T[t][j] *= bt * expf(Gt - sm.G[j]);
+                m &= m - 1;
+            }
+        } else {
+            while (m) {
+                const int j = __builtin_ctzll(m);
+                sm.T[j][t] *= expf(Gt - sm.G[j]);
+                m &= m - 1;
             }
         }
     }
@@ -313,18 +323,18 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
         lds_barrier();
         const int s0 = sm.lvl_start[L], cnt = sm.lvl_start[L + 1] - s0;
         for (int idx = tid; idx < cnt * (D / 2); idx += NT) {
-            const int t = sm.lvl_nodes[s0 + (idx >> 6)], c = 2 * (idx & 63);
+            const int t = sm.lvl_nodes[s0 + (idx >> 6)], cc = 2 * (idx & 63);
             uint64_t m = sm.anc[t] & ~(1ull << t);
-            float2 acc2 = *reinterpret_cast<const float2 *>(&sm.u.ru[t][c]);
+            float2 acc2 = *reinterpret_cast<const float2 *>(&sm.ru[t][cc]);
             while (m) {
                 const int j = __builtin_ctzll(m);
-                const float aj = sm.A[t][j];
-                const float2 uj = *reinterpret_cast<const float2 *>(&sm.u.ru[j][c]);
+                const float aj = sm.T[t][j];
+                const float2 uj = *reinterpret_cast<const float2 *>(&sm.ru[j][cc]);
                 acc2.x = fmaf(-aj, uj.x, acc2.x);
                 acc2.y = fmaf(-aj, uj.y, acc2.y);
                 m &= m - 1;
             }
-            *reinterpret_cast<float2 *>(&sm.u.ru[t][c]) = acc2;
+            *reinterpret_cast<float2 *>(&sm.ru[t][cc]) = acc2;
         }
     }
     lds_barrier();
@@ -333,27 +343,35 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
     for (int idx = tid; idx < N * (D / 4); idx += NT) {
         const int t = idx >> 5, c4 = idx & 31;
         reinterpret_cast<float4 *>(a.U + ((size_t)(lo + t) * a.Hv + h) * D)[c4] =
-            *reinterpret_cast<const float4 *>(&sm.u.ru[t][4 * c4]);
+            *reinterpret_cast<const float4 *>(&sm.ru[t][4 * c4]);
     }
-    // ---- outputs o_t = gamma_t Z_t + sum_j D_tj QK_tj u_j, from the Z tiles ----
+    // ---- pass 2: Q tiles -> Z -> o_t = gamma_t Z_t + sum_j D_tj QK_tj u_j ----
 #pragma unroll
-    for (int tau = 0; tau < MT; ++tau) {
-        if (tau < nmt) {
+    for (int tau = 0; tau < KT; ++tau) {
+        if (tau < nkt) {
+            u32x4 af[4];
+            load_rows(qbase, krow, 16 * tau + n, N, grp, af);
+            f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = z0;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                z0 = mfma(af[s], bhi[s][0], z0);
+                z1 = mfma(af[s], bhi[s][1], z1);
+                z0 = mfma(af[s], blo[s][0], z0);
+                z1 = mfma(af[s], blo[s][1], z1);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * tau + 4 * grp + i;
-                if (r >= N && r < 2 * N) {
-                    const int t = r - N;
-                    const int c = 32 * w + 2 * n;
+                const int t = 16 * tau + 4 * grp + i;
+                if (t < N) {
                     const float gm = sm.gam[t];
                     float2 o;
-                    o.x = gm * acc[tau][0][i];
-                    o.y = gm * acc[tau][1][i];
+                    o.x = gm * z0[i];
+                    o.y = gm * z1[i];
                     uint64_t m = sm.anc[t];
                     while (m) {
                         const int j = __builtin_ctzll(m);
-                        const float pj = sm.P[t][j];
-                        const float2 uj = *reinterpret_cast<const float2 *>(&sm.u.ru[j][c]);
+                        const float pj = sm.T[j][t];
+                        const float2 uj = *reinterpret_cast<const float2 *>(&sm.ru[j][c]);
                         o.x = fmaf(pj, uj.x, o.x);
                         o.y = fmaf(pj, uj.y, o.y);
                         m &= m - 1;
