@@ -24,14 +24,14 @@
 // H0).  Lane (n, grp) of the wave loads float2 columns 32w + 2n, 2n+1 of rows
 // 32s + 8grp .. +7; the even columns form n-tile 0 and the odd ones n-tile 1,
 // so every load instruction reads whole 128-byte row segments.  A operands
-// (16-node tiles of K or Q rows) come straight from L2.  Pass 1 runs the K
-// tiles: W = K H0 becomes R in LDS, and wave w also multiplies K and Q tiles
-// by K^T for node columns 16w .. 16w+15 (the grams).  After the solve, pass 2
-// runs the Q tiles and turns each Z tile into outputs directly, so only one
-// tile of accumulators is ever live.  The grams share one LDS table: A_tj in
-// the strict lower triangle, P_tj stored transposed in the upper triangle.
-// H0, v and the per-node scalars are all requested before the first barrier;
-// barriers are LDS-only so those loads stay in flight.
+// (16-node tiles of K or Q rows) come straight from L2.  One MFMA pass over
+// the tiles gives W = K H0 (turned into R in LDS at once), Z = Q H0 (kept in
+// registers until the outputs) and, in wave w, the grams against K^T for node
+// columns 16w .. 16w+15, whose ancestor entries are scaled on the spot into a
+// coefficient table.  That pass ends with the only workgroup barrier after
+// the tree pre-pass: the solve and the outputs are independent per column,
+// so each wave finishes its own 32 columns alone (LDS operations of one wave
+// complete in order, so one level's writes are seen by the next level).
 #include "common.h"
 #include "launch.h"
 
@@ -74,17 +74,33 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Coefficient table T is indexed by ancestor position: the ancestor j of t
+// at depth dep(j) sits at position q = dep(j) - 1 of t's root-first list.
+//   T[t][q], q < dep(t) - 1 : A = beta_t D_tj (k_t.k_j)   (strict lower triangle)
+//   T[q][t], q < dep(t)     : P = D_tj (q_t.k_j)           (upper triangle)
+// alistT[q][t] is the node at position q of t's list (root first).
+// Coefficient table T is indexed by ancestor position: the ancestor j of t
+// at depth dep(j) sits at position q = dep(j) - 1 of t's root-first list.
+//   T[t][q], q < dep(t) - 1 : A = beta_t D_tj (k_t.k_j)   (strict lower triangle)
+//   T[q][t], q < dep(t)     : P = D_tj (q_t.k_j)           (upper triangle)
 template <int NM>
 struct VerifySmem {
-    float ru[NM][D + 4];   // R, then U after the solve
-    float T[NM][NM + 1];   // [t][j], j < t: beta_t D_tj KK_tj;  [j][t], j <= t: D_tj QK_tj
-    uint64_t anc[NM];
-    float gam[NM], beta[NM], G[NM];
+    float ru[NM][D + 4];                       // R, then U after the solve
+    float T[NM][NM];
+    __attribute__((aligned(16))) uint64_t anc[NM];
+    __attribute__((aligned(16))) float gam[NM];
+    __attribute__((aligned(16))) float beta[NM];
+    __attribute__((aligned(16))) float G2[NM];   // log2(e) * path-cumulative log-decay
+    __attribute__((aligned(16))) int dep[NM];
     int lvl_nodes[NM], lvl_start[NM + 2];
     int bad, maxdep;
 };
 
-// A or B fragment of a 16-node tile: lane (n, grp) gets row `row`, elements
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A fragment of a 16-node tile: lane (n, grp) gets row `row`, elements
 // 32 s + 8 grp .. +7 for s = 0..3 (16 bytes each); zero past the last node.
 __device__ __forceinline__ void load_rows(const uint16_t *base, size_t row_stride, int row, int nrows,
                                           int grp, u32x4 (&f)[4]) {
@@ -121,8 +137,7 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
         return;
     }
     const int slot = resolve_slot(a, b);
-    const int nkt = (N + 15) >> 4;
-    const size_t krow = (size_t)a.Hk * D;            // q/k row stride (elements)
+    const size_t krow = (size_t)a.Hk * D;   // q/k row stride (elements)
     const uint16_t *kbase = a.k + ((size_t)lo * a.Hk + hk) * D;
     const uint16_t *qbase = a.q + ((size_t)lo * a.Hk + hk) * D;
 
@@ -131,13 +146,12 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
     float g_mine = 0.f, b_mine = 0.f;
     float2 hraw[4][8];
     uint32_t vv[KT][4];
-    if (st == GDN_TREE_S_OK) {
-        if (tid < N) {
-            const size_t gi = (size_t)(lo + tid) * a.Hv + h;
-            p_mine = a.parent[lo + tid];
-            g_mine = a.g[gi];
-            b_mine = a.beta[gi];
-        }
+    if (st == GDN_TREE_S_OK && N > 0) {
+        const int tc = min(tid, N - 1);
+        const size_t gi = (size_t)(lo + tc) * a.Hv + h;
+        p_mine = a.parent[lo + tc];
+        g_mine = a.g[gi];
+        b_mine = a.beta[gi];
         if (slot >= 0) {
             const float *H = a.S0 + ((size_t)slot * a.Hv + h) * D * D + 8 * grp * D + c;
 #pragma unroll
@@ -146,15 +160,13 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
                 for (int e = 0; e < 8; ++e)
                     hraw[s][e] = *reinterpret_cast<const float2 *>(H + (32 * s + e) * D);
         }
+        const uint16_t *V = a.v + ((size_t)lo * a.Hv + h) * D + c;
+        const size_t vrow = (size_t)a.Hv * D;
 #pragma unroll
         for (int tau = 0; tau < KT; ++tau)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * tau + 4 * grp + i;
-                vv[tau][i] = 0;
-                if (r < N)
-                    vv[tau][i] = *reinterpret_cast<const uint32_t *>(a.v + ((size_t)(lo + r) * a.Hv + h) * D + c);
-            }
+            for (int i = 0; i < 4; ++i)   // rows past N read the last row; their R rows are never used
+                vv[tau][i] = *reinterpret_cast<const uint32_t *>(V + (size_t)min(16 * tau + 4 * grp + i, N - 1) * vrow);
         if (tid < N) sm.beta[tid] = b_mine;
         if (w == 0) {
             const bool bad = (tid < N) && (p_mine < -1 || p_mine >= tid);
@@ -218,16 +230,20 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
             sm.lvl_start[maxd + 1] = base;
             sm.maxdep = maxd;
         }
-        if (live) {
+        if (lane < NM) {   // rows past N get empty ancestry so no coefficient is written for them
+            const float G2 = G * LOG2E;
             sm.anc[lane] = m;
-            sm.G[lane] = G;
-            sm.gam[lane] = expf(G);
+            sm.G2[lane] = G2;
+            sm.gam[lane] = exp2_fast(G2);
+            sm.dep[lane] = dep;
+        }
+        if (live) {
             sm.lvl_nodes[pos] = lane;
             if (h == 0 && a.anc_mask) a.anc_mask[lo + lane] = m;
         }
     }
 
-    // ---- B operands: H0 slab (hi, lo); K^T for node columns 16w .. 16w+15 ----
+    // ---- B operands: H0 slab (hi, lo) and K^T for node columns 16w .. 16w+15 ----
     u32x4 bhi[4][2], blo[4][2], bg[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -245,149 +261,180 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
     const bool gram = 16 * w < N;
     const int jcol = 16 * w + n;   // gram column (node) of this lane
     if (gram) load_rows(kbase, krow, jcol, N, grp, bg);
-    lds_barrier();   // ancestry, G, gamma, levels visible
+    lds_barrier();   // ancestry, G, gamma, depths, levels visible
 
-    // ---- pass 1: K tiles -> R rows and raw K.K^T; Q tiles -> raw Q.K^T ----
+    // ---- one MFMA pass: K tiles -> R, Q tiles -> Z (registers), grams -> T ----
+    const int nkt = (N + 15) >> 4;
+    const float G2_j = gram && jcol < N ? sm.G2[jcol] : 0.f;
+    const int qj = gram && jcol < N ? sm.dep[jcol] - 1 : 0;   // position of node jcol in its descendants' lists
+    f32x4 zt[KT][2];
 #pragma unroll
-    for (int tau = 0; tau < KT; ++tau) {
+    for (int tau = 0; tau < KT; ++tau) {   // K tiles: R rows and A entries
         if (tau < nkt) {
-            u32x4 af[4];
-            load_rows(kbase, krow, 16 * tau + n, N, grp, af);
+            u32x4 ak[4];
+            load_rows(kbase, krow, 16 * tau + n, N, grp, ak);
             f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0, gk = w0;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                w0 = mfma(af[s], bhi[s][0], w0);
-                w1 = mfma(af[s], bhi[s][1], w1);
-                w0 = mfma(af[s], blo[s][0], w0);
-                w1 = mfma(af[s], blo[s][1], w1);
-                if (gram) gk = mfma(af[s], bg[s], gk);
+                w0 = mfma(ak[s], bhi[s][0], w0);
+                w1 = mfma(ak[s], bhi[s][1], w1);
+                w0 = mfma(ak[s], blo[s][0], w0);
+                w1 = mfma(ak[s], blo[s][1], w1);
+                if (gram) gk = mfma(ak[s], bg[s], gk);
             }
+            // rows r0 .. r0+3 of this lane (rows past N are scratch rows of ru)
+            const int r0 = 16 * tau + 4 * grp;
+            const float4 bt4 = *reinterpret_cast<const float4 *>(&sm.beta[r0]);
+            const float4 gm4 = *reinterpret_cast<const float4 *>(&sm.gam[r0]);
+            const float4 g24 = *reinterpret_cast<const float4 *>(&sm.G2[r0]);
+            const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+            const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
+            const float g2[4] = {g24.x, g24.y, g24.z, g24.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * tau + 4 * grp + i;
-                if (r < N) {
-                    const float bt = sm.beta[r], gm = sm.gam[r];
-                    float2 rr;
-                    rr.x = bt * (bf16_lo(vv[tau][i]) - gm * w0[i]);
-                    rr.y = bt * (bf16_hi(vv[tau][i]) - gm * w1[i]);
-                    *reinterpret_cast<float2 *>(&sm.ru[r][c]) = rr;
-                    if (gram && jcol < r) sm.T[r][jcol] = gk[i];
-                }
+                const int r = r0 + i;
+                float2 rr;
+                rr.x = bt[i] * (bf16_lo(vv[tau][i]) - gm[i] * w0[i]);
+                rr.y = bt[i] * (bf16_hi(vv[tau][i]) - gm[i] * w1[i]);
+                *reinterpret_cast<float2 *>(&sm.ru[r][c]) = rr;
+                // strict ancestor jcol of r: A = beta_r D_rj (k_r.k_j) at position dep(j)-1
+                if (gram && jcol < r && ((sm.anc[r] >> jcol) & 1ull))
+                    sm.T[r][qj] = bt[i] * exp2_fast(g2[i] - G2_j) * gk[i];
             }
         }
+        __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
     }
-    if (gram) {
 #pragma unroll
-        for (int tau = 0; tau < KT; ++tau) {
-            if (tau < nkt) {
-                u32x4 af[4];
-                load_rows(qbase, krow, 16 * tau + n, N, grp, af);
-                f32x4 gq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) gq = mfma(af[s], bg[s], gq);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * tau + 4 * grp + i;
-                    if (t < N && jcol <= t) sm.T[jcol][t] = gq[i];
-                }
-            }
-        }
-    }
-    lds_barrier();
-
-    // ---- decay and beta factors on the ancestor entries only ----
-    if (w < 2 && lane < N) {
-        const int t = lane;
-        const float Gt = sm.G[t];
-        uint64_t m = sm.anc[t];
-        if (w == 0) {
-            const float bt = sm.beta[t];
-            m &= ~(1ull << t);
-            while (m) {
-                const int j = __builtin_ctzll(m);
-                sm.T[t][j] *= bt * expf(Gt - sm.G[j]);
-                m &= m - 1;
-            }
-        } else {
-            while (m) {
-                const int j = __builtin_ctzll(m);
-                sm.T[j][t] *= expf(Gt - sm.G[j]);
-                m &= m - 1;
-            }
-        }
-    }
-
-    // ---- forward substitution over depth levels ----
-    const int maxdep = sm.maxdep;
-    for (int L = 2; L <= maxdep; ++L) {
-        lds_barrier();
-        const int s0 = sm.lvl_start[L], cnt = sm.lvl_start[L + 1] - s0;
-        for (int idx = tid; idx < cnt * (D / 2); idx += NT) {
-            const int t = sm.lvl_nodes[s0 + (idx >> 6)], cc = 2 * (idx & 63);
-            uint64_t m = sm.anc[t] & ~(1ull << t);
-            float2 acc2 = *reinterpret_cast<const float2 *>(&sm.ru[t][cc]);
-            while (m) {
-                const int j = __builtin_ctzll(m);
-                const float aj = sm.T[t][j];
-                const float2 uj = *reinterpret_cast<const float2 *>(&sm.ru[j][cc]);
-                acc2.x = fmaf(-aj, uj.x, acc2.x);
-                acc2.y = fmaf(-aj, uj.y, acc2.y);
-                m &= m - 1;
-            }
-            *reinterpret_cast<float2 *>(&sm.ru[t][cc]) = acc2;
-        }
-    }
-    lds_barrier();
-
-    // ---- pseudo-values out (coalesced rows) ----
-    for (int idx = tid; idx < N * (D / 4); idx += NT) {
-        const int t = idx >> 5, c4 = idx & 31;
-        reinterpret_cast<float4 *>(a.U + ((size_t)(lo + t) * a.Hv + h) * D)[c4] =
-            *reinterpret_cast<const float4 *>(&sm.ru[t][4 * c4]);
-    }
-    // ---- pass 2: Q tiles -> Z -> o_t = gamma_t Z_t + sum_j D_tj QK_tj u_j ----
-#pragma unroll
-    for (int tau = 0; tau < KT; ++tau) {
+    for (int tau = 0; tau < KT; ++tau) {   // Q tiles: Z kept in registers, P entries
+        zt[tau][0] = zt[tau][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (tau < nkt) {
-            u32x4 af[4];
-            load_rows(qbase, krow, 16 * tau + n, N, grp, af);
-            f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = z0;
+            u32x4 aq[4];
+            load_rows(qbase, krow, 16 * tau + n, N, grp, aq);
+            f32x4 gq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                z0 = mfma(af[s], bhi[s][0], z0);
-                z1 = mfma(af[s], bhi[s][1], z1);
-                z0 = mfma(af[s], blo[s][0], z0);
-                z1 = mfma(af[s], blo[s][1], z1);
+                zt[tau][0] = mfma(aq[s], bhi[s][0], zt[tau][0]);
+                zt[tau][1] = mfma(aq[s], bhi[s][1], zt[tau][1]);
+                zt[tau][0] = mfma(aq[s], blo[s][0], zt[tau][0]);
+                zt[tau][1] = mfma(aq[s], blo[s][1], zt[tau][1]);
+                if (gram) gq = mfma(aq[s], bg[s], gq);
             }
+            if (gram) {
+                const int r0 = 16 * tau + 4 * grp;
+                const float4 g24 = *reinterpret_cast<const float4 *>(&sm.G2[r0]);
+                const float g2[4] = {g24.x, g24.y, g24.z, g24.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tau + 4 * grp + i;
-                if (t < N) {
-                    const float gm = sm.gam[t];
-                    float2 o;
-                    o.x = gm * z0[i];
-                    o.y = gm * z1[i];
-                    uint64_t m = sm.anc[t];
-                    while (m) {
-                        const int j = __builtin_ctzll(m);
-                        const float pj = sm.T[j][t];
-                        const float2 uj = *reinterpret_cast<const float2 *>(&sm.ru[j][c]);
-                        o.x = fmaf(pj, uj.x, o.x);
-                        o.y = fmaf(pj, uj.y, o.y);
-                        m &= m - 1;
-                    }
-                    *reinterpret_cast<float2 *>(a.out + ((size_t)(lo + t) * a.Hv + h) * D + c) = o;
+                for (int i = 0; i < 4; ++i) {
+                    // inclusive ancestor jcol of r: P = D_rj (q_r.k_j) at [dep(j)-1][r]
+                    const int r = r0 + i;
+                    if (jcol < N && ((sm.anc[r] >> jcol) & 1ull)) sm.T[qj][r] = exp2_fast(g2[i] - G2_j) * gq[i];
                 }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();   // R rows and every coefficient visible; from here each wave works alone
+
+    // ---- forward substitution over depth levels, this wave's 32 columns ----
+    // Lane (k, p) = (lane >> 4, lane & 15) takes node k of each group of four
+    // nodes of the level and the column pair c = 32w + 2p.  U rows go to HBM
+    // as soon as their level is done.
+    {
+        const int kk = lane >> 4;   // == grp
+        const int maxdep = sm.maxdep;
+        const size_t ustride = (size_t)a.Hv * D;
+        float *Ubase = a.U + ((size_t)lo * a.Hv + h) * D + c;
+        for (int L = 1; L <= maxdep; ++L) {
+            const int s0 = sm.lvl_start[L], cnt = sm.lvl_start[L + 1] - s0;
+            for (int g0 = 0; g0 < cnt; g0 += 4) {
+                if (g0 + kk < cnt) {
+                    const int t = sm.lvl_nodes[s0 + g0 + kk];
+                    float2 acc2 = *reinterpret_cast<const float2 *>(&sm.ru[t][c]);
+                    uint64_t m = sm.anc[t] & ~(1ull << t);   // the L-1 strict ancestors, root first
+                    for (int q = 0; q < L - 1; ++q) {
+                        const int j = __builtin_ctzll(m);
+                        m &= m - 1;
+                        const float aj = sm.T[t][q];
+                        const float2 uj = *reinterpret_cast<const float2 *>(&sm.ru[j][c]);
+                        acc2.x = fmaf(-aj, uj.x, acc2.x);
+                        acc2.y = fmaf(-aj, uj.y, acc2.y);
+                    }
+                    if (L > 1) *reinterpret_cast<float2 *>(&sm.ru[t][c]) = acc2;
+                    *reinterpret_cast<float2 *>(Ubase + (size_t)t * ustride) = acc2;
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+
+    // ---- outputs o_t = gamma_t Z_t + sum_{j in anc*(t)} P_tj u_j, every tile at once ----
+    {
+        int deps[KT][4];
+        uint64_t am[KT][4];
+        int dmax = 0;
+#pragma unroll
+        for (int tau = 0; tau < KT; ++tau) {
+            const int r0 = 16 * tau + 4 * grp;
+            if (tau < nkt) {
+                const float4 gm4 = *reinterpret_cast<const float4 *>(&sm.gam[r0]);
+                const int4 dp4 = *reinterpret_cast<const int4 *>(&sm.dep[r0]);
+                const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
+                const int dp[4] = {dp4.x, dp4.y, dp4.z, dp4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    deps[tau][i] = r0 + i < N ? dp[i] : 0;
+                    am[tau][i] = sm.anc[r0 + i];
+                    dmax = max(dmax, deps[tau][i]);
+                    zt[tau][0][i] *= gm[i];
+                    zt[tau][1][i] *= gm[i];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    deps[tau][i] = 0;
+                    am[tau][i] = 0;
+                }
+            }
+        }
+        for (int q = 0; q < dmax; ++q) {   // position q of every row's ancestor list
+#pragma unroll
+            for (int tau = 0; tau < KT; ++tau) {
+                if (tau < nkt) {
+                    const int r0 = 16 * tau + 4 * grp;
+                    const float4 p4 = *reinterpret_cast<const float4 *>(&sm.T[q][r0]);
+                    const float pj[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (q < deps[tau][i]) {
+                            const int j = __builtin_ctzll(am[tau][i]);
+                            am[tau][i] &= am[tau][i] - 1;
+                            const float2 uj = *reinterpret_cast<const float2 *>(&sm.ru[j][c]);
+                            zt[tau][0][i] = fmaf(pj[i], uj.x, zt[tau][0][i]);
+                            zt[tau][1][i] = fmaf(pj[i], uj.y, zt[tau][1][i]);
+                        }
+                    }
+                }
+            }
+        }
+        const size_t ostride = (size_t)a.Hv * D;
+        float *Obase = a.out + ((size_t)lo * a.Hv + h) * D + c;
+#pragma unroll
+        for (int tau = 0; tau < KT; ++tau)
+            if (tau < nkt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * tau + 4 * grp + i;
+                    if (r < N)
+                        *reinterpret_cast<float2 *>(Obase + (size_t)r * ostride) =
+                            make_float2(zt[tau][0][i], zt[tau][1][i]);
+                }
     }
 }
 
 }  // namespace
 
 hipError_t launch_verify(const Args &a, hipStream_t stream) {
-    const int n_units = a.B * a.Hv;
-    const dim3 grid(xcd_grid(n_units)), block(NT);
+    const dim3 grid(xcd_grid(a.B * a.Hv)), block(NT);
     if (a.max_nodes <= 16)
         verify_kernel<16><<<grid, block, 0, stream>>>(a);
     else if (a.max_nodes <= 32)
