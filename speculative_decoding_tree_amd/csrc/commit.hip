@@ -20,11 +20,15 @@ namespace {
 constexpr int NT = 256;
 constexpr int KCHUNK = 16;   // path rows staged per pass
 
+// The unit's 64 KiB of H0 is requested first (it depends only on the slot);
+// wave 0 then validates parents and the path with ballots, and turns the path
+// gates into decay coefficients with a suffix scan over shuffles, while those
+// loads are in flight.
 __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
     __shared__ float s_k[KCHUNK][D];   // D_aj * k_j rows of the current chunk
     __shared__ float s_coef[MAXN];
     __shared__ int s_path[MAXN];
-    __shared__ int s_bad;
+    __shared__ int s_st, s_L;
     __shared__ float s_gam;
 
     const int n_units = a.B * a.Hv;
@@ -34,78 +38,86 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
     const int h = unit - b * a.Hv;
     const int hk = h / (a.Hv / a.Hk);
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
 
-    int lo, N;
-    int st = check_offsets(a, b, lo, N);
-    if (st == GDN_TREE_S_OK) {
-        if (tid == 0) s_bad = 0;
-        __syncthreads();
-        for (int t = tid; t < N; t += NT) {
-            const int p = a.parent[lo + t];
-            if (p < -1 || p >= t) s_bad = 1;
-        }
-        __syncthreads();
-        if (s_bad) st = GDN_TREE_S_BAD_PARENT;
-    }
     const int slot = resolve_slot(a, b);
-    if (st == GDN_TREE_S_OK && slot < 0) st = GDN_TREE_S_BAD_SLOT;
-    int L = 0;
-    if (st == GDN_TREE_S_OK) {
-        L = a.path_len[b];
-        if (L < 0 || L > a.max_nodes || L > N) {
-            st = GDN_TREE_S_BAD_PATH;
-        } else {
-            __syncthreads();
-            if (tid == 0) {
-                int prev = -1;
-                for (int j = 0; j < L; ++j) {
-                    const int p = a.path[(size_t)b * a.max_nodes + j];
-                    if (p < 0 || p >= N || a.parent[lo + p] != prev) {
-                        s_bad = 1;
-                        break;
-                    }
-                    s_path[j] = p;
-                    prev = p;
-                }
-                if (!s_bad) {   // suffix sums of g along the path
-                    float s = 0.f;
-                    for (int j = L - 1; j >= 0; --j) {
-                        s_coef[j] = expf(s);
-                        s += a.g[(size_t)(lo + s_path[j]) * a.Hv + h];
-                    }
-                    s_gam = expf(s);
-                }
-            }
-            __syncthreads();
-            if (s_bad) st = GDN_TREE_S_BAD_PATH;
-        }
-    }
-    if (h == 0 && tid == 0 && a.status) a.status[b] = st;
-    if (slot < 0) return;   // nowhere to write
-
-    const size_t base = ((size_t)slot * a.Hv + h) * D * D;
+    const size_t base = ((size_t)(slot < 0 ? 0 : slot) * a.Hv + h) * D * D;
     const float4 *src = reinterpret_cast<const float4 *>(a.S0 + base);
     float4 *dst = reinterpret_cast<float4 *>(a.S_out + base);
     const int c4 = tid & 31, r0 = tid >> 5;   // rows r0 + 8 i, columns 4 c4 .. 4 c4 + 3
+    float4 acc[16];
+    if (slot >= 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = src[(r0 + 8 * i) * 32 + c4];
+    }
+
+    if (tid < 64) {
+        int lo, N;
+        int st = check_offsets(a, b, lo, N);
+        int L = 0;
+        if (st == GDN_TREE_S_OK) {
+            const bool live = lane < N;
+            const int p = live ? a.parent[lo + lane] : -1;
+            if (__ballot(live && (p < -1 || p >= lane))) st = GDN_TREE_S_BAD_PARENT;
+        }
+        if (st == GDN_TREE_S_OK && slot < 0) st = GDN_TREE_S_BAD_SLOT;
+        if (st == GDN_TREE_S_OK) {
+            L = a.path_len[b];
+            if (L < 0 || L > a.max_nodes || L > N) {
+                st = GDN_TREE_S_BAD_PATH;
+            } else {
+                // lane j holds path entry j; it must be the child of entry j-1 (S0 for j = 0)
+                const bool on = lane < L;
+                const int pj = on ? a.path[(size_t)b * a.max_nodes + lane] : 0;
+                const bool inr = on && pj >= 0 && pj < N;
+                const int par = inr ? a.parent[lo + pj] : -2;
+                const int prev = __shfl(pj, lane > 0 ? lane - 1 : 0);
+                if (__ballot(on && (!inr || par != (lane == 0 ? -1 : prev)))) {
+                    st = GDN_TREE_S_BAD_PATH;
+                } else {
+                    // suffix sums: sfx_j = sum of g over path entries j .. L-1
+                    float sfx = on ? a.g[(size_t)(lo + pj) * a.Hv + h] : 0.f;
+                    const float gj = sfx;
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const float up = __shfl_down(sfx, off);
+                        if (lane + off < 64) sfx += up;
+                    }
+                    if (on) {
+                        s_path[lane] = pj;
+                        s_coef[lane] = expf(sfx - gj);   // D_aj: gates of the entries after j
+                    }
+                    const float total = __shfl(sfx, 0);
+                    if (lane == 0) s_gam = expf(total);
+                }
+            }
+        }
+        if (lane == 0) {
+            s_st = st;
+            s_L = L;
+            if (h == 0 && a.status) a.status[b] = st;
+        }
+    }
+    __syncthreads();
+    const int st = s_st, L = s_L;
+    if (slot < 0) return;   // nowhere to write
 
     if (st != GDN_TREE_S_OK || L == 0) {   // S_out = S0, bit-exact
         if (a.S_out != a.S0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) dst[(r0 + 8 * i) * 32 + c4] = src[(r0 + 8 * i) * 32 + c4];
+            for (int i = 0; i < 16; ++i) dst[(r0 + 8 * i) * 32 + c4] = acc[i];
         }
         return;
     }
 
-    float4 acc[16];
     const float gam = s_gam;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float4 x = src[(r0 + 8 * i) * 32 + c4];
-        acc[i] = make_float4(gam * x.x, gam * x.y, gam * x.z, gam * x.w);
-    }
+    for (int i = 0; i < 16; ++i) acc[i] = make_float4(gam * acc[i].x, gam * acc[i].y, gam * acc[i].z, gam * acc[i].w);
+    int lo, N;
+    check_offsets(a, b, lo, N);
     for (int j0 = 0; j0 < L; j0 += KCHUNK) {
         const int nj = min(KCHUNK, L - j0);
-        __syncthreads();
+        if (j0 > 0) __syncthreads();
         for (int idx = tid; idx < nj * D; idx += NT) {
             const int jj = idx >> 7, c = idx & (D - 1);
             const int t = s_path[j0 + jj];
@@ -129,33 +141,46 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
     for (int i = 0; i < 16; ++i) dst[(r0 + 8 * i) * 32 + c4] = acc[i];
 }
 
-// One lane per request: validate, then write the root-first path.
-__global__ __launch_bounds__(64) void accepted_path_kernel(Args a) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per request, lane t = node t: parents are validated with a ballot,
+// the accepted node's ancestor set comes from pointer doubling over shuffles,
+// and each lane on the path writes its own entry (position = its depth - 1).
+__global__ __launch_bounds__(256) void accepted_path_kernel(Args a) {
+    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     if (b >= a.B) return;
     int lo, N;
     int st = check_offsets(a, b, lo, N);
+    const int acc = a.accept_node[b];
+    int32_t *row = a.path_out + (size_t)b * a.max_nodes;
+    uint64_t path_mask = 0;
     if (st == GDN_TREE_S_OK) {
-        for (int t = 0; t < N; ++t) {
-            const int p = a.parent[lo + t];
-            if (p < -1 || p >= t) {
-                st = GDN_TREE_S_BAD_PARENT;
-                break;
+        const bool live = lane < N;
+        const int p = live ? a.parent[lo + lane] : -1;
+        if (__ballot(live && (p < -1 || p >= lane))) st = GDN_TREE_S_BAD_PARENT;
+        else if (acc < -1 || acc >= N) st = GDN_TREE_S_BAD_ACCEPT;
+        else if (acc >= 0) {
+            int jp = p;
+            uint64_t m = live ? (1ull << lane) : 0ull;
+            while (__ballot(jp >= 0)) {
+                const int src = jp >= 0 ? jp : lane;
+                const uint64_t m_up = __shfl(m, src);
+                const int jp_up = __shfl(jp, src);
+                if (jp >= 0) {
+                    m |= m_up;
+                    jp = jp_up;
+                }
             }
+            path_mask = __shfl(m, acc);   // inclusive ancestors of the accepted node
         }
     }
-    const int acc = a.accept_node[b];
-    if (st == GDN_TREE_S_OK && (acc < -1 || acc >= N)) st = GDN_TREE_S_BAD_ACCEPT;
-    int32_t *row = a.path_out + (size_t)b * a.max_nodes;
-    int L = 0;
-    if (st == GDN_TREE_S_OK && acc >= 0) {
-        for (int j = acc; j >= 0; j = a.parent[lo + j]) ++L;
-        int pos = L;
-        for (int j = acc; j >= 0; j = a.parent[lo + j]) row[--pos] = j;
+    const int L = __popcll(path_mask);
+    // the path in index order is root first; lane t on it sits at the number of path nodes below t
+    if ((path_mask >> lane) & 1ull) row[__popcll(path_mask & ((1ull << lane) - 1ull))] = lane;
+    for (int i = L + lane; i < a.max_nodes; i += 64) row[i] = 0;
+    if (lane == 0) {
+        a.path_len_out[b] = L;
+        if (a.status) a.status[b] = st;
     }
-    for (int i = L; i < a.max_nodes; ++i) row[i] = 0;
-    a.path_len_out[b] = L;
-    if (a.status) a.status[b] = st;
 }
 
 }  // namespace
@@ -167,7 +192,7 @@ hipError_t launch_commit(const Args &a, hipStream_t stream) {
 }
 
 hipError_t launch_accepted_path(const Args &a, hipStream_t stream) {
-    accepted_path_kernel<<<dim3((a.B + 63) / 64), dim3(64), 0, stream>>>(a);
+    accepted_path_kernel<<<dim3((a.B + 3) / 4), dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 
