@@ -48,7 +48,7 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
     float4 acc[16];
     if (slot >= 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = src[(r0 + 8 * i) * 32 + c4];
+        for (int i = 0; i < 16; ++i) acc[i] = ld_stream4(src + (r0 + 8 * i) * 32 + c4);
     }
 
     if (tid < 64) {
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
     if (st != GDN_TREE_S_OK || L == 0) {   // S_out = S0, bit-exact
         if (a.S_out != a.S0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) dst[(r0 + 8 * i) * 32 + c4] = acc[i];
+            for (int i = 0; i < 16; ++i) st_stream4(dst + (r0 + 8 * i) * 32 + c4, acc[i]);
         }
         return;
     }
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
         }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dst[(r0 + 8 * i) * 32 + c4] = acc[i];
+    for (int i = 0; i < 16; ++i) st_stream4(dst + (r0 + 8 * i) * 32 + c4, acc[i]);
 }
 
 // One wave per request, lane t = node t: parents are validated with a ballot,

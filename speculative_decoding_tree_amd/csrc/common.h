@@ -29,6 +29,26 @@ struct Args {
     const float *node_state_in;
 };
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming accesses: each byte of a committed state is touched once per
+// call, so loads and stores carry the non-temporal hint (no cache retention).
+__device__ __forceinline__ float2 ld_stream2(const float *p) {
+    const f32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x2_t *>(p));
+    return make_float2(v.x, v.y);
+}
+__device__ __forceinline__ float4 ld_stream4(const float4 *p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream4(float4 *p, float4 x) {
+    __builtin_nontemporal_store(f32x4_t{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4_t *>(p));
+}
+__device__ __forceinline__ void st_stream2(float *p, float2 x) {
+    __builtin_nontemporal_store(f32x2_t{x.x, x.y}, reinterpret_cast<f32x2_t *>(p));
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) {
     return __uint_as_float(b16 << 16);
 }

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    hraw[s][e] = *reinterpret_cast<const float2 *>(H + (32 * s + e) * D);
+                    hraw[s][e] = ld_stream2(H + (32 * s + e) * D);
         }
         const uint16_t *V = a.v + ((size_t)lo * a.Hv + h) * D + c;
         const size_t vrow = (size_t)a.Hv * D;
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
                         acc2.y = fmaf(-aj, uj.y, acc2.y);
                     }
                     if (L > 1) *reinterpret_cast<float2 *>(&sm.ru[t][c]) = acc2;
-                    *reinterpret_cast<float2 *>(Ubase + (size_t)t * ustride) = acc2;
+                    st_stream2(Ubase + (size_t)t * ustride, acc2);
                 }
             }
             __builtin_amdgcn_wave_barrier();
@@ -425,8 +425,7 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * tau + 4 * grp + i;
                     if (r < N)
-                        *reinterpret_cast<float2 *>(Obase + (size_t)r * ostride) =
-                            make_float2(zt[tau][0][i], zt[tau][1][i]);
+                        st_stream2(Obase + (size_t)r * ostride, make_float2(zt[tau][0][i], zt[tau][1][i]));
                 }
     }
 }
