@@ -34,6 +34,37 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "verified tree-nodes/s (all heads) + commits/s at batch 256; % HBM peak"
 D = 128
+KERNEL_SOURCES = ("speculative_decoding_tree_amd/csrc/common.h", "speculative_decoding_tree_amd/csrc/verify.hip",
+                  "speculative_decoding_tree_amd/csrc/commit.hip")
+
+
+def kernel_source_sha() -> str:
+    """sha256 over the sources of the verify and commit kernels."""
+    import hashlib
+    hsh = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size),
+    or None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_sha():
+        return None
+    key = f"{kernel}.hbm_bytes_per_launch"
+    return int(float(vals[key])) if key in vals else None
 
 
 # ----------------------------------------------------------------------------
@@ -238,8 +269,10 @@ def main():
     dom = max(("gdn_tree_verify", "gdn_tree_commit"), key=lambda k: kernels[k]["avg_us"])
     ach = kernels[dom]["alg_GBps"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name, dom),
                 "alg_bytes_per_launch": kernels[dom]["alg_bytes"]}
+    for kname in ("gdn_tree_verify", "gdn_tree_commit"):
+        kernels[kname]["hbm_traffic_bytes"] = measured_traffic(wl.name, kname)
 
     nodes_per_s = wl.T / (ms_step * 1e-3)
     result = {
