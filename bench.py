@@ -148,6 +148,59 @@ def cpu_baseline(wl, n_req: int):
 # GPU timing
 # ----------------------------------------------------------------------------
 
+def _time_launches(fn, n, stream):
+    """Average duration (us) of fn() from HIP events recorded around each call."""
+    import numpy as np
+    import torch
+    for _ in range(3):
+        fn(0)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        fn(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3)
+
+
+def next_rows(args, wl, pools, mn, stream):
+    """Rows beyond the core step: device-side greedy acceptance, alone and fused
+    with the commit, on the same batch (synthetic draft/target token ids)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from speculative_decoding_tree_amd import gdn_tree as G
+    dev = pools[0]["S0"].device
+    draft, tgt, root = W.greedy_tokens(wl)
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    dt, tg, rt = tt(draft), tt(tgt), tt(root)
+    B = wl.B
+    acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    path = torch.empty((B, mn), dtype=torch.int32, device=dev)
+    plen = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = torch.empty((B,), dtype=torch.int32, device=dev)
+    n = max(10, args.steps // 2)
+
+    def greedy(i):
+        p = pools[i % len(pools)]
+        G.accept_greedy(p["off"], p["par"], dt, tg, rt, max_nodes=mn, accept_node=acc, path=path,
+                        path_len=plen, status=st, stream=stream)
+
+    def fused(i):
+        p = pools[i % len(pools)]
+        G.accept_commit(p["S0"], p["U"], p["k"], p["g"], p["off"], p["par"], dt, tg, rt, max_nodes=mn,
+                        S_out=p["S_out"], accept_node=acc, path=path, path_len=plen, status=st, stream=stream)
+
+    t_greedy = _time_launches(greedy, n, stream)
+    t_fused = _time_launches(fused, n, stream)
+    L = plen.cpu().numpy()
+    cb = commit_bytes(wl, L)
+    return {"accept_greedy": {"avg_us": t_greedy, "mean_accepted_len": float(L.mean())},
+            "accept_commit_fused": {"avg_us": t_fused, "alg_bytes": cb,
+                                    "alg_GBps": cb / (t_fused * 1e-6) / 1e9,
+                                    "hbm_frac": cb / (t_fused * 1e-6) / 1e9 / HBM_PEAK_GBS}}
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +211,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-storeall", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=128, help="requests in the oracle sample")
+    ap.add_argument("--no-next", action="store_true", help="skip the next-row measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -329,6 +383,9 @@ def main():
         }
         del node_state
         torch.cuda.empty_cache()
+
+    if not args.no_next:
+        result["next_rows"] = next_rows(args, wl, pools, mn, stream)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)

@@ -158,6 +158,39 @@ int gdn_tree_accepted_path(const gdn_tree_dims *dims, const int32_t *node_offset
                            int32_t *path_len, int32_t *status, void *stream);
 
 /*
+ * gdn_tree_accept_greedy -- greedy acceptance on the device.
+ *
+ * Per request, starting at the committed root whose target prediction is
+ * root_token[b]: among the current position's children in index order, enter
+ * the first whose draft_token equals the target's prediction at the current
+ * position (target_token[t] after node t), until none matches (TreeWY,
+ * "Results": greedy drafting and verification; GDN Tree-Scan, abstract:
+ * device-side choice of the committed draft).  Writes accept_node[b] (-1 when
+ * the first level already fails), the root-first path (zero-filled row) and
+ * path_len.  draft_token, target_token int32 [T] and root_token int32 [B] are
+ * arbitrary token ids.  Device errors (status 1..3) give accept_node = -1,
+ * path_len = 0.
+ */
+int gdn_tree_accept_greedy(const gdn_tree_dims *dims, const int32_t *node_offset, const int32_t *parent,
+                           const int32_t *draft_token, const int32_t *target_token,
+                           const int32_t *root_token, int32_t *accept_node, int32_t *path,
+                           int32_t *path_len, int32_t *status, void *stream);
+
+/*
+ * gdn_tree_accept_commit -- greedy acceptance fused with the commit, in one
+ * launch: each (request, v-head) workgroup repeats the greedy walk of
+ * gdn_tree_accept_greedy (one wave, no host round trip) and composes that
+ * path's pseudo-values into S_out exactly as gdn_tree_commit does.
+ * accept_node, path and path_len are optional outputs (NULL = not written).
+ * Device errors as in gdn_tree_commit (bad path cannot occur).
+ */
+int gdn_tree_accept_commit(const gdn_tree_dims *dims, const float *S0, float *S_out,
+                           const int32_t *state_slot, const float *U, const uint16_t *k, const float *g,
+                           const int32_t *node_offset, const int32_t *parent, const int32_t *draft_token,
+                           const int32_t *target_token, const int32_t *root_token, int32_t *accept_node,
+                           int32_t *path, int32_t *path_len, int32_t *status, void *stream);
+
+/*
  * gdn_tree_verify_storeall -- the snapshot-per-node comparison scheme.
  *
  * Walks each request's nodes in order with the sequential rule and writes

@@ -48,7 +48,7 @@ __all__ = [
     "parents_valid", "ancestry", "depths", "root_to_node", "accepted_path", "gated_delta_step",
     "verify_unit", "commit_unit", "replay_commit_unit", "verify_request", "verify_batch",
     "commit_batch", "accepted_path_batch", "verify_storeall_batch", "commit_storeall_batch",
-    "state_bytes", "PINS",
+    "state_bytes", "PINS", "greedy_accept", "greedy_accept_batch",
 ]
 
 # Status codes written per request.  These numbers are part of the C-ABI's
@@ -77,6 +77,9 @@ PINS = {
                    "verify-then-commit composition",
     "verify_storeall_batch": "node states equal the per-path sequential states; state count "
                              "of a depth-3 chain is 4 including S0 (TreeWY, Prior work)",
+    "greedy_accept": "brute force over every root-first path: with distinct sibling tokens the "
+                     "result is the longest path whose every token matches the target's "
+                     "prediction at its parent; a chain accepts exactly its matching prefix",
 }
 
 
@@ -395,6 +398,50 @@ def commit_storeall_batch(S0, node_state, node_offset, parent, accept_node, max_
             continue
         out[slot] = _f64(S0[slot]) if (st != STATUS_OK or a < 0) else _f64(node_state[lo + a])
     return out, status
+
+
+def greedy_accept(parent: Sequence[int], draft: Sequence[int], target_next: Sequence[int],
+                  root_next: int) -> int:
+    """Greedy tree acceptance (TreeWY, Results: greedy drafting and verification; GDN
+    Tree-Scan: the committed draft is chosen on the device).
+
+    Start at the committed root, whose target prediction is root_next.  Among the
+    current position's children, in index order, take the first whose draft token
+    equals the target's prediction at the current position; continue from it with
+    its own prediction target_next[child].  Stop when no child matches.  Returns
+    the last accepted node, or -1 when the first level already fails.
+    """
+    children = {}
+    for t, p in enumerate(parent):
+        children.setdefault(int(p), []).append(t)
+    cur, want = -1, int(root_next)
+    while True:
+        nxt = next((c for c in children.get(cur, []) if int(draft[c]) == want), None)
+        if nxt is None:
+            return cur
+        cur, want = nxt, int(target_next[nxt])
+
+
+def greedy_accept_batch(node_offset, parent, draft, target_next, root_next, max_nodes: int = MAX_NODES):
+    """(accept_node [B], path [B][max_nodes], path_len [B], status [B]) for a batch."""
+    B = len(node_offset) - 1
+    T = len(parent)
+    acc = np.full(B, -1, dtype=np.int32)
+    path = np.zeros((B, max_nodes), dtype=np.int32)
+    plen = np.zeros(B, dtype=np.int32)
+    status = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        st = _request_status(node_offset, b, T, max_nodes, parent)
+        status[b] = st
+        if st != STATUS_OK:
+            continue
+        lo, hi = int(node_offset[b]), int(node_offset[b + 1])
+        a = greedy_accept(parent[lo:hi], draft[lo:hi], target_next[lo:hi], root_next[b])
+        acc[b] = a
+        pth = accepted_path(parent[lo:hi], a)
+        plen[b] = len(pth)
+        path[b, :len(pth)] = pth
+    return acc, path, plen, status
 
 
 def state_bytes(B: int, Hv: int, d_k: int, d_v: int, T: int, storeall: bool) -> int:

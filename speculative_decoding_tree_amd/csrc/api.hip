@@ -154,6 +154,58 @@ int gdn_tree_accepted_path(const gdn_tree_dims *dims, const int32_t *node_offset
     return finish(gdn::launch_accepted_path(a, (hipStream_t)stream));
 }
 
+int gdn_tree_accept_greedy(const gdn_tree_dims *dims, const int32_t *node_offset, const int32_t *parent,
+                           const int32_t *draft_token, const int32_t *target_token, const int32_t *root_token,
+                           int32_t *accept_node, int32_t *path, int32_t *path_len, int32_t *status,
+                           void *stream) {
+    int rc = check_dims(dims);
+    if (rc != GDN_TREE_OK || dims->B == 0) return rc;
+    if (!node_offset || !root_token || !accept_node || !path || !path_len) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && (!parent || !draft_token || !target_token)) return GDN_TREE_E_NULL;
+    Args a = base_args(dims);
+    a.node_offset = node_offset;
+    a.parent = parent;
+    a.draft_token = draft_token;
+    a.target_token = target_token;
+    a.root_token = root_token;
+    a.accept_out = accept_node;
+    a.path_out = path;
+    a.path_len_out = path_len;
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_accept_greedy(a, (hipStream_t)stream));
+}
+
+int gdn_tree_accept_commit(const gdn_tree_dims *dims, const float *S0, float *S_out, const int32_t *state_slot,
+                           const float *U, const uint16_t *k, const float *g, const int32_t *node_offset,
+                           const int32_t *parent, const int32_t *draft_token, const int32_t *target_token,
+                           const int32_t *root_token, int32_t *accept_node, int32_t *path, int32_t *path_len,
+                           int32_t *status, void *stream) {
+    int rc = check_dims(dims);
+    if (rc != GDN_TREE_OK || dims->B == 0) return rc;
+    if (!S0 || !S_out || !node_offset || !root_token) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && (!U || !k || !g || !parent || !draft_token || !target_token)) return GDN_TREE_E_NULL;
+    if (any_misaligned(S0, S_out, U, k)) return GDN_TREE_E_ALIGN;
+    Args a = base_args(dims);
+    a.S0 = S0;
+    a.S_out = S_out;
+    a.state_slot = state_slot;
+    a.U = const_cast<float *>(U);
+    a.k = k;
+    a.g = g;
+    a.node_offset = node_offset;
+    a.parent = parent;
+    a.draft_token = draft_token;
+    a.target_token = target_token;
+    a.root_token = root_token;
+    a.accept_out = accept_node;
+    a.path_out = path;
+    a.path_len_out = path_len;
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_accept_commit(a, (hipStream_t)stream));
+}
+
 int gdn_tree_verify_storeall(const gdn_tree_dims *dims, const float *S0, const int32_t *state_slot,
                              const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                              const float *beta, const int32_t *node_offset, const int32_t *parent,

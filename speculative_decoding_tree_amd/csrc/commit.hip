@@ -10,12 +10,45 @@
 //
 // a rank-L update that streams H0 in and H' out exactly once (64 KiB each per
 // (request, v-head)).  GDN Tree-Scan (arXiv 2609.23900), abstract: the
-// accepted chain is the only state that gets published.
+// accepted chain is the only state that gets published, and the committed
+// draft is chosen on the device.  The greedy variants take that choice from
+// token ids (TreeWY, "Results": greedy drafting and verification): from the
+// committed root, enter the first child (index order) whose draft token equals
+// the target's prediction at the current position, until none matches.
+
 #include "common.h"
 #include "launch.h"
 
 namespace gdn {
 namespace {
+
+// Greedy walk in one wave, lane t = node t (parents already validated).
+// Returns the inclusive ancestor set of the accepted node (0 when none).
+__device__ __forceinline__ uint64_t greedy_walk(const Args &a, int b, int lo, int N, int lane, int p,
+                                                int &accept) {
+    const bool live = lane < N;
+    const int dtok = live ? a.draft_token[lo + lane] : 0;
+    const int ttok = live ? a.target_token[lo + lane] : 0;
+    int cur = -1, want = a.root_token[b];
+    uint64_t pm = 0;
+    for (int step = 0; step < N; ++step) {
+        const uint64_t mk = __ballot(live && p == cur && dtok == want);
+        if (!mk) break;
+        cur = __builtin_ctzll(mk);
+        pm |= 1ull << cur;
+        want = __shfl(ttok, cur);
+    }
+    accept = cur;
+    return pm;
+}
+
+// Node at position `lane` (root first) of the path set pm, or 0 past its end.
+__device__ __forceinline__ int path_entry(uint64_t pm, int lane) {
+    uint64_t m = pm;
+    for (int k = 0; k < lane && m; ++k) m &= m - 1;
+    return m ? __builtin_ctzll(m) : 0;
+}
+
 
 constexpr int NT = 256;
 constexpr int KCHUNK = 16;   // path rows staged per pass
@@ -24,6 +57,7 @@ constexpr int KCHUNK = 16;   // path rows staged per pass
 // wave 0 then validates parents and the path with ballots, and turns the path
 // gates into decay coefficients with a suffix scan over shuffles, while those
 // loads are in flight.
+template <bool GREEDY>
 __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
     __shared__ float s_k[KCHUNK][D];   // D_aj * k_j rows of the current chunk
     __shared__ float s_coef[MAXN];
@@ -61,36 +95,58 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
             if (__ballot(live && (p < -1 || p >= lane))) st = GDN_TREE_S_BAD_PARENT;
         }
         if (st == GDN_TREE_S_OK && slot < 0) st = GDN_TREE_S_BAD_SLOT;
-        if (st == GDN_TREE_S_OK) {
+        bool have_path = false;
+        int pj = 0;
+        if (GREEDY) {
+            int accept = -1;
+            uint64_t pm = 0;
+            if (st == GDN_TREE_S_OK) {
+                const int p = lane < N ? a.parent[lo + lane] : -1;
+                pm = greedy_walk(a, b, lo, N, lane, p, accept);
+                L = __popcll(pm);
+                pj = path_entry(pm, lane);
+                have_path = true;
+            }
+            if (h == 0) {   // one head publishes the decision
+                if (a.accept_out && lane == 0) a.accept_out[b] = accept;
+                if (a.path_out) {
+                    int32_t *row = a.path_out + (size_t)b * a.max_nodes;
+                    if (lane < L) row[lane] = pj;
+                    for (int i = L + lane; i < a.max_nodes; i += 64) row[i] = 0;
+                }
+                if (a.path_len_out && lane == 0) a.path_len_out[b] = L;
+            }
+        } else if (st == GDN_TREE_S_OK) {
             L = a.path_len[b];
             if (L < 0 || L > a.max_nodes || L > N) {
                 st = GDN_TREE_S_BAD_PATH;
             } else {
                 // lane j holds path entry j; it must be the child of entry j-1 (S0 for j = 0)
                 const bool on = lane < L;
-                const int pj = on ? a.path[(size_t)b * a.max_nodes + lane] : 0;
+                pj = on ? a.path[(size_t)b * a.max_nodes + lane] : 0;
                 const bool inr = on && pj >= 0 && pj < N;
                 const int par = inr ? a.parent[lo + pj] : -2;
                 const int prev = __shfl(pj, lane > 0 ? lane - 1 : 0);
-                if (__ballot(on && (!inr || par != (lane == 0 ? -1 : prev)))) {
-                    st = GDN_TREE_S_BAD_PATH;
-                } else {
-                    // suffix sums: sfx_j = sum of g over path entries j .. L-1
-                    float sfx = on ? a.g[(size_t)(lo + pj) * a.Hv + h] : 0.f;
-                    const float gj = sfx;
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) {
-                        const float up = __shfl_down(sfx, off);
-                        if (lane + off < 64) sfx += up;
-                    }
-                    if (on) {
-                        s_path[lane] = pj;
-                        s_coef[lane] = expf(sfx - gj);   // D_aj: gates of the entries after j
-                    }
-                    const float total = __shfl(sfx, 0);
-                    if (lane == 0) s_gam = expf(total);
-                }
+                if (__ballot(on && (!inr || par != (lane == 0 ? -1 : prev)))) st = GDN_TREE_S_BAD_PATH;
+                else have_path = true;
             }
+        }
+        if (have_path) {
+            // suffix sums: sfx_j = sum of g over path entries j .. L-1
+            const bool on = lane < L;
+            float sfx = on ? a.g[(size_t)(lo + pj) * a.Hv + h] : 0.f;
+            const float gj = sfx;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float up = __shfl_down(sfx, off);
+                if (lane + off < 64) sfx += up;
+            }
+            if (on) {
+                s_path[lane] = pj;
+                s_coef[lane] = expf(sfx - gj);   // D_aj: gates of the entries after j
+            }
+            const float total = __shfl(sfx, 0);
+            if (lane == 0) s_gam = expf(total);
         }
         if (lane == 0) {
             s_st = st;
@@ -144,19 +200,21 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
 // One wave per request, lane t = node t: parents are validated with a ballot,
 // the accepted node's ancestor set comes from pointer doubling over shuffles,
 // and each lane on the path writes its own entry (position = its depth - 1).
+template <bool GREEDY>
 __global__ __launch_bounds__(256) void accepted_path_kernel(Args a) {
     const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (b >= a.B) return;
     int lo, N;
     int st = check_offsets(a, b, lo, N);
-    const int acc = a.accept_node[b];
+    int acc = GREEDY ? -1 : a.accept_node[b];
     int32_t *row = a.path_out + (size_t)b * a.max_nodes;
     uint64_t path_mask = 0;
     if (st == GDN_TREE_S_OK) {
         const bool live = lane < N;
         const int p = live ? a.parent[lo + lane] : -1;
         if (__ballot(live && (p < -1 || p >= lane))) st = GDN_TREE_S_BAD_PARENT;
+        else if (GREEDY) path_mask = greedy_walk(a, b, lo, N, lane, p, acc);
         else if (acc < -1 || acc >= N) st = GDN_TREE_S_BAD_ACCEPT;
         else if (acc >= 0) {
             int jp = p;
@@ -180,19 +238,29 @@ __global__ __launch_bounds__(256) void accepted_path_kernel(Args a) {
     if (lane == 0) {
         a.path_len_out[b] = L;
         if (a.status) a.status[b] = st;
+        if (GREEDY && a.accept_out) a.accept_out[b] = st == GDN_TREE_S_OK ? acc : -1;
     }
 }
 
 }  // namespace
 
 hipError_t launch_commit(const Args &a, hipStream_t stream) {
-    const int n_units = a.B * a.Hv;
-    commit_kernel<<<dim3(xcd_grid(n_units)), dim3(NT), 0, stream>>>(a);
+    commit_kernel<false><<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_accept_commit(const Args &a, hipStream_t stream) {
+    commit_kernel<true><<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_accepted_path(const Args &a, hipStream_t stream) {
-    accepted_path_kernel<<<dim3((a.B + 3) / 4), dim3(256), 0, stream>>>(a);
+    accepted_path_kernel<false><<<dim3((a.B + 3) / 4), dim3(256), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_accept_greedy(const Args &a, hipStream_t stream) {
+    accepted_path_kernel<true><<<dim3((a.B + 3) / 4), dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -27,6 +27,8 @@ struct Args {
     int32_t *path_out, *path_len_out;
     float *node_state;
     const float *node_state_in;
+    const int32_t *draft_token, *target_token, *root_token;
+    int32_t *accept_out;
 };
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -286,3 +286,59 @@ def test_commit_alone_from_oracle_pseudo_values():
     torch.cuda.synchronize()
     So, _ = O.commit_batch(*oracle_inputs(wl), po, plo, wl.Hv, wl.Hk, max_nodes=mn)
     assert matwise_rel_err(host(S1), So) <= 1e-5
+
+
+# ----------------------------------------------------------------------------
+# device-side greedy acceptance, alone and fused with the commit
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c2", "c3_b16", "mixed_small", "forest_empty_single", "deep_chain64"])
+def test_greedy_accept_and_fused_commit(name):
+    wl = SMALL[name]()
+    mn = _mn(wl)
+    draft, tgt, root = W.greedy_tokens(wl, p_match=0.8, seed=3)
+    acc_o, path_o, plen_o, st_o = O.greedy_accept_batch(wl.node_offset, wl.parent, draft, tgt, root, max_nodes=mn)
+    d = upload(wl)
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+    acc, path, plen, st = G.accept_greedy(d["node_offset"], d["parent"], tt(draft), tt(tgt), tt(root), max_nodes=mn)
+    out, U, _, _ = G.verify(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"], d["parent"],
+                            max_nodes=mn)
+    S1, acc2, path2, plen2, st2 = G.accept_commit(d["S0"], U, d["k"], d["g"], d["node_offset"], d["parent"],
+                                                  tt(draft), tt(tgt), tt(root), max_nodes=mn)
+    torch.cuda.synchronize()
+    for got in ((acc, path, plen, st), (acc2, path2, plen2, st2)):
+        assert np.array_equal(host(got[0]), acc_o)
+        assert np.array_equal(host(got[1]), path_o) and np.array_equal(host(got[2]), plen_o)
+        assert np.array_equal(host(got[3]), st_o)
+    So, _ = O.commit_batch(*oracle_inputs(wl), path_o, plen_o, wl.Hv, wl.Hk, max_nodes=mn)
+    assert matwise_rel_err(host(S1), So) <= TOL
+    # the fused launch equals verify -> accepted path -> commit bit for bit
+    S3, _ = G.commit(d["S0"], U, d["k"], d["g"], d["node_offset"], d["parent"], path, plen, max_nodes=mn)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(S3), host(S1))
+
+
+def test_fused_accept_commit_full_batch():
+    wl = W.make_c5()
+    mn = wl.max_nodes
+    draft, tgt, root = W.greedy_tokens(wl)
+    acc_o, path_o, plen_o, _ = O.greedy_accept_batch(wl.node_offset, wl.parent, draft, tgt, root, max_nodes=mn)
+    d = upload(wl)
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+    out, U, _, _ = G.verify(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"], d["parent"],
+                            max_nodes=mn)
+    S1, acc, path, plen, st = G.accept_commit(d["S0"], U, d["k"], d["g"], d["node_offset"], d["parent"],
+                                              tt(draft), tt(tgt), tt(root), max_nodes=mn)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc), acc_o) and np.array_equal(host(path), path_o)
+    assert np.array_equal(host(plen), plen_o) and np.all(host(st) == 0)
+    rng = np.random.default_rng(1)
+    S1h = host(S1)
+    for b in sorted(rng.choice(wl.B, 12, replace=False).tolist()):
+        lo, hi = wl.node_offset[b], wl.node_offset[b + 1]
+        pth = O.accepted_path(wl.parents_of(b), int(acc_o[b]))
+        for h in range(0, wl.Hv, 7):
+            want = O.replay_commit_unit(wl.S0[b, h], wl.q64()[lo:hi, h // 3], wl.k64()[lo:hi, h // 3],
+                                        wl.v64()[lo:hi, h], wl.g[lo:hi, h].astype(np.float64),
+                                        wl.beta[lo:hi, h].astype(np.float64), pth)
+            assert matwise_rel_err(S1h[b, h][None], want[None]) <= TOL

@@ -391,3 +391,67 @@ def test_c1_worked_cases():
         assert st == 0 and np.all(np.isfinite(Ob))
         H1 = O.commit_unit(wl.S0[0, 0], states[0], p)
         assert np.array_equal(H1, states[0][p[-1]].T)
+
+
+# ----------------------------------------------------------------------------
+# greedy acceptance
+# ----------------------------------------------------------------------------
+
+def _all_root_paths(par):
+    n = len(par)
+    return [O.root_to_node(par, t) for t in range(n)]
+
+
+@pytest.mark.parametrize("n", range(1, 7))
+def test_greedy_accept_is_longest_matching_path(n):
+    """With distinct sibling tokens, greedy acceptance equals the longest root-first
+    path on which every node's token is the target's prediction at its parent
+    (brute force over all paths), for every tree of n nodes."""
+    rng = np.random.default_rng(20 + n)
+    for par in all_trees(n):
+        par = list(par)
+        draft = np.zeros(n, dtype=np.int64)
+        kids = {}
+        for t, p in enumerate(par):
+            kids.setdefault(p, []).append(t)
+        for p, ch in kids.items():
+            draft[ch] = rng.choice(6, size=len(ch), replace=False)
+        for _ in range(4):
+            tgt = rng.integers(0, 6, size=n)
+            root = int(rng.integers(0, 6))
+            a = O.greedy_accept(par, draft, tgt, root)
+            def ok(path):
+                want = root
+                for t in path:
+                    if draft[t] != want:
+                        return False
+                    want = tgt[t]
+                return True
+            best = [p for p in _all_root_paths(par) if ok(p)]
+            longest = max((len(p) for p in best), default=0)
+            assert len(O.accepted_path(par, a)) == longest
+            if a >= 0:
+                assert ok(O.root_to_node(par, a))
+
+
+def test_greedy_accept_chain_prefix():
+    par = list(range(-1, 7))
+    draft = np.arange(10, 18)
+    tgt = np.arange(11, 19).copy()
+    assert O.greedy_accept(par, draft, tgt, 10) == 7          # everything matches
+    tgt[3] = 0                                                # node 4 no longer predicted
+    assert O.greedy_accept(par, draft, tgt, 10) == 3
+    assert O.greedy_accept(par, draft, tgt, 99) == -1          # first token already wrong
+
+
+def test_greedy_tokens_generator_contract():
+    import workloads as W
+    wl = W.make_c5(per_kind=4, Hv=2, Hk=1)
+    draft, tgt, root = W.greedy_tokens(wl)
+    for b in range(wl.B):
+        lo = wl.node_offset[b]
+        par = wl.parents_of(b)
+        kids = {}
+        for t, p in enumerate(par):
+            kids.setdefault(int(p), []).append(int(draft[lo + t]))
+        assert all(len(v) == len(set(v)) for v in kids.values())

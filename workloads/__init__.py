@@ -36,7 +36,7 @@ import numpy as np
 __all__ = [
     "Workload", "CONFIGS", "make", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "chain", "root_branch", "random_tree", "accept_by_edge", "tree_depths",
-    "zero_pad", "subset",
+    "zero_pad", "subset", "greedy_tokens",
 ]
 
 
@@ -343,3 +343,48 @@ def subset(wl: Workload, requests) -> Workload:
                     S0=wl.S0[reqs].copy(), q=wl.q[idx].copy(), k=wl.k[idx].copy(),
                     v=wl.v[idx].copy(), g=wl.g[idx].copy(), beta=wl.beta[idx].copy(),
                     fp64=wl.fp64, kinds=[wl.kinds[b] for b in reqs] if wl.kinds else None)
+
+
+# ----------------------------------------------------------------------------
+# token ids for greedy acceptance (synthetic: no model, no vocabulary file)
+# ----------------------------------------------------------------------------
+
+def greedy_tokens(wl: Workload, vocab: int = 32000, p_match: float = 0.7, seed: int = 1):
+    """Draft token per node and the target's greedy prediction after every node
+    and after each request's committed context.
+
+    Siblings get distinct draft tokens (a drafter proposes distinct children).
+    At every position the target's prediction equals the draft token of one of
+    the position's children with probability p_match (that child chosen
+    uniformly), else a token no child carries.
+    Returns (draft [T], target_next [T], root_next [B]) as int32.
+    """
+    rng = np.random.default_rng(seed)
+    T, B = wl.T, wl.B
+    draft = np.zeros(T, dtype=np.int32)
+    target = np.zeros(T, dtype=np.int32)
+    root = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        lo, hi = int(wl.node_offset[b]), int(wl.node_offset[b + 1])
+        par = wl.parent[lo:hi]
+        kids = {}
+        for i, p in enumerate(par):
+            kids.setdefault(int(p), []).append(i)
+        for p, ch in kids.items():
+            toks = rng.choice(vocab, size=len(ch), replace=False)
+            for i, tk in zip(ch, toks):
+                draft[lo + i] = tk
+        for pos in [-1] + list(range(hi - lo)):
+            ch = kids.get(pos, [])
+            if ch and rng.random() < p_match:
+                want = int(draft[lo + ch[int(rng.integers(len(ch)))]])
+            else:
+                taken = {int(draft[lo + i]) for i in ch}
+                want = int(rng.integers(vocab))
+                while want in taken:
+                    want = int(rng.integers(vocab))
+            if pos < 0:
+                root[b] = want
+            else:
+                target[lo + pos] = want
+    return draft, target, root
