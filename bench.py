@@ -192,11 +192,23 @@ def next_rows(args, wl, pools, mn, stream):
         G.accept_commit(p["S0"], p["U"], p["k"], p["g"], p["off"], p["par"], dt, tg, rt, max_nodes=mn,
                         S_out=p["S_out"], accept_node=acc, path=path, path_len=plen, status=st, stream=stream)
 
+    def replay(i):
+        p = pools[i % len(pools)]
+        G.commit_replay(p["S0"], p["k"], p["v"], p["g"], p["beta"], p["off"], p["par"], p["path"], p["plen"],
+                        max_nodes=mn, S_out=p["S_out"], status=st, stream=stream)
+
     t_greedy = _time_launches(greedy, n, stream)
     t_fused = _time_launches(fused, n, stream)
     L = plen.cpu().numpy()
     cb = commit_bytes(wl, L)
-    return {"accept_greedy": {"avg_us": t_greedy, "mean_accepted_len": float(L.mean())},
+    t_replay = _time_launches(replay, n, stream)
+    Lr = pools[0]["plen"].cpu().numpy()
+    # replay reads k and v rows and the two gates of each path node instead of U
+    rb = int(commit_bytes(wl, Lr) - (wl.Hv * Lr * (4 * D + 4)).sum() + (wl.Hv * Lr * (2 * D + 8)).sum())
+    return {"commit_replay": {"avg_us": t_replay, "alg_bytes": rb, "alg_GBps": rb / (t_replay * 1e-6) / 1e9,
+                              "hbm_frac": rb / (t_replay * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                              "mean_accepted_len": float(Lr.mean())},
+            "accept_greedy": {"avg_us": t_greedy, "mean_accepted_len": float(L.mean())},
             "accept_commit_fused": {"avg_us": t_fused, "alg_bytes": cb,
                                     "alg_GBps": cb / (t_fused * 1e-6) / 1e9,
                                     "hbm_frac": cb / (t_fused * 1e-6) / 1e9 / HBM_PEAK_GBS}}

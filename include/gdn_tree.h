@@ -147,6 +147,20 @@ int gdn_tree_commit(const gdn_tree_dims *dims, const float *S0, float *S_out,
                     const int32_t *path_len, int32_t *status, void *stream);
 
 /*
+ * gdn_tree_commit_replay -- the next committed state by replaying the accepted
+ * path with the sequential gated delta rule from S0, without pseudo-values:
+ * for each path node in order, u = beta (v - alpha S k), S <- alpha S + u k^T
+ * (ReplaySSM, named in TreeWY's "Prior work"; GDN Tree-Scan, abstract:
+ * branch-local scan/replay).  Reads k, v, g, beta of the path nodes instead of
+ * U.  Same path format, statuses and fallbacks as gdn_tree_commit; L = 0
+ * copies S0 bit-exactly; S_out may alias S0.
+ */
+int gdn_tree_commit_replay(const gdn_tree_dims *dims, const float *S0, float *S_out,
+                           const int32_t *state_slot, const uint16_t *k, const uint16_t *v, const float *g,
+                           const float *beta, const int32_t *node_offset, const int32_t *parent,
+                           const int32_t *path, const int32_t *path_len, int32_t *status, void *stream);
+
+/*
  * gdn_tree_accepted_path -- root-first path from each request's accepted node.
  *
  * path[b][0..L) = the nodes from the S0-attached root down to accept_node[b]

@@ -136,6 +136,32 @@ int gdn_tree_commit(const gdn_tree_dims *dims, const float *S0, float *S_out, co
     return finish(gdn::launch_commit(a, (hipStream_t)stream));
 }
 
+int gdn_tree_commit_replay(const gdn_tree_dims *dims, const float *S0, float *S_out, const int32_t *state_slot,
+                           const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
+                           const int32_t *node_offset, const int32_t *parent, const int32_t *path,
+                           const int32_t *path_len, int32_t *status, void *stream) {
+    int rc = check_dims(dims);
+    if (rc != GDN_TREE_OK || dims->B == 0) return rc;
+    if (!S0 || !S_out || !node_offset || !path || !path_len) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && (!k || !v || !g || !beta || !parent)) return GDN_TREE_E_NULL;
+    if (any_misaligned(S0, S_out, k, v)) return GDN_TREE_E_ALIGN;
+    Args a = base_args(dims);
+    a.S0 = S0;
+    a.S_out = S_out;
+    a.state_slot = state_slot;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.node_offset = node_offset;
+    a.parent = parent;
+    a.path = path;
+    a.path_len = path_len;
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_commit_replay(a, (hipStream_t)stream));
+}
+
 int gdn_tree_accepted_path(const gdn_tree_dims *dims, const int32_t *node_offset, const int32_t *parent,
                            const int32_t *accept_node, int32_t *path, int32_t *path_len, int32_t *status,
                            void *stream) {

@@ -242,6 +242,138 @@ __global__ __launch_bounds__(256) void accepted_path_kernel(Args a) {
     }
 }
 
+// gdn_tree_commit_replay: the next committed state by replaying the accepted
+// path with the sequential gated delta rule from S0 (ReplaySSM, which TreeWY's
+// "Prior work" names as solving the same system but materialising the state at
+// another time; Tree-Scan's branch-local scan/replay).  No pseudo-values are
+// read: each step computes u = beta (v - alpha S k) from the running state.
+// Lane (c4, r0) keeps rows r0 + 8 i, columns 4 c4 .. +3 of the state in
+// registers; S k is reduced over the 8 row groups through LDS, twice-buffered
+// so one barrier per step suffices.
+__global__ __launch_bounds__(NT) void replay_kernel(Args a) {
+    __shared__ float s_kv[KCHUNK][2][D];      // k and v rows of the current chunk of the path
+    __shared__ float4 s_part[2][8][32];       // per row-group partial sums of S k
+    __shared__ int s_path[MAXN];
+    __shared__ float s_alpha[MAXN], s_beta[MAXN];
+    __shared__ int s_st, s_L;
+
+    const int n_units = a.B * a.Hv;
+    const int unit = xcd_unit(blockIdx.x, n_units);
+    if (unit >= n_units) return;
+    const int b = unit / a.Hv;
+    const int h = unit - b * a.Hv;
+    const int hk = h / (a.Hv / a.Hk);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+
+    const int slot = resolve_slot(a, b);
+    const size_t base = ((size_t)(slot < 0 ? 0 : slot) * a.Hv + h) * D * D;
+    const float4 *src = reinterpret_cast<const float4 *>(a.S0 + base);
+    float4 *dst = reinterpret_cast<float4 *>(a.S_out + base);
+    const int c4 = tid & 31, r0 = tid >> 5;   // rows r0 + 8 i, columns 4 c4 .. 4 c4 + 3
+    float4 st4[16];
+    if (slot >= 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st4[i] = ld_stream4(src + (r0 + 8 * i) * 32 + c4);
+    }
+    int lo, N;
+    if (tid < 64) {
+        int st = check_offsets(a, b, lo, N);
+        int L = 0;
+        if (st == GDN_TREE_S_OK) {
+            const bool live = lane < N;
+            const int p = live ? a.parent[lo + lane] : -1;
+            if (__ballot(live && (p < -1 || p >= lane))) st = GDN_TREE_S_BAD_PARENT;
+        }
+        if (st == GDN_TREE_S_OK && slot < 0) st = GDN_TREE_S_BAD_SLOT;
+        if (st == GDN_TREE_S_OK) {
+            L = a.path_len[b];
+            if (L < 0 || L > a.max_nodes || L > N) {
+                st = GDN_TREE_S_BAD_PATH;
+            } else {
+                const bool on = lane < L;
+                const int pj = on ? a.path[(size_t)b * a.max_nodes + lane] : 0;
+                const bool inr = on && pj >= 0 && pj < N;
+                const int par = inr ? a.parent[lo + pj] : -2;
+                const int prev = __shfl(pj, lane > 0 ? lane - 1 : 0);
+                if (__ballot(on && (!inr || par != (lane == 0 ? -1 : prev)))) {
+                    st = GDN_TREE_S_BAD_PATH;
+                } else if (on) {
+                    const size_t gi = (size_t)(lo + pj) * a.Hv + h;
+                    s_path[lane] = pj;
+                    s_alpha[lane] = expf(a.g[gi]);
+                    s_beta[lane] = a.beta[gi];
+                }
+            }
+        }
+        if (lane == 0) {
+            s_st = st;
+            s_L = L;
+            if (h == 0 && a.status) a.status[b] = st;
+        }
+    }
+    __syncthreads();
+    const int st = s_st, L = s_L;
+    if (slot < 0) return;
+    if (st != GDN_TREE_S_OK || L == 0) {   // S_out = S0, bit-exact
+        if (a.S_out != a.S0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st_stream4(dst + (r0 + 8 * i) * 32 + c4, st4[i]);
+        }
+        return;
+    }
+    check_offsets(a, b, lo, N);
+    for (int j0 = 0; j0 < L; j0 += KCHUNK) {
+        const int nj = min(KCHUNK, L - j0);
+        if (j0 > 0) __syncthreads();
+        for (int idx = tid; idx < nj * D; idx += NT) {
+            const int jj = idx >> 7, c = idx & (D - 1);
+            const int t = s_path[j0 + jj];
+            s_kv[jj][0][c] = bf16_to_f32(a.k[((size_t)(lo + t) * a.Hk + hk) * D + c]);
+            s_kv[jj][1][c] = bf16_to_f32(a.v[((size_t)(lo + t) * a.Hv + h) * D + c]);
+        }
+        __syncthreads();
+        for (int jj = 0; jj < nj; ++jj) {
+            const int buf = (j0 + jj) & 1;
+            // partial S k over this lane's 16 rows, for its 4 columns
+            float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float kr = s_kv[jj][0][r0 + 8 * i];
+                part.x = fmaf(st4[i].x, kr, part.x);
+                part.y = fmaf(st4[i].y, kr, part.y);
+                part.z = fmaf(st4[i].z, kr, part.z);
+                part.w = fmaf(st4[i].w, kr, part.w);
+            }
+            s_part[buf][r0][c4] = part;
+            __syncthreads();
+            float4 sk = s_part[buf][0][c4];
+#pragma unroll
+            for (int g8 = 1; g8 < 8; ++g8) {
+                const float4 x = s_part[buf][g8][c4];
+                sk.x += x.x;
+                sk.y += x.y;
+                sk.z += x.z;
+                sk.w += x.w;
+            }
+            const float al = s_alpha[j0 + jj], be = s_beta[j0 + jj];
+            const float4 vv = *reinterpret_cast<const float4 *>(&s_kv[jj][1][4 * c4]);
+            const float4 u = make_float4(be * (vv.x - al * sk.x), be * (vv.y - al * sk.y),
+                                         be * (vv.z - al * sk.z), be * (vv.w - al * sk.w));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {   // S <- alpha S + u k^T  (storage: H[i][c] = alpha H + k_i u_c)
+                const float kr = s_kv[jj][0][r0 + 8 * i];
+                st4[i].x = fmaf(al, st4[i].x, kr * u.x);
+                st4[i].y = fmaf(al, st4[i].y, kr * u.y);
+                st4[i].z = fmaf(al, st4[i].z, kr * u.z);
+                st4[i].w = fmaf(al, st4[i].w, kr * u.w);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st_stream4(dst + (r0 + 8 * i) * 32 + c4, st4[i]);
+}
+
 }  // namespace
 
 hipError_t launch_commit(const Args &a, hipStream_t stream) {
@@ -251,6 +383,11 @@ hipError_t launch_commit(const Args &a, hipStream_t stream) {
 
 hipError_t launch_accept_commit(const Args &a, hipStream_t stream) {
     commit_kernel<true><<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_commit_replay(const Args &a, hipStream_t stream) {
+    replay_kernel<<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
     return hipGetLastError();
 }
 

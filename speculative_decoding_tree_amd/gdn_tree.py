@@ -57,6 +57,7 @@ _SIGS = {
     "gdn_tree_commit_storeall": [ctypes.POINTER(Dims)] + [_P] * 9,
     "gdn_tree_accept_greedy": [ctypes.POINTER(Dims)] + [_P] * 10,
     "gdn_tree_accept_commit": [ctypes.POINTER(Dims)] + [_P] * 16,
+    "gdn_tree_commit_replay": [ctypes.POINTER(Dims)] + [_P] * 13,
 }
 
 _lib = None
@@ -326,3 +327,27 @@ def accept_commit(S0, U, k, g, node_offset, parent, draft_token, target_token, r
         _ptr(path_len, "path_len", _I32, (B,)), _ptr(status, "status", _I32, (B,)), _stream(stream))
     _check("gdn_tree_accept_commit", rc)
     return S_out, accept_node, path, path_len, status
+
+
+def commit_replay(S0, k, v, g, beta, node_offset, parent, path, path_len, max_nodes: int, S_out=None,
+                  state_slot=None, status=None, stream=None):
+    """gdn_tree_commit_replay (sequential replay of the accepted path, no U)."""
+    n_slots, Hv = int(S0.shape[0]), int(S0.shape[1])
+    B = int(node_offset.numel()) - 1
+    T = int(parent.numel())
+    Hk = int(k.shape[1])
+    S_out = S_out if S_out is not None else torch.empty_like(S0)
+    status = status if status is not None else torch.empty((B,), dtype=torch.int32, device=S0.device)
+    dims = make_dims(B, Hv, Hk, T, max_nodes, n_slots)
+    rc = lib().gdn_tree_commit_replay(
+        ctypes.byref(dims),
+        _ptr(S0, "S0", _F32, (n_slots, Hv, HEAD_DIM, HEAD_DIM)),
+        _ptr(S_out, "S_out", _F32, (n_slots, Hv, HEAD_DIM, HEAD_DIM)),
+        _ptr(state_slot, "state_slot", _I32, (B,)),
+        _ptr(k, "k", _B16, (T, Hk, HEAD_DIM)), _ptr(v, "v", _B16, (T, Hv, HEAD_DIM)),
+        _ptr(g, "g", _F32, (T, Hv)), _ptr(beta, "beta", _F32, (T, Hv)),
+        _ptr(node_offset, "node_offset", _I32, (B + 1,)), _ptr(parent, "parent", _I32, (T,)),
+        _ptr(path, "path", _I32, (B, max_nodes)), _ptr(path_len, "path_len", _I32, (B,)),
+        _ptr(status, "status", _I32, (B,)), _stream(stream))
+    _check("gdn_tree_commit_replay", rc)
+    return S_out, status

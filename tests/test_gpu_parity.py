@@ -342,3 +342,44 @@ def test_fused_accept_commit_full_batch():
                                         wl.v64()[lo:hi, h], wl.g[lo:hi, h].astype(np.float64),
                                         wl.beta[lo:hi, h].astype(np.float64), pth)
             assert matwise_rel_err(S1h[b, h][None], want[None]) <= TOL
+
+
+# ----------------------------------------------------------------------------
+# replay commit (no pseudo-values)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c2", "c3_b16", "mixed_small", "deep_chain64", "forest_empty_single"])
+def test_commit_replay_parity(name):
+    wl = SMALL[name]()
+    mn = _mn(wl)
+    d = upload(wl)
+    po, plo, _ = O.accepted_path_batch(wl.node_offset, wl.parent, wl.accept_node, max_nodes=mn)
+    path, plen = torch.from_numpy(po).cuda(), torch.from_numpy(plo).cuda()
+    S1, st = G.commit_replay(d["S0"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"], d["parent"], path,
+                             plen, max_nodes=mn)
+    out, U, _, _ = G.verify(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"], d["parent"],
+                            max_nodes=mn)
+    S2, _ = G.commit(d["S0"], U, d["k"], d["g"], d["node_offset"], d["parent"], path, plen, max_nodes=mn)
+    torch.cuda.synchronize()
+    So, cso = O.commit_batch(*oracle_inputs(wl), po, plo, wl.Hv, wl.Hk, max_nodes=mn)
+    assert np.array_equal(host(st), cso)
+    assert matwise_rel_err(host(S1), So) <= TOL
+    assert matwise_rel_err(host(S1), host(S2).astype(np.float64)) <= TOL
+    for b in range(wl.B):
+        if plo[b] == 0:
+            assert np.array_equal(host(S1)[b], wl.S0[b])
+
+
+def test_commit_replay_inplace_and_bad_path():
+    wl = W.make_custom([W.chain(3), W.root_branch()], [2, 4], Hv=2, Hk=1)
+    d = upload(wl)
+    path = torch.tensor([[0, 1, 2, 0, 0, 0], [0, 2, 0, 0, 0, 0]], dtype=torch.int32, device="cuda")
+    plen = torch.tensor([3, 2], dtype=torch.int32, device="cuda")
+    S = d["S0"].clone()
+    S1, st = G.commit_replay(S, d["k"], d["v"], d["g"], d["beta"], d["node_offset"], d["parent"], path, plen,
+                             max_nodes=6, S_out=S)
+    torch.cuda.synchronize()
+    assert list(host(st)) == [0, O.STATUS_BAD_PATH]
+    So, _ = O.commit_batch(*oracle_inputs(wl), host(path), host(plen), wl.Hv, wl.Hk, max_nodes=6)
+    assert matwise_rel_err(host(S1)[:1], So[:1]) <= TOL
+    assert np.array_equal(host(S1)[1], wl.S0[1])
