@@ -205,7 +205,20 @@ def next_rows(args, wl, pools, mn, stream):
     Lr = pools[0]["plen"].cpu().numpy()
     # replay reads k and v rows and the two gates of each path node instead of U
     rb = int(commit_bytes(wl, Lr) - (wl.Hv * Lr * (4 * D + 4)).sum() + (wl.Hv * Lr * (2 * D + 8)).sum())
-    return {"commit_replay": {"avg_us": t_replay, "alg_bytes": rb, "alg_GBps": rb / (t_replay * 1e-6) / 1e9,
+    # load-adaptive budget: half of the batch's nodes, no threshold
+    prob = torch.from_numpy(W.acceptance_probs(wl)).to(dev)
+    surv = torch.empty((wl.T,), dtype=torch.float32, device=dev)
+    keep = torch.empty((wl.T,), dtype=torch.uint8, device=dev)
+    kept = torch.empty((B,), dtype=torch.int32, device=dev)
+
+    def budget(i):
+        p = pools[i % len(pools)]
+        G.budget_select(p["off"], p["par"], prob, wl.T // 2, 0.0, max_nodes=mn, survival=surv, keep=keep,
+                        kept=kept, status=st, stream=stream)
+
+    t_budget = _time_launches(budget, n, stream)
+    return {"budget_select": {"avg_us": t_budget, "budget": wl.T // 2, "nodes": wl.T},
+            "commit_replay": {"avg_us": t_replay, "alg_bytes": rb, "alg_GBps": rb / (t_replay * 1e-6) / 1e9,
                               "hbm_frac": rb / (t_replay * 1e-6) / 1e9 / HBM_PEAK_GBS,
                               "mean_accepted_len": float(Lr.mean())},
             "accept_greedy": {"avg_us": t_greedy, "mean_accepted_len": float(L.mean())},

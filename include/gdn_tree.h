@@ -205,6 +205,25 @@ int gdn_tree_accept_commit(const gdn_tree_dims *dims, const float *S0, float *S_
                            int32_t *path, int32_t *path_len, int32_t *status, void *stream);
 
 /*
+ * gdn_tree_budget_select -- load-adaptive choice of the draft nodes to verify.
+ *
+ * survival[t] = product of accept_prob over t's root-to-node path, formed in
+ * float32 root first (s = s_parent * p) (DSpark adaptive verification: per-token
+ * acceptance -> per-position survival; TreeSpark: a branch's value).  Nodes of
+ * all valid requests are ordered by survival descending, then depth, then
+ * global index; the first `budget` of them with survival >= threshold get
+ * keep[t] = 1 (DSpark: a global budget to the positions with the highest
+ * survival across requests; TreeSpark: growth stops below a threshold).  Every
+ * ancestor of a kept node is kept.  kept[b] counts request b's kept nodes.
+ * accept_prob float32 [T] must lie in [0, 1]; survival float32 [T]; keep
+ * uint8 [T]; kept int32 [B].  Invalid requests (status 1..3) get NaN survival
+ * and no kept node.  Requires T < 2^24.  Three small launches; no workspace.
+ */
+int gdn_tree_budget_select(const gdn_tree_dims *dims, const int32_t *node_offset, const int32_t *parent,
+                           const float *accept_prob, int32_t budget, float threshold, float *survival,
+                           uint8_t *keep, int32_t *kept, int32_t *status, void *stream);
+
+/*
  * gdn_tree_verify_storeall -- the snapshot-per-node comparison scheme.
  *
  * Walks each request's nodes in order with the sequential rule and writes

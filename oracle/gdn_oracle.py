@@ -48,7 +48,7 @@ __all__ = [
     "parents_valid", "ancestry", "depths", "root_to_node", "accepted_path", "gated_delta_step",
     "verify_unit", "commit_unit", "replay_commit_unit", "verify_request", "verify_batch",
     "commit_batch", "accepted_path_batch", "verify_storeall_batch", "commit_storeall_batch",
-    "state_bytes", "PINS", "greedy_accept", "greedy_accept_batch",
+    "state_bytes", "PINS", "greedy_accept", "greedy_accept_batch", "survival", "budget_select",
 ]
 
 # Status codes written per request.  These numbers are part of the C-ABI's
@@ -77,6 +77,9 @@ PINS = {
                    "verify-then-commit composition",
     "verify_storeall_batch": "node states equal the per-path sequential states; state count "
                              "of a depth-3 chain is 4 including S0 (TreeWY, Prior work)",
+    "survival": "equals the running product over each explicit root-to-node path; chain closed form",
+    "budget_select": "order property (every kept node outranks every dropped one), ancestor closure, "
+                     "count = min(budget, nodes at or above the threshold), threshold respected",
     "greedy_accept": "brute force over every root-first path: with distinct sibling tokens the "
                      "result is the longest path whose every token matches the target's "
                      "prediction at its parent; a chain accepts exactly its matching prefix",
@@ -442,6 +445,59 @@ def greedy_accept_batch(node_offset, parent, draft, target_next, root_next, max_
         plen[b] = len(pth)
         path[b, :len(pth)] = pth
     return acc, path, plen, status
+
+
+def survival(parent: Sequence[int], p: Sequence[float]) -> np.ndarray:
+    """Probability that the draft survives verification down to each node: the
+    product of the acceptance probabilities along its root-to-node path (DSpark
+    adaptive verification: per-token acceptance, then per-position survival;
+    TreeSpark: a branch's value is the product of calibrated estimates along it).
+    Computed in float32, root first: s_t = s_parent(t) * p_t, so that a device
+    making the same fp32 products takes the same selection decisions."""
+    s = np.zeros(len(parent), dtype=np.float32)
+    for t, par in enumerate(parent):
+        pt = np.float32(p[t])
+        s[t] = pt if int(par) < 0 else np.float32(s[int(par)] * pt)
+    return s
+
+
+def budget_select(node_offset, parent, p, budget: int, threshold: float, max_nodes: int = MAX_NODES):
+    """Load-adaptive choice of the nodes to verify (DSpark: a global budget B is
+    given to the positions with the highest survival across requests; TreeSpark:
+    growth stops when the best remaining value is below a threshold).
+
+    Order: survival descending, then depth ascending, then global node index
+    ascending (a total order in which every ancestor precedes its descendants,
+    survival never increasing along a path).  Keep the first `budget` nodes of
+    the valid requests, then drop those with survival below `threshold`.
+    Returns (survival f32 [T] (NaN for invalid requests), keep u8 [T],
+    kept_per_request i32 [B], status i32 [B]).
+    """
+    B = len(node_offset) - 1
+    T = len(parent)
+    surv = np.full(T, np.nan, dtype=np.float32)
+    keep = np.zeros(T, dtype=np.uint8)
+    status = np.zeros(B, dtype=np.int32)
+    cand = []
+    for b in range(B):
+        st = _request_status(node_offset, b, T, max_nodes, parent)
+        status[b] = st
+        if st != STATUS_OK:
+            continue
+        lo, hi = int(node_offset[b]), int(node_offset[b + 1])
+        sb = survival(parent[lo:hi], p[lo:hi])
+        dep = depths(parent[lo:hi])
+        surv[lo:hi] = sb
+        cand += [(-float(sb[t]), dep[t], lo + t) for t in range(hi - lo)]
+    cand.sort()
+    for _, _, gt in cand[:max(0, int(budget))]:
+        if surv[gt] >= np.float32(threshold):
+            keep[gt] = 1
+    counts = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        if status[b] == STATUS_OK:
+            counts[b] = int(keep[int(node_offset[b]):int(node_offset[b + 1])].sum())
+    return surv, keep, counts, status
 
 
 def state_bytes(B: int, Hv: int, d_k: int, d_v: int, T: int, storeall: bool) -> int:

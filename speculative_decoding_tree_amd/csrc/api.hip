@@ -232,6 +232,26 @@ int gdn_tree_accept_commit(const gdn_tree_dims *dims, const float *S0, float *S_
     return finish(gdn::launch_accept_commit(a, (hipStream_t)stream));
 }
 
+int gdn_tree_budget_select(const gdn_tree_dims *dims, const int32_t *node_offset, const int32_t *parent,
+                           const float *accept_prob, int32_t budget, float threshold, float *survival,
+                           uint8_t *keep, int32_t *kept, int32_t *status, void *stream) {
+    int rc = check_dims(dims);
+    if (rc != GDN_TREE_OK || dims->B == 0) return rc;
+    if (dims->T >= (1 << 24)) return GDN_TREE_E_SIZE;
+    if (!node_offset || !kept) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && (!parent || !accept_prob || !survival || !keep)) return GDN_TREE_E_NULL;
+    Args a = base_args(dims);
+    a.node_offset = node_offset;
+    a.parent = parent;
+    a.prob = accept_prob;
+    a.survival = survival;
+    a.keep = keep;
+    a.kept = kept;
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_budget_select(a, budget, threshold, (hipStream_t)stream));
+}
+
 int gdn_tree_verify_storeall(const gdn_tree_dims *dims, const float *S0, const int32_t *state_slot,
                              const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                              const float *beta, const int32_t *node_offset, const int32_t *parent,

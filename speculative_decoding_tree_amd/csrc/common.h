@@ -29,6 +29,10 @@ struct Args {
     const float *node_state_in;
     const int32_t *draft_token, *target_token, *root_token;
     int32_t *accept_out;
+    const float *prob;      // budget selection: acceptance probabilities [T]
+    float *survival;        // [T]
+    uint8_t *keep;          // [T]
+    int32_t *kept;          // [B]
 };
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

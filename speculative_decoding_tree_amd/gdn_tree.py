@@ -58,6 +58,8 @@ _SIGS = {
     "gdn_tree_accept_greedy": [ctypes.POINTER(Dims)] + [_P] * 10,
     "gdn_tree_accept_commit": [ctypes.POINTER(Dims)] + [_P] * 16,
     "gdn_tree_commit_replay": [ctypes.POINTER(Dims)] + [_P] * 13,
+    "gdn_tree_budget_select": [ctypes.POINTER(Dims), _P, _P, _P, ctypes.c_int32, ctypes.c_float,
+                               _P, _P, _P, _P, _P],
 }
 
 _lib = None
@@ -351,3 +353,24 @@ def commit_replay(S0, k, v, g, beta, node_offset, parent, path, path_len, max_no
         _ptr(status, "status", _I32, (B,)), _stream(stream))
     _check("gdn_tree_commit_replay", rc)
     return S_out, status
+
+
+def budget_select(node_offset, parent, accept_prob, budget: int, threshold: float, max_nodes: int,
+                  survival=None, keep=None, kept=None, status=None, stream=None):
+    """gdn_tree_budget_select.  Returns (survival, keep (uint8), kept, status)."""
+    B = int(node_offset.numel()) - 1
+    T = int(parent.numel())
+    dev = node_offset.device
+    survival = survival if survival is not None else torch.empty((T,), dtype=torch.float32, device=dev)
+    keep = keep if keep is not None else torch.empty((T,), dtype=torch.uint8, device=dev)
+    kept = kept if kept is not None else torch.empty((B,), dtype=torch.int32, device=dev)
+    status = status if status is not None else torch.empty((B,), dtype=torch.int32, device=dev)
+    dims = make_dims(B, 1, 1, T, max_nodes, 1)
+    rc = lib().gdn_tree_budget_select(
+        ctypes.byref(dims),
+        _ptr(node_offset, "node_offset", _I32, (B + 1,)), _ptr(parent, "parent", _I32, (T,)),
+        _ptr(accept_prob, "accept_prob", _F32, (T,)), int(budget), float(threshold),
+        _ptr(survival, "survival", _F32, (T,)), _ptr(keep, "keep", (torch.uint8,), (T,)),
+        _ptr(kept, "kept", _I32, (B,)), _ptr(status, "status", _I32, (B,)), _stream(stream))
+    _check("gdn_tree_budget_select", rc)
+    return survival, keep, kept, status

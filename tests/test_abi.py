@@ -14,7 +14,7 @@ def test_library_exports_every_declared_symbol():
     names = G.declared_symbols()
     assert {"gdn_tree_verify", "gdn_tree_commit", "gdn_tree_accepted_path", "gdn_tree_verify_storeall",
             "gdn_tree_commit_storeall", "gdn_tree_state_bytes", "gdn_tree_strerror",
-            "gdn_tree_abi_version", "gdn_tree_accept_greedy", "gdn_tree_accept_commit", "gdn_tree_commit_replay"} <= set(names)
+            "gdn_tree_abi_version", "gdn_tree_accept_greedy", "gdn_tree_accept_commit", "gdn_tree_commit_replay", "gdn_tree_budget_select"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert G.abi_version() == 1

@@ -383,3 +383,40 @@ def test_commit_replay_inplace_and_bad_path():
     So, _ = O.commit_batch(*oracle_inputs(wl), host(path), host(plen), wl.Hv, wl.Hk, max_nodes=6)
     assert matwise_rel_err(host(S1)[:1], So[:1]) <= TOL
     assert np.array_equal(host(S1)[1], wl.S0[1])
+
+
+# ----------------------------------------------------------------------------
+# load-adaptive budget selection
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("budget_frac,thr", [(0.0, 0.0), (0.1, 0.0), (0.5, 0.05), (0.9, 0.3), (1.2, 0.0)])
+def test_budget_select_bit_exact(budget_frac, thr):
+    wl = W.make_c5(per_kind=8, Hv=2, Hk=1, seed=4)
+    p = W.acceptance_probs(wl, seed=5)
+    p[::11] = 1.0                                    # exact survival ties along paths
+    budget = int(budget_frac * wl.T)
+    so, ko, co, sto = O.budget_select(wl.node_offset, wl.parent, p, budget, thr)
+    d = upload(wl)
+    s, keep, kept, st = G.budget_select(d["node_offset"], d["parent"], torch.from_numpy(p).cuda(), budget, thr,
+                                        max_nodes=wl.max_nodes)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(keep), ko) and np.array_equal(host(kept), co) and np.array_equal(host(st), sto)
+
+
+def test_budget_select_invalid_request_and_full_batch():
+    wl = W.make_c5()
+    p = W.acceptance_probs(wl)
+    par = wl.parent.copy()
+    par[wl.node_offset[7] + 1] = 5                   # request 7 breaks parent order
+    so, ko, co, sto = O.budget_select(wl.node_offset, par, p, wl.T // 3, 0.01)
+    assert sto[7] == O.STATUS_BAD_PARENT
+    d = upload(wl)
+    s, keep, kept, st = G.budget_select(d["node_offset"], torch.from_numpy(par).cuda(), torch.from_numpy(p).cuda(),
+                                        wl.T // 3, 0.01, max_nodes=wl.max_nodes)
+    torch.cuda.synchronize()
+    sh = host(s)
+    assert np.array_equal(np.isnan(sh), np.isnan(so))
+    ok = ~np.isnan(so)
+    assert np.array_equal(sh[ok].view(np.uint32), so[ok].view(np.uint32))
+    assert np.array_equal(host(keep), ko) and np.array_equal(host(kept), co) and np.array_equal(host(st), sto)

@@ -455,3 +455,59 @@ def test_greedy_tokens_generator_contract():
         for t, p in enumerate(par):
             kids.setdefault(int(p), []).append(int(draft[lo + t]))
         assert all(len(v) == len(set(v)) for v in kids.values())
+
+
+# ----------------------------------------------------------------------------
+# survival and the load-adaptive budget
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", range(1, 7))
+def test_survival_is_path_product(n):
+    rng = np.random.default_rng(30 + n)
+    for par in all_trees(n):
+        p = rng.random(n).astype(np.float32)
+        s = O.survival(par, p)
+        for t in range(n):
+            want = np.float32(1.0)
+            for j in O.root_to_node(par, t):
+                want = np.float32(want * p[j]) if j != O.root_to_node(par, t)[0] else p[j]
+            assert s[t] == want
+
+
+def test_survival_chain_closed_form():
+    p = np.full(10, 0.5, np.float32)
+    s = O.survival(list(range(-1, 9)), p)
+    assert np.array_equal(s, (0.5 ** np.arange(1, 11)).astype(np.float32))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_budget_select_properties(seed):
+    import workloads as W
+    wl = W.make_c5(per_kind=3, Hv=2, Hk=1, seed=seed)
+    p = W.acceptance_probs(wl, seed=seed)
+    p[::7] = 1.0                                     # exact ties along paths
+    for budget, thr in ((0, 0.0), (10, 0.0), (wl.T // 2, 0.05), (wl.T + 5, 0.2), (wl.T, 0.0)):
+        s, keep, cnt, st = O.budget_select(wl.node_offset, wl.parent, p, budget, thr)
+        assert np.all(st == 0)
+        eligible = int((s >= np.float32(thr)).sum())
+        # the threshold only removes a suffix of the order, so the count is exact
+        assert keep.sum() == min(budget, eligible)
+        kept, dropped = s[keep == 1], s[(keep == 0) & (s >= np.float32(thr))]
+        if len(kept) and len(dropped):
+            assert kept.min() >= dropped.max()
+        assert np.all(kept >= np.float32(thr))
+        for b in range(wl.B):
+            lo = wl.node_offset[b]
+            par = wl.parents_of(b)
+            for t in range(len(par)):
+                if keep[lo + t] and par[t] >= 0:
+                    assert keep[lo + par[t]]             # ancestor-closed
+            assert cnt[b] == keep[lo:lo + len(par)].sum()
+
+
+def test_acceptance_probs_follow_pages_decay():
+    import workloads as W
+    facts = json.load(open(os.path.join(GOLDEN, "pages_facts.json")))["dspark_acceptance_by_position"]
+    wl = W.make_custom([W.chain(7)] * 400, [0] * 400, Hv=1, Hk=1, d=4)
+    p = W.acceptance_probs(wl).reshape(400, 7)
+    assert p[:, 0].mean() > facts["first_above"] and p[:, -1].mean() < facts["last_below"]

@@ -36,7 +36,7 @@ import numpy as np
 __all__ = [
     "Workload", "CONFIGS", "make", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "chain", "root_branch", "random_tree", "accept_by_edge", "tree_depths",
-    "zero_pad", "subset", "greedy_tokens",
+    "zero_pad", "subset", "greedy_tokens", "acceptance_probs",
 ]
 
 
@@ -388,3 +388,21 @@ def greedy_tokens(wl: Workload, vocab: int = 32000, p_match: float = 0.7, seed: 
             else:
                 target[lo + pos] = want
     return draft, target, root
+
+
+def acceptance_probs(wl: Workload, first: float = 0.75, last: float = 0.08, positions: int = 7,
+                     spread: float = 0.08, seed: int = 2) -> np.ndarray:
+    """Per-node acceptance probability estimates (float32 [T]) that fall with
+    depth: the mean is `first` at depth 1 and `last` at depth `positions`,
+    geometric in between and flat beyond (the DSpark page reports the first of
+    seven draft tokens accepted more than 70% of the time and the last less
+    than 10%), with N(0, spread^2) noise clipped to [0, 1]."""
+    rng = np.random.default_rng(seed)
+    p = np.zeros(wl.T, dtype=np.float32)
+    ratio = (last / first) ** (1.0 / max(1, positions - 1))
+    for b in range(wl.B):
+        lo = int(wl.node_offset[b])
+        dep = tree_depths(wl.parents_of(b))
+        mean = first * ratio ** (np.minimum(dep, positions) - 1)
+        p[lo:lo + len(dep)] = np.clip(mean + spread * rng.standard_normal(len(dep)), 0.0, 1.0)
+    return p
