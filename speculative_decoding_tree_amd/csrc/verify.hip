@@ -74,19 +74,17 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Coefficient table T is indexed by ancestor position: the ancestor j of t
-// at depth dep(j) sits at position q = dep(j) - 1 of t's root-first list.
-//   T[t][q], q < dep(t) - 1 : A = beta_t D_tj (k_t.k_j)   (strict lower triangle)
-//   T[q][t], q < dep(t)     : P = D_tj (q_t.k_j)           (upper triangle)
-// alistT[q][t] is the node at position q of t's list (root first).
-// Coefficient table T is indexed by ancestor position: the ancestor j of t
-// at depth dep(j) sits at position q = dep(j) - 1 of t's root-first list.
-//   T[t][q], q < dep(t) - 1 : A = beta_t D_tj (k_t.k_j)   (strict lower triangle)
-//   T[q][t], q < dep(t)     : P = D_tj (q_t.k_j)           (upper triangle)
+// Coefficient table T:
+//   T[t][q], q < dep(t) - 1 : A = beta_t D_tj (k_t.k_j) for the ancestor j of t at
+//                             position q = dep(j) - 1 of t's root-first list (strict
+//                             lower triangle; read by the solve)
+//   T[j][t], j <= t         : P_tj = D_tj (q_t.k_j) for ancestors j, 0 otherwise
+//                             (upper triangle, node-indexed: the A operand of the
+//                             output product (P masked) U)
 template <int NM>
 struct VerifySmem {
     float ru[NM][D + 4];                       // R, then U after the solve
-    float T[NM][NM];
+    float T[NM][NM + 4];
     __attribute__((aligned(16))) uint64_t anc[NM];
     __attribute__((aligned(16))) float gam[NM];
     __attribute__((aligned(16))) float beta[NM];
@@ -115,7 +113,7 @@ __device__ __forceinline__ void load_rows(const uint16_t *base, size_t row_strid
 }
 
 template <int NM>
-__global__ __launch_bounds__(NT) void verify_kernel(Args a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(Args a) {
     constexpr int KT = NM / 16;   // max 16-node tiles
     __shared__ VerifySmem<NM> sm;
 
@@ -325,9 +323,10 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
                 const float g2[4] = {g24.x, g24.y, g24.z, g24.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    // inclusive ancestor jcol of r: P = D_rj (q_r.k_j) at [dep(j)-1][r]
+                    // P_rj = D_rj (q_r.k_j) for an inclusive ancestor jcol of r, 0 for other j <= r
                     const int r = r0 + i;
-                    if (jcol < N && ((sm.anc[r] >> jcol) & 1ull)) sm.T[qj][r] = exp2_fast(g2[i] - G2_j) * gq[i];
+                    if (jcol < N && jcol <= r)
+                        sm.T[jcol][r] = ((sm.anc[r] >> jcol) & 1ull) ? exp2_fast(g2[i] - G2_j) * gq[i] : 0.f;
                 }
             }
         }
@@ -367,50 +366,69 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
         }
     }
 
-    // ---- outputs o_t = gamma_t Z_t + sum_{j in anc*(t)} P_tj u_j, every tile at once ----
+    // ---- outputs O = diag(gamma) Z + (P masked) U on MFMA ----
+    // A operand: P rows t = 16 tau + n, elements j = 32 ks + 8 grp + e (from the
+    // transposed table; j > t, j >= N are 0 by select).  B operand: U rows j,
+    // this wave's columns (rows j >= N are 0 by select).  Both are split into
+    // bf16 hi + lo and combined as hi.hi + hi.lo + lo.hi (~16 mantissa bits).
     {
-        int deps[KT][4];
-        uint64_t am[KT][4];
-        int dmax = 0;
+        const int nks = (N + 31) >> 5;
 #pragma unroll
         for (int tau = 0; tau < KT; ++tau) {
-            const int r0 = 16 * tau + 4 * grp;
             if (tau < nkt) {
+                const int r0 = 16 * tau + 4 * grp;
                 const float4 gm4 = *reinterpret_cast<const float4 *>(&sm.gam[r0]);
-                const int4 dp4 = *reinterpret_cast<const int4 *>(&sm.dep[r0]);
                 const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
-                const int dp[4] = {dp4.x, dp4.y, dp4.z, dp4.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    deps[tau][i] = r0 + i < N ? dp[i] : 0;
-                    am[tau][i] = sm.anc[r0 + i];
-                    dmax = max(dmax, deps[tau][i]);
                     zt[tau][0][i] *= gm[i];
                     zt[tau][1][i] *= gm[i];
                 }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    deps[tau][i] = 0;
-                    am[tau][i] = 0;
-                }
             }
         }
-        for (int q = 0; q < dmax; ++q) {   // position q of every row's ancestor list
 #pragma unroll
-            for (int tau = 0; tau < KT; ++tau) {
-                if (tau < nkt) {
-                    const int r0 = 16 * tau + 4 * grp;
-                    const float4 p4 = *reinterpret_cast<const float4 *>(&sm.T[q][r0]);
-                    const float pj[4] = {p4.x, p4.y, p4.z, p4.w};
+        for (int ks = 0; ks < (NM + 31) / 32; ++ks) {
+            if (ks < nks) {
+                // B fragments for this K step: U rows 32 ks + 8 grp + e, columns c (n-tile 0), c+1 (n-tile 1)
+                u32x4 ubh[2], ubl[2];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if (q < deps[tau][i]) {
-                            const int j = __builtin_ctzll(am[tau][i]);
-                            am[tau][i] &= am[tau][i] - 1;
-                            const float2 uj = *reinterpret_cast<const float2 *>(&sm.ru[j][c]);
-                            zt[tau][0][i] = fmaf(pj[i], uj.x, zt[tau][0][i]);
-                            zt[tau][1][i] = fmaf(pj[i], uj.y, zt[tau][1][i]);
+                for (int pr = 0; pr < 4; ++pr) {
+                    const int j0 = 32 * ks + 8 * grp + 2 * pr;
+                    const int jr = j0 < NM ? j0 : 0;   // rows past the table (NM = 16) are read in range, then zeroed
+                    float2 u0 = *reinterpret_cast<const float2 *>(&sm.ru[jr][c]);
+                    float2 u1 = *reinterpret_cast<const float2 *>(&sm.ru[jr + 1][c]);
+                    if (j0 >= N) u0 = make_float2(0.f, 0.f);
+                    if (j0 + 1 >= N) u1 = make_float2(0.f, 0.f);
+                    uint32_t h0, l0, h1, l1;
+                    split_bf16x2(u0.x, u1.x, h0, l0);
+                    split_bf16x2(u0.y, u1.y, h1, l1);
+                    ubh[0][pr] = h0;
+                    ubl[0][pr] = l0;
+                    ubh[1][pr] = h1;
+                    ubl[1][pr] = l1;
+                }
+#pragma unroll
+                for (int tau = 0; tau < KT; ++tau) {
+                    if (tau < nkt) {
+                        const int t = 16 * tau + n;
+                        u32x4 pah, pal;
+#pragma unroll
+                        for (int pr = 0; pr < 4; ++pr) {
+                            const int j0 = 32 * ks + 8 * grp + 2 * pr;
+                            const int jr = j0 < NM ? j0 : 0;
+                            float p0 = sm.T[jr][t], p1 = sm.T[jr + 1][t];
+                            if (j0 > t || j0 >= N) p0 = 0.f;
+                            if (j0 + 1 > t || j0 + 1 >= N) p1 = 0.f;
+                            uint32_t hh, ll;
+                            split_bf16x2(p0, p1, hh, ll);
+                            pah[pr] = hh;
+                            pal[pr] = ll;
+                        }
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) {
+                            zt[tau][jj] = mfma(pah, ubh[jj], zt[tau][jj]);
+                            zt[tau][jj] = mfma(pah, ubl[jj], zt[tau][jj]);
+                            zt[tau][jj] = mfma(pal, ubh[jj], zt[tau][jj]);
                         }
                     }
                 }
@@ -424,8 +442,7 @@ __global__ __launch_bounds__(NT) void verify_kernel(Args a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * tau + 4 * grp + i;
-                    if (r < N)
-                        st_stream2(Obase + (size_t)r * ostride, make_float2(zt[tau][0][i], zt[tau][1][i]));
+                    if (r < N) st_stream2(Obase + (size_t)r * ostride, make_float2(zt[tau][0][i], zt[tau][1][i]));
                 }
     }
 }
