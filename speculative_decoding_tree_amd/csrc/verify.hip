@@ -24,7 +24,8 @@
 // H0).  Lane (n, grp) of the wave loads float2 columns 32w + 2n, 2n+1 of rows
 // 32s + 8grp .. +7; the even columns form n-tile 0 and the odd ones n-tile 1,
 // so every load instruction reads whole 128-byte row segments.  A operands
-// (16-node tiles of K or Q rows) come straight from L2.  One MFMA pass over
+// (16-node tiles of K or Q rows) come from L2, fetched one tile ahead, the
+// first ones together with H0.  One MFMA pass over
 // the tiles gives W = K H0 (turned into R in LDS at once), Z = Q H0 (kept in
 // registers until the outputs) and, in wave w, the grams against K^T for node
 // columns 16w .. 16w+15, whose ancestor entries are scaled on the spot into a
@@ -115,6 +116,9 @@ __device__ __forceinline__ void load_rows(const uint16_t *base, size_t row_strid
 template <int NM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(Args a) {
     constexpr int KT = NM / 16;   // max 16-node tiles
+    // Q tiles are fetched one tile ahead where the registers allow it (the
+    // 32-node variant would spill; it loads each Q tile after the previous one).
+    constexpr bool QPF = NM != 32;
     __shared__ VerifySmem<NM> sm;
 
     const int n_units = a.B * a.Hv;
@@ -138,12 +142,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
     const size_t krow = (size_t)a.Hk * D;   // q/k row stride (elements)
     const uint16_t *kbase = a.k + ((size_t)lo * a.Hk + hk) * D;
     const uint16_t *qbase = a.q + ((size_t)lo * a.Hk + hk) * D;
+    const uint16_t *vbase = a.v + ((size_t)lo * a.Hv + h) * D + c;
+    const size_t vrow = (size_t)a.Hv * D;
 
     // ---- issue the unit's global reads: per-node scalars, H0, v ----
     int p_mine = -1;
     float g_mine = 0.f, b_mine = 0.f;
     float2 hraw[4][8];
-    uint32_t vv[KT][4];
+    uint32_t vv[4];   // v of the current K tile's rows (the next tile's come with its A fragments)
+    // A fragments of the first K and Q tiles and the K rows of this wave's gram
+    // columns are issued with H0; later tiles are fetched one tile ahead.
+    const bool gram = 16 * w < N;
+    const int jcol = 16 * w + n;   // gram column (node) of this lane
+    u32x4 ka[4], qa[4], bg[4];
     if (st == GDN_TREE_S_OK && N > 0) {
         const int tc = min(tid, N - 1);
         const size_t gi = (size_t)(lo + tc) * a.Hv + h;
@@ -158,13 +169,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
                 for (int e = 0; e < 8; ++e)
                     hraw[s][e] = ld_stream2(H + (32 * s + e) * D);
         }
-        const uint16_t *V = a.v + ((size_t)lo * a.Hv + h) * D + c;
-        const size_t vrow = (size_t)a.Hv * D;
 #pragma unroll
-        for (int tau = 0; tau < KT; ++tau)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)   // rows past N read the last row; their R rows are never used
-                vv[tau][i] = *reinterpret_cast<const uint32_t *>(V + (size_t)min(16 * tau + 4 * grp + i, N - 1) * vrow);
+        for (int i = 0; i < 4; ++i)   // rows past N read the last row; their R rows are never used
+            vv[i] = *reinterpret_cast<const uint32_t *>(vbase + (size_t)min(4 * grp + i, N - 1) * vrow);
+        load_rows(kbase, krow, jcol, N, grp, bg);
+        load_rows(kbase, krow, n, N, grp, ka);
         if (tid < N) sm.beta[tid] = b_mine;
         if (w == 0) {
             const bool bad = (tid < N) && (p_mine < -1 || p_mine >= tid);
@@ -242,7 +251,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
     }
 
     // ---- B operands: H0 slab (hi, lo) and K^T for node columns 16w .. 16w+15 ----
-    u32x4 bhi[4][2], blo[4][2], bg[4];
+    u32x4 bhi[4][2], blo[4][2];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -256,9 +265,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
             blo[s][1][pr] = l1;
         }
     }
-    const bool gram = 16 * w < N;
-    const int jcol = 16 * w + n;   // gram column (node) of this lane
-    if (gram) load_rows(kbase, krow, jcol, N, grp, bg);
     lds_barrier();   // ancestry, G, gamma, depths, levels visible
 
     // ---- one MFMA pass: K tiles -> R, Q tiles -> Z (registers), grams -> T ----
@@ -269,8 +275,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
 #pragma unroll
     for (int tau = 0; tau < KT; ++tau) {   // K tiles: R rows and A entries
         if (tau < nkt) {
-            u32x4 ak[4];
-            load_rows(kbase, krow, 16 * tau + n, N, grp, ak);
+            u32x4 ak[4], nx[4];
+            uint32_t vc[4], vn[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                ak[s] = ka[s];
+                vc[s] = vv[s];
+            }
+            if (tau + 1 == nkt) load_rows(qbase, krow, n, N, grp, qa);
+            if (tau + 1 < KT) {
+                load_rows(kbase, krow, 16 * (tau + 1) + n, N, grp, nx);   // zeros past N
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    vn[i] = *reinterpret_cast<const uint32_t *>(vbase + (size_t)min(16 * (tau + 1) + 4 * grp + i, N - 1) * vrow);
+            }
             f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0, gk = w0;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -292,13 +310,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
             for (int i = 0; i < 4; ++i) {
                 const int r = r0 + i;
                 float2 rr;
-                rr.x = bt[i] * (bf16_lo(vv[tau][i]) - gm[i] * w0[i]);
-                rr.y = bt[i] * (bf16_hi(vv[tau][i]) - gm[i] * w1[i]);
+                rr.x = bt[i] * (bf16_lo(vc[i]) - gm[i] * w0[i]);
+                rr.y = bt[i] * (bf16_hi(vc[i]) - gm[i] * w1[i]);
                 *reinterpret_cast<float2 *>(&sm.ru[r][c]) = rr;
                 // strict ancestor jcol of r: A = beta_r D_rj (k_r.k_j) at position dep(j)-1
                 if (gram && jcol < r && ((sm.anc[r] >> jcol) & 1ull))
                     sm.T[r][qj] = bt[i] * exp2_fast(g2[i] - G2_j) * gk[i];
             }
+            if (tau + 1 < KT)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    ka[s] = nx[s];
+                    vv[s] = vn[s];
+                }
         }
         __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
     }
@@ -306,8 +330,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
     for (int tau = 0; tau < KT; ++tau) {   // Q tiles: Z kept in registers, P entries
         zt[tau][0] = zt[tau][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (tau < nkt) {
-            u32x4 aq[4];
-            load_rows(qbase, krow, 16 * tau + n, N, grp, aq);
+            u32x4 aq[4], nx[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) aq[s] = qa[s];
+            if (QPF && tau + 1 < KT) load_rows(qbase, krow, 16 * (tau + 1) + n, N, grp, nx);
             f32x4 gq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -327,6 +353,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
                     const int r = r0 + i;
                     if (jcol < N && jcol <= r)
                         sm.T[jcol][r] = ((sm.anc[r] >> jcol) & 1ull) ? exp2_fast(g2[i] - G2_j) * gq[i] : 0.f;
+                }
+            }
+            if (tau + 1 < KT) {
+                if (QPF) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) qa[s] = nx[s];
+                } else {
+                    load_rows(qbase, krow, 16 * (tau + 1) + n, N, grp, qa);
                 }
             }
         }
