@@ -101,12 +101,15 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 // A fragment of a 16-node tile: lane (n, grp) gets row `row`, elements
 // 32 s + 8 grp .. +7 for s = 0..3 (16 bytes each); zero past the last node.
-__device__ __forceinline__ void load_rows(const uint16_t *base, size_t row_stride, int row, int nrows,
+// `base` is the same for the whole workgroup and the per-lane part is a
+// 32-bit byte offset, so the address needs no 64-bit vector registers.
+__device__ __forceinline__ void load_rows(const uint16_t *base, uint32_t row_stride, int row, int nrows,
                                           int grp, u32x4 (&f)[4]) {
     if (row < nrows) {
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(base + (size_t)row * row_stride + 8 * grp);
+        const uint32_t off = ((uint32_t)row * row_stride + 8u * grp) * 2u;
+        const char *p = reinterpret_cast<const char *>(base) + off;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) f[s] = p[4 * s];
+        for (int s = 0; s < 4; ++s) f[s] = *reinterpret_cast<const u32x4 *>(p + 64 * s);
     } else {
 #pragma unroll
         for (int s = 0; s < 4; ++s) f[s] = u32x4{0u, 0u, 0u, 0u};
@@ -139,11 +142,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
         return;
     }
     const int slot = resolve_slot(a, b);
-    const size_t krow = (size_t)a.Hk * D;   // q/k row stride (elements)
+    const uint32_t krow = (uint32_t)a.Hk * D;   // q/k row stride (elements)
     const uint16_t *kbase = a.k + ((size_t)lo * a.Hk + hk) * D;
     const uint16_t *qbase = a.q + ((size_t)lo * a.Hk + hk) * D;
-    const uint16_t *vbase = a.v + ((size_t)lo * a.Hv + h) * D + c;
-    const size_t vrow = (size_t)a.Hv * D;
+    const uint16_t *vbase = a.v + ((size_t)lo * a.Hv + h) * D;   // + 32-bit per-lane offsets
+    const uint32_t vrow = (uint32_t)a.Hv * D;
 
     // ---- issue the unit's global reads: per-node scalars, H0, v ----
     int p_mine = -1;
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)   // rows past N read the last row; their R rows are never used
-            vv[i] = *reinterpret_cast<const uint32_t *>(vbase + (size_t)min(4 * grp + i, N - 1) * vrow);
+            vv[i] = *reinterpret_cast<const uint32_t *>(vbase + ((uint32_t)min(4 * grp + i, N - 1) * vrow + c));
         load_rows(kbase, krow, jcol, N, grp, bg);
         load_rows(kbase, krow, n, N, grp, ka);
         if (tid < N) sm.beta[tid] = b_mine;
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
                 load_rows(kbase, krow, 16 * (tau + 1) + n, N, grp, nx);   // zeros past N
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    vn[i] = *reinterpret_cast<const uint32_t *>(vbase + (size_t)min(16 * (tau + 1) + 4 * grp + i, N - 1) * vrow);
+                    vn[i] = *reinterpret_cast<const uint32_t *>(vbase + ((uint32_t)min(16 * (tau + 1) + 4 * grp + i, N - 1) * vrow + c));
             }
             f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0, gk = w0;
 #pragma unroll
