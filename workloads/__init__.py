@@ -37,6 +37,7 @@ __all__ = [
     "Workload", "CONFIGS", "make", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "chain", "root_branch", "random_tree", "accept_by_edge", "tree_depths",
     "zero_pad", "subset", "greedy_tokens", "acceptance_probs",
+    "AttnWorkload", "make_attn", "make_attn_small", "make_attn_c5",
 ]
 
 
@@ -406,3 +407,93 @@ def acceptance_probs(wl: Workload, first: float = 0.75, last: float = 0.08, posi
         mean = first * ratio ** (np.minimum(dep, positions) - 1)
         p[lo:lo + len(dep)] = np.clip(mean + spread * rng.standard_normal(len(dep)), 0.0, 1.0)
     return p
+
+
+# ----------------------------------------------------------------------------
+# Tree-bias attention inputs (the hybrid's attention layers over the same trees)
+# ----------------------------------------------------------------------------
+
+@dataclass
+class AttnWorkload:
+    """Inputs of ancestry-masked decode attention for a draft forest.
+
+    q bf16 bits [T][Hq][d]; k_ctx, v_ctx bf16 bits [C][Hkv][d] (request b's
+    committed context is rows ctx_offset[b] .. ctx_offset[b+1]-1);
+    k_node, v_node bf16 bits [T][Hkv][d] (the draft nodes' own keys/values);
+    node_offset, ctx_offset int32 [B+1]; parent int32 [T]."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    node_offset: np.ndarray
+    parent: np.ndarray
+    ctx_offset: np.ndarray
+    q: np.ndarray
+    k_ctx: np.ndarray
+    v_ctx: np.ndarray
+    k_node: np.ndarray
+    v_node: np.ndarray
+    scale: float
+    kinds: Optional[List[str]] = None
+
+    @property
+    def T(self) -> int:
+        return int(self.node_offset[-1])
+
+    @property
+    def C(self) -> int:
+        return int(self.ctx_offset[-1])
+
+    @property
+    def max_nodes(self) -> int:
+        return int(np.max(np.diff(self.node_offset))) if self.B else 1
+
+    @property
+    def max_ctx(self) -> int:
+        return int(np.max(np.diff(self.ctx_offset))) if self.B else 0
+
+    def f32(self, name: str) -> np.ndarray:
+        return bf16_bits_to_f32(getattr(self, name))
+
+
+def make_attn(parents: List[np.ndarray], ctx_lens: List[int], Hq: int = 32, Hkv: int = 8, d: int = 128,
+              seed: int = 0, name: str = "attn", kinds=None) -> AttnWorkload:
+    """q, k, v ~ N(0, 1) rounded to bf16, context keys/values likewise; scale 1/sqrt(d).
+    Draw order: q, k_node, v_node, k_ctx, v_ctx."""
+    rng = np.random.default_rng(seed)
+    sizes = [len(p) for p in parents]
+    node_offset = np.zeros(len(parents) + 1, dtype=np.int32)
+    node_offset[1:] = np.cumsum(sizes)
+    ctx_offset = np.zeros(len(parents) + 1, dtype=np.int32)
+    ctx_offset[1:] = np.cumsum(ctx_lens)
+    T, C = int(node_offset[-1]), int(ctx_offset[-1])
+    parent = np.concatenate([np.asarray(p, dtype=np.int32) for p in parents]) if T else np.zeros(0, np.int32)
+    bf = lambda shape: f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    q = bf((T, Hq, d))
+    k_node = bf((T, Hkv, d))
+    v_node = bf((T, Hkv, d))
+    k_ctx = bf((C, Hkv, d))
+    v_ctx = bf((C, Hkv, d))
+    return AttnWorkload(name, len(parents), Hq, Hkv, d, node_offset, parent, ctx_offset, q, k_ctx, v_ctx,
+                        k_node, v_node, 1.0 / float(np.sqrt(d)), kinds)
+
+
+def make_attn_small(seed: int = 0) -> AttnWorkload:
+    """Edge mix for parity: empty context, one key, block-boundary lengths, a
+    forest, a 64-node tree, an empty request; 8 query heads over 2 kv heads."""
+    rng = np.random.default_rng(seed + 100)
+    parents = [chain(3), root_branch(), np.array([-1, -1, 0], np.int32), np.array([-1], np.int32),
+               random_tree(rng, 16), random_tree(rng, 64), np.zeros(0, np.int32), chain(5)]
+    ctx = [0, 1, 63, 64, 65, 200, 7, 130]
+    return make_attn(parents, ctx, Hq=8, Hkv=2, seed=seed, name="attn_small")
+
+
+def make_attn_c5(seed: int = 0, ctx_lo: int = 1024, ctx_hi: int = 4096, Hq: int = 32, Hkv: int = 8) -> AttnWorkload:
+    """The mixed batch-256 trees (64 each of chain-3, root-branch-6, random-16,
+    random-64, shuffled) with committed contexts uniform in [ctx_lo, ctx_hi]."""
+    wl = make_c5(seed)
+    parents = [wl.parents_of(b) for b in range(wl.B)]
+    rng = np.random.default_rng(seed + 7)
+    ctx = [int(x) for x in rng.integers(ctx_lo, ctx_hi + 1, size=wl.B)]
+    return make_attn(parents, ctx, Hq=Hq, Hkv=Hkv, seed=seed + 11, name="attn_c5_b256", kinds=wl.kinds)
