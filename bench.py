@@ -226,6 +226,58 @@ def next_rows(args, wl, pools, mn, stream):
                                     "alg_GBps": cb / (t_fused * 1e-6) / 1e9,
                                     "hbm_frac": cb / (t_fused * 1e-6) / 1e9 / HBM_PEAK_GBS}}
 
+def attention_bytes(wl):
+    """Algorithmic HBM bytes of one tree-bias attention launch: every context
+    key/value row once per kv head, the nodes' own keys/values, q, out, lse and
+    the masks."""
+    import numpy as np
+    C = int(wl.ctx_offset[-1])
+    return int(C * wl.Hkv * 2 * D * 2 + wl.T * wl.Hkv * 2 * D * 2 + wl.T * wl.Hq * (D * 2 + D * 4 + 4)
+               + wl.T * 8 + 2 * (wl.B + 1) * 4)
+
+
+def attention_row(args, stream):
+    """Tree-bias attention of the hybrid's attention layers over the batch-256
+    mixed trees with contexts of 1k-4k tokens (32 query / 8 kv heads)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from speculative_decoding_tree_amd import gdn_tree as G
+    t0 = time.time()
+    wl = W.make_attn_c5(0)
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    q, kc, vc, kn, vn = bf(wl.q), bf(wl.k_ctx), bf(wl.v_ctx), bf(wl.k_node), bf(wl.v_node)
+    co, no, par = i32(wl.ctx_offset), i32(wl.node_offset), i32(wl.parent)
+    print(f"[bench] tree attention inputs: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} T={wl.T} context rows={wl.C} "
+          f"in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    mn, mc = wl.max_nodes, wl.max_ctx
+    anc = torch.empty((wl.T,), dtype=torch.int64, device=dev)
+    st = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+    out = torch.empty((wl.T, wl.Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((wl.T, wl.Hq), dtype=torch.float32, device=dev)
+    n = max(10, args.steps // 4)
+    t_anc = _time_launches(lambda i: G.ancestry(no, par, max_nodes=mn, anc_mask=anc, status=st, stream=stream),
+                           n, stream)
+    res = {"workload": "mixed batch-256 trees, contexts U[1024, 4096], Hq=32, Hkv=8, d=128",
+           "context_rows": wl.C, "nodes": wl.T, "ancestry_avg_us": t_anc}
+    nbytes = attention_bytes(wl)
+    for split in (None, 1024):
+        ws_need = G.attention_workspace_bytes(G.make_attn_dims(wl.B, wl.Hq, wl.Hkv, wl.T, wl.C, mn, mc, split))
+        ws = torch.empty((max(ws_need, 16),), dtype=torch.uint8, device=dev)
+
+        def run(i, split=split, ws=ws):
+            G.attention(q, kc, vc, co, kn, vn, no, anc, wl.scale, max_nodes=mn, max_ctx=mc, split=split,
+                        out=out, lse=lse, workspace=ws, status=st, stream=stream)
+        t = _time_launches(run, n, stream)
+        key = "one_pass" if split is None else f"split_{split}"
+        res[key] = {"avg_us": t, "alg_bytes": nbytes, "alg_GBps": nbytes / (t * 1e-6) / 1e9,
+                    "hbm_frac": nbytes / (t * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    assert (st.cpu().numpy() == 0).all()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +289,7 @@ def main():
     ap.add_argument("--no-storeall", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=128, help="requests in the oracle sample")
     ap.add_argument("--no-next", action="store_true", help="skip the next-row measurements")
+    ap.add_argument("--no-attention", action="store_true", help="skip the tree-bias attention measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -411,6 +464,8 @@ def main():
 
     if not args.no_next:
         result["next_rows"] = next_rows(args, wl, pools, mn, stream)
+        if not args.no_attention:
+            result["next_rows"]["tree_attention"] = attention_row(args, stream)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)

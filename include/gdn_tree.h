@@ -85,6 +85,7 @@ extern "C" {
 #define GDN_TREE_E_LAUNCH (-5)    /* the HIP runtime refused the launch */
 #define GDN_TREE_E_SIZE (-6)      /* a buffer would exceed 2^62 bytes */
 #define GDN_TREE_E_ALIGN (-7)     /* a state / q / k / v / out / U / node_state pointer is not 16-byte aligned */
+#define GDN_TREE_E_WORKSPACE (-8) /* attention workspace missing, misaligned or smaller than required */
 
 /* device-side per-request status codes (status[b]) */
 #define GDN_TREE_S_OK 0
@@ -94,6 +95,8 @@ extern "C" {
 #define GDN_TREE_S_BAD_PATH 4     /* path is not a root-first chain of the tree, or path_len out of range */
 #define GDN_TREE_S_BAD_ACCEPT 5   /* accept_node outside [-1, N_b) */
 #define GDN_TREE_S_BAD_SLOT 6     /* state_slot[b] outside [0, n_slots) */
+#define GDN_TREE_S_BAD_CONTEXT 7  /* ctx_offset[b] < 0, decreasing, beyond C, or context longer than max_ctx */
+#define GDN_TREE_S_BAD_MASK 8     /* some anc_mask[t] lacks bit t or has a bit above t */
 
 typedef struct gdn_tree_dims {
     int32_t B;         /* requests in the batch (>= 0) */
@@ -222,6 +225,70 @@ int gdn_tree_accept_commit(const gdn_tree_dims *dims, const float *S0, float *S_
 int gdn_tree_budget_select(const gdn_tree_dims *dims, const int32_t *node_offset, const int32_t *parent,
                            const float *accept_prob, int32_t budget, float threshold, float *survival,
                            uint8_t *keep, int32_t *kept, int32_t *status, void *stream);
+
+/*
+ * gdn_tree_ancestry -- inclusive ancestor bitsets of every draft node.
+ *
+ * anc_mask[t] (uint64 [T]) has bit j set for every request-local node j on
+ * t's root-to-node path, t included (TreeWY, "Method": parent-before-child
+ * order, a node couples only to its ancestors).  One set per forward pass
+ * serves every attention layer (gdn_tree_attention) and equals the masks
+ * gdn_tree_verify writes.  Uses B, T and max_nodes of dims (the other fields
+ * are validated as for every entry point).  Device errors: bad offsets (1)
+ * write nothing; too many nodes or a bad parent (2, 3) write zero masks.
+ */
+int gdn_tree_ancestry(const gdn_tree_dims *dims, const int32_t *node_offset, const int32_t *parent,
+                      uint64_t *anc_mask, int32_t *status, void *stream);
+
+/* Dimensions of the tree-bias attention entry points. */
+typedef struct gdn_tree_attn_dims {
+    int32_t B;         /* requests (>= 0) */
+    int32_t Hq;        /* query heads (>= 1, a multiple of Hkv) */
+    int32_t Hkv;       /* key/value heads (>= 1); query head h reads kv head h / (Hq / Hkv) */
+    int32_t head_dim;  /* must be 128 */
+    int32_t T;         /* total draft nodes = node_offset[B] (>= 0) */
+    int32_t C;         /* total committed-context rows = ctx_offset[B] (>= 0) */
+    int32_t max_nodes; /* per-request node cap (1..64) */
+    int32_t max_ctx;   /* per-request context cap (0 .. 2^30) */
+    int32_t split;     /* context keys per workgroup (>= 1); split >= max_ctx = one pass, no workspace */
+} gdn_tree_attn_dims;
+
+/*
+ * gdn_tree_attention -- ancestry-masked (tree-bias) decode attention for the
+ * attention layers of a hybrid model over a draft forest.
+ *
+ * Row (t, h) of draft node t attends to every key of its request's committed
+ * context and to the draft nodes in anc_mask[t] (its inclusive ancestors):
+ * exactly what sequential decode of t's root-to-node path sees (GDN
+ * Tree-Scan, abstract: attention layers need only an ancestry mask, applied
+ * as tree-bias attention).  With s_j = scale * (q_t,h . key_j):
+ *   out[t][h] = sum_j softmax(s)_j value_j,    lse[t][h] = log sum_j exp(s_j)
+ * Layouts (bfloat16 bit patterns unless stated):
+ *   q              [T][Hq][128]
+ *   k_ctx, v_ctx   [C][Hkv][128]; request b's context is rows ctx_offset[b] ..
+ *                  ctx_offset[b+1]-1 (int32 [B+1], ctx_offset[B] = C)
+ *   k_node, v_node [T][Hkv][128]: the draft nodes' own keys and values
+ *   anc_mask       uint64 [T] as written by gdn_tree_ancestry
+ *   out            float32 [T][Hq][128];  lse float32 [T][Hq] (may be NULL)
+ * When split < max_ctx the context is cut into ceil(max_ctx / split) parts
+ * handled by separate workgroups and merged by a second launch; that needs a
+ * caller-owned device workspace of gdn_tree_attention_workspace_bytes(dims)
+ * bytes (16-byte aligned; contents need no initialisation).  Otherwise
+ * workspace may be NULL.  q, k_ctx, v_ctx, k_node, v_node and out must be
+ * 16-byte aligned.  scale must be finite.
+ * Device errors: bad node offsets (1) write nothing for the request; too
+ * many nodes (2), a bad context range (7) or a malformed mask (8) give NaN
+ * rows in out and lse.
+ */
+int gdn_tree_attention(const gdn_tree_attn_dims *dims, const uint16_t *q, const uint16_t *k_ctx,
+                       const uint16_t *v_ctx, const int32_t *ctx_offset, const uint16_t *k_node,
+                       const uint16_t *v_node, const int32_t *node_offset, const uint64_t *anc_mask,
+                       float scale, float *out, float *lse, void *workspace, size_t workspace_bytes,
+                       int32_t *status, void *stream);
+
+/* Workspace bytes gdn_tree_attention needs for dims (0 when split >= max_ctx
+ * or dims are invalid).  Host only. */
+size_t gdn_tree_attention_workspace_bytes(const gdn_tree_attn_dims *dims);
 
 /*
  * gdn_tree_verify_storeall -- the snapshot-per-node comparison scheme.

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libgdn_tree.so")
-SOURCES = ["api.hip", "verify.hip", "commit.hip", "storeall.hip", "budget.hip"]
+SOURCES = ["api.hip", "verify.hip", "commit.hip", "storeall.hip", "budget.hip", "attention.hip"]
 ARCH = "gfx950"
 
 

@@ -3,6 +3,7 @@
 // the caller's stream.  The library holds no state, allocates nothing and
 // never synchronises.
 #include <limits.h>
+#include <math.h>
 
 #include "common.h"
 #include "launch.h"
@@ -46,6 +47,33 @@ bool any_misaligned(Ps... ps) {
     return (misaligned((const void *)ps) || ...);
 }
 
+// Attention dims; also derives the launch shape.  Returns a GDN_TREE_* code.
+int check_attn_dims(const gdn_tree_attn_dims *d, int &n_split, int &n_rg) {
+    n_split = 1;
+    n_rg = 1;
+    if (!d) return GDN_TREE_E_NULL;
+    if (d->B < 0 || d->T < 0 || d->C < 0) return GDN_TREE_E_DIMS;
+    if (d->B == 0) return GDN_TREE_OK;
+    if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv != 0) return GDN_TREE_E_DIMS;
+    if (d->head_dim != GDN_TREE_HEAD_DIM) return GDN_TREE_E_HEAD_DIM;
+    if (d->max_nodes < 1 || d->max_nodes > GDN_TREE_MAX_NODES) return GDN_TREE_E_MAX_NODES;
+    if (d->max_ctx < 0 || d->max_ctx > (1 << 30) || d->split < 1) return GDN_TREE_E_DIMS;
+    const long long G = d->Hq / d->Hkv;
+    n_rg = (int)((d->max_nodes * G + 63) / 64);
+    n_split = d->max_ctx > d->split ? (int)(((long long)d->max_ctx + d->split - 1) / d->split) : 1;
+    const long long units = (long long)d->B * d->Hkv * n_split * n_rg;
+    if (units > (long long)INT_MAX - 8) return GDN_TREE_E_SIZE;
+    const long long row = (long long)GDN_TREE_HEAD_DIM * 4;
+    if ((long long)d->T * d->Hq > (1ll << 62) / row || (long long)d->C * d->Hkv > (1ll << 62) / row)
+        return GDN_TREE_E_SIZE;
+    return GDN_TREE_OK;
+}
+
+size_t attn_workspace(const gdn_tree_attn_dims *d, int n_split, int n_rg) {
+    if (n_split <= 1) return 0;
+    return (size_t)d->B * d->Hkv * n_split * n_rg * 64u * (GDN_TREE_HEAD_DIM + 2) * sizeof(float);
+}
+
 int finish(hipError_t e) { return e == hipSuccess ? GDN_TREE_OK : GDN_TREE_E_LAUNCH; }
 
 // Clear an error left by earlier, unrelated work so that the check after our
@@ -68,12 +96,15 @@ const char *gdn_tree_strerror(int code) {
         case GDN_TREE_E_LAUNCH: return "kernel launch failed";
         case GDN_TREE_E_SIZE: return "buffer or grid size out of range";
         case GDN_TREE_E_ALIGN: return "state, q, k, v, out, U and node_state pointers must be 16-byte aligned";
+        case GDN_TREE_E_WORKSPACE: return "attention workspace missing, misaligned or too small";
         case GDN_TREE_S_BAD_OFFSETS: return "status: node_offset out of order or beyond T";
         case GDN_TREE_S_TOO_MANY: return "status: request has more than max_nodes nodes";
         case GDN_TREE_S_BAD_PARENT: return "status: parent[t] must satisfy -1 <= parent[t] < t";
         case GDN_TREE_S_BAD_PATH: return "status: path is not a root-first chain of the request's tree";
         case GDN_TREE_S_BAD_ACCEPT: return "status: accept_node outside [-1, N_b)";
         case GDN_TREE_S_BAD_SLOT: return "status: state_slot outside [0, n_slots)";
+        case GDN_TREE_S_BAD_CONTEXT: return "status: ctx_offset out of order, beyond C, or context longer than max_ctx";
+        case GDN_TREE_S_BAD_MASK: return "status: an ancestry mask lacks its own node or has a later one";
         default: return "unknown gdn_tree code";
     }
 }
@@ -250,6 +281,71 @@ int gdn_tree_budget_select(const gdn_tree_dims *dims, const int32_t *node_offset
     a.status = status;
     clear_pending();
     return finish(gdn::launch_budget_select(a, budget, threshold, (hipStream_t)stream));
+}
+
+int gdn_tree_ancestry(const gdn_tree_dims *dims, const int32_t *node_offset, const int32_t *parent,
+                      uint64_t *anc_mask, int32_t *status, void *stream) {
+    int rc = check_dims(dims);
+    if (rc != GDN_TREE_OK || dims->B == 0) return rc;
+    if (!node_offset) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && (!parent || !anc_mask)) return GDN_TREE_E_NULL;
+    Args a = base_args(dims);
+    a.node_offset = node_offset;
+    a.parent = parent;
+    a.anc_mask = anc_mask;
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_ancestry(a, (hipStream_t)stream));
+}
+
+size_t gdn_tree_attention_workspace_bytes(const gdn_tree_attn_dims *dims) {
+    int n_split, n_rg;
+    if (check_attn_dims(dims, n_split, n_rg) != GDN_TREE_OK || dims->B == 0) return 0;
+    return attn_workspace(dims, n_split, n_rg);
+}
+
+int gdn_tree_attention(const gdn_tree_attn_dims *dims, const uint16_t *q, const uint16_t *k_ctx,
+                       const uint16_t *v_ctx, const int32_t *ctx_offset, const uint16_t *k_node,
+                       const uint16_t *v_node, const int32_t *node_offset, const uint64_t *anc_mask,
+                       float scale, float *out, float *lse, void *workspace, size_t workspace_bytes,
+                       int32_t *status, void *stream) {
+    int n_split, n_rg;
+    int rc = check_attn_dims(dims, n_split, n_rg);
+    if (rc != GDN_TREE_OK || dims->B == 0) return rc;
+    if (!isfinite(scale)) return GDN_TREE_E_DIMS;
+    if (!node_offset || !ctx_offset) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && (!q || !k_node || !v_node || !anc_mask || !out)) return GDN_TREE_E_NULL;
+    if (dims->C > 0 && (!k_ctx || !v_ctx)) return GDN_TREE_E_NULL;
+    if (any_misaligned(q, k_ctx, v_ctx, k_node, v_node, out)) return GDN_TREE_E_ALIGN;
+    const size_t need = attn_workspace(dims, n_split, n_rg);
+    if (need > 0 && (!workspace || misaligned(workspace) || workspace_bytes < need)) return GDN_TREE_E_WORKSPACE;
+    gdn::AttnArgs a = {};
+    a.B = dims->B;
+    a.Hq = dims->Hq;
+    a.Hkv = dims->Hkv;
+    a.G = dims->Hq / dims->Hkv;
+    a.T = dims->T;
+    a.C = dims->C;
+    a.max_nodes = dims->max_nodes;
+    a.max_ctx = dims->max_ctx;
+    a.split = dims->split;
+    a.n_split = n_split;
+    a.n_rg = n_rg;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.q = q;
+    a.k_ctx = k_ctx;
+    a.v_ctx = v_ctx;
+    a.k_node = k_node;
+    a.v_node = v_node;
+    a.ctx_offset = ctx_offset;
+    a.node_offset = node_offset;
+    a.anc_mask = anc_mask;
+    a.out = out;
+    a.lse = lse;
+    a.ws = static_cast<float *>(workspace);
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_attention(a, (hipStream_t)stream));
 }
 
 int gdn_tree_verify_storeall(const gdn_tree_dims *dims, const float *S0, const int32_t *state_slot,

@@ -1,0 +1,402 @@
+// gdn_tree_ancestry and gdn_tree_attention: the draft tree's ancestry bitsets
+// and the attention layers' tree-bias decode attention.
+//
+// GDN Tree-Scan (abstract): in one target pass over a draft tree, the
+// attention layers need only an ancestry mask (tree-bias attention); the
+// recurrent layers need the per-path state (the verify kernels).  Row (t, h)
+// attends to the request's committed context and to t's inclusive ancestors
+// among the draft nodes, which is what sequential decode along t's
+// root-to-node path attends to.
+//
+// gfx950 layout.  A workgroup (4 wave64) owns 64 query rows of one
+// (request, kv-head): row r = (node r / G, query head hk G + r % G), so the
+// G query heads of a node sit in neighbouring rows and every row of the
+// workgroup shares the same keys.  Wave w owns rows 16w .. 16w+15.  Keys go
+// through LDS 64 at a time: K rows as they are, V transposed ([d][key]) so
+// that a lane can hold eight keys of one column.  Per block and wave:
+//   S^T = K Q^T          (v_mfma_f32_16x16x32_bf16; A = K rows from LDS,
+//                         B = the wave's Q rows, loaded once into registers)
+// leaves lane (n, grp) with keys 16kt + 4grp + i of query row n, so the
+// online-softmax statistics of row n live in lane n (reduced over the four
+// lane groups with two xor shuffles), and the probabilities are already laid
+// out as the B operand of
+//   O^T += V^T P^T       (A = V^T from LDS; k-slot 8grp + e holds key
+//                         32ks + 16(e/4) + 4grp + e%4, the same key in both)
+// with P split into bf16 hi + lo (two MFMAs, ~16 mantissa bits), so no
+// register moves between lanes.  Global loads of the next block are issued
+// before the current block is computed.
+//
+// When a request's context is split over several workgroups, each writes an
+// unnormalised partial (O, running max, sum) to the workspace and a second
+// kernel merges them.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+#include "mfma.h"
+
+namespace gdn {
+namespace {
+
+// ---- ancestry ------------------------------------------------------------
+
+// One wave per request, lane t = node t.  Pointer doubling: m is the set of
+// nodes from t up to (excluding) jp; each round joins the segment above.
+__global__ __launch_bounds__(256) void ancestry_kernel(Args a) {
+    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (b >= a.B) return;
+    int lo, N;
+    int st = check_offsets(a, b, lo, N);
+    if (st == GDN_TREE_S_BAD_OFFSETS) {
+        if (lane == 0 && a.status) a.status[b] = st;
+        return;
+    }
+    const bool live = st == GDN_TREE_S_OK && lane < N;
+    int jp = live ? a.parent[lo + lane] : -1;
+    if (st == GDN_TREE_S_OK && __ballot(live && (jp < -1 || jp >= lane))) st = GDN_TREE_S_BAD_PARENT;
+    uint64_t m = 0ull;
+    if (st == GDN_TREE_S_OK) {
+        m = live ? (1ull << lane) : 0ull;
+        while (__ballot(jp >= 0)) {
+            const int src = jp >= 0 ? jp : lane;
+            const uint64_t m_up = __shfl(m, src);
+            const int jp_up = __shfl(jp, src);
+            if (jp >= 0) {
+                m |= m_up;
+                jp = jp_up;
+            }
+        }
+    }
+    for (int t = lane; t < N; t += 64) a.anc_mask[lo + t] = st == GDN_TREE_S_OK ? m : 0ull;
+    if (lane == 0 && a.status) a.status[b] = st;
+}
+
+// ---- attention -------------------------------------------------------------
+
+constexpr int AT = 256;              // threads per workgroup
+constexpr int KB = 64;               // keys per staged block
+constexpr int KS = D + 8;            // K block row stride (bf16 elements; 272 bytes)
+constexpr int VS = KB + 8;           // transposed V row stride (bf16 elements; 144 bytes)
+constexpr int ROWS = 64;             // query rows per workgroup
+constexpr int PART = ROWS * (D + 2); // floats per partial record: O rows, then max, then sum
+constexpr float LN2 = 0.6931471805599453f;
+
+// Request checks shared by both kernels: offsets, node count, context range.
+__device__ __forceinline__ int attn_request(const AttnArgs &a, int b, int &lo, int &N, int &c0, int &Lc) {
+    lo = a.node_offset[b];
+    const int hi = a.node_offset[b + 1];
+    N = hi - lo;
+    c0 = 0;
+    Lc = 0;
+    if (lo < 0 || hi < lo || hi > a.T) return GDN_TREE_S_BAD_OFFSETS;
+    if (N > a.max_nodes) return GDN_TREE_S_TOO_MANY;
+    c0 = a.ctx_offset[b];
+    const int c1 = a.ctx_offset[b + 1];
+    Lc = c1 - c0;
+    if (c0 < 0 || c1 < c0 || c1 > a.C || Lc > a.max_ctx) return GDN_TREE_S_BAD_CONTEXT;
+    return GDN_TREE_S_OK;
+}
+
+// A node's mask must hold the node itself and nothing after it.  Uniform per
+// workgroup (every thread calls the barrier).
+__device__ __forceinline__ int check_masks(const AttnArgs &a, int st, int lo, int N) {
+    if (st != GDN_TREE_S_OK || N == 0) return st;
+    const int t = threadIdx.x;
+    const bool bad = t < N && (a.anc_mask[lo + t] >> t) != 1ull;
+    return __syncthreads_or(bad) ? GDN_TREE_S_BAD_MASK : st;
+}
+
+// NaN out / lse rows [r_begin, r_end) of (request at lo, kv-head hk), all threads.
+__device__ void nan_rows(const AttnArgs &a, int lo, int hk, int r_begin, int r_end) {
+    const float qnan = __int_as_float(0x7fc00000);
+    const int G = a.G;
+    for (int idx = threadIdx.x; idx < (r_end - r_begin) * D; idx += AT) {
+        const int r = r_begin + idx / D, t = r / G, g = r - t * G;
+        a.out[((size_t)(lo + t) * a.Hq + hk * G + g) * D + (idx & (D - 1))] = qnan;
+    }
+    if (a.lse)
+        for (int i = threadIdx.x; i < r_end - r_begin; i += AT) {
+            const int r = r_begin + i, t = r / G, g = r - t * G;
+            a.lse[(size_t)(lo + t) * a.Hq + hk * G + g] = qnan;
+        }
+}
+
+// Rows a workgroup of row group rg answers for when the request is invalid:
+// its 64 rows, and for the last group every row beyond (a request with more
+// nodes than max_nodes has rows no group was sized for).
+__device__ __forceinline__ int nan_end(const AttnArgs &a, int rg, int R) {
+    return rg == a.n_rg - 1 ? R : min(R, ROWS * (rg + 1));
+}
+
+__global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void attn_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+
+    const int n_units = a.B * a.Hkv * a.n_split * a.n_rg;
+    const int unit = xcd_unit(blockIdx.x, n_units);
+    if (unit >= n_units) return;
+    const int rg = unit % a.n_rg;   // row groups of one (request, kv-head, split) are neighbours
+    int rest = unit / a.n_rg;
+    const int sp = rest % a.n_split;
+    rest /= a.n_split;
+    const int hk = rest % a.Hkv;
+    const int b = rest / a.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, grp = lane >> 4;
+
+    int lo, N, c0, Lc;
+    int st = attn_request(a, b, lo, N, c0, Lc);
+    st = check_masks(a, st, lo, N);
+    if (hk == 0 && sp == 0 && rg == 0 && tid == 0 && a.status) a.status[b] = st;
+    if (st == GDN_TREE_S_BAD_OFFSETS) return;
+    const int G = a.G;
+    const int R = N * G;
+    const int row0 = ROWS * rg;
+    if (row0 >= R) return;
+    if (st != GDN_TREE_S_OK) {   // NaN rows (the merge kernel writes them when the context is split)
+        if (a.n_split == 1) nan_rows(a, lo, hk, row0, nan_end(a, rg, R));
+        return;
+    }
+    const int k0 = sp * a.split;
+    if (sp > 0 && k0 >= Lc) return;   // nothing of this request's context falls in this part
+    const int k1 = min(Lc, k0 + a.split);
+    const int nctx = k1 > k0 ? (k1 - k0 + KB - 1) / KB : 0;
+    const int nblk = nctx + (sp == 0 ? 1 : 0);   // the draft nodes' own block goes with the first part
+
+    // ---- this lane's query row (MFMA B column n) ----
+    const int r = row0 + 16 * w + n;
+    const bool rvalid = r < R;
+    const bool active = row0 + 16 * w < R;
+    int t = 0, g = 0;
+    if (rvalid) {
+        t = r / G;
+        g = r - t * G;
+    }
+    const uint64_t anc_row = rvalid ? a.anc_mask[lo + t] : 0ull;
+    u32x4 qf[4];
+    if (rvalid) {
+        const uint16_t *qp = a.q + ((size_t)(lo + t) * a.Hq + hk * G + g) * D + 8 * grp;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const u32x4 *>(qp + 32 * s);
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // ---- staging: thread (kk, kpart) moves K row kk, columns 32 kpart .. +31;
+    //      thread (kp, vpart) moves V rows 2kp, 2kp+1, columns 16 vpart .. +15 ----
+    const int kk = tid >> 2, kpart = tid & 3;
+    const int kp = tid >> 3, vpart = tid & 7;
+    const size_t kvrow = (size_t)a.Hkv * D;
+    const uint16_t *kctx = a.k_ctx + ((size_t)c0 * a.Hkv + hk) * D;
+    const uint16_t *vctx = a.v_ctx + ((size_t)c0 * a.Hkv + hk) * D;
+    const uint16_t *knode = a.k_node + ((size_t)lo * a.Hkv + hk) * D;
+    const uint16_t *vnode = a.v_node + ((size_t)lo * a.Hkv + hk) * D;
+    u32x4 kst[4], vst[4];
+    auto load_block = [&](int blk) {
+        const bool nodeb = blk >= nctx;
+        // key rows past the end read the last real row; their scores are masked
+        const int last = nodeb ? N - 1 : k1 - 1;
+        const int first = nodeb ? 0 : k0 + KB * blk;
+        const uint16_t *kb = nodeb ? knode : kctx;
+        const uint16_t *vb = nodeb ? vnode : vctx;
+        const uint16_t *ks = kb + (size_t)min(first + kk, last) * kvrow + 32 * kpart;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kst[c] = *reinterpret_cast<const u32x4 *>(ks + 8 * c);
+        const uint16_t *v0 = vb + (size_t)min(first + 2 * kp, last) * kvrow + 16 * vpart;
+        const uint16_t *v1 = vb + (size_t)min(first + 2 * kp + 1, last) * kvrow + 16 * vpart;
+        vst[0] = *reinterpret_cast<const u32x4 *>(v0);
+        vst[1] = *reinterpret_cast<const u32x4 *>(v0 + 8);
+        vst[2] = *reinterpret_cast<const u32x4 *>(v1);
+        vst[3] = *reinterpret_cast<const u32x4 *>(v1 + 8);
+    };
+    auto store_block = [&]() {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4 *>(&Ks[kk * KS + 32 * kpart + 8 * c]) = kst[c];
+        // column d = 16 vpart + e of keys 2kp (low half) and 2kp + 1 (high half)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t w0 = vst[e >> 3][(e & 7) >> 1];
+            const uint32_t w1 = vst[2 + (e >> 3)][(e & 7) >> 1];
+            const uint32_t pair = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
+            *reinterpret_cast<uint32_t *>(&Vt[(16 * vpart + e) * VS + 2 * kp]) = pair;
+        }
+    };
+
+    float m = -INFINITY, l = 0.f;   // running max (log2 units) and sum of row n
+    f32x4 ot[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    load_block(0);
+    for (int blk = 0; blk < nblk; ++blk) {
+        if (blk > 0) lds_barrier();   // every wave is done with the previous block
+        store_block();
+        lds_barrier();
+        if (blk + 1 < nblk) load_block(blk + 1);
+        if (!active) continue;
+        const bool nodeb = blk >= nctx;
+        const int kfirst = k0 + KB * blk;
+
+        // scores S^T for keys 16 kt + 4 grp + i of row n
+        f32x4 sc[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const u32x4 kf = *reinterpret_cast<const u32x4 *>(&Ks[(16 * kt + n) * KS + 32 * s + 8 * grp]);
+                sc[kt] = mfma(kf, qf[s], sc[kt]);
+            }
+        }
+        float x[4][4];
+        float mb = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = 16 * kt + 4 * grp + i;
+                const bool ok = nodeb ? ((anc_row >> key) & 1ull) != 0ull : kfirst + key < k1;
+                x[kt][i] = ok ? sc[kt][i] * a.scale_log2 : -INFINITY;
+                mb = fmaxf(mb, x[kt][i]);
+            }
+        mb = fmaxf(mb, __shfl_xor(mb, 16));
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        const float mnew = fmaxf(m, mb);
+        const float mref = mnew == -INFINITY ? 0.f : mnew;   // a row with nothing visible yet keeps p = 0
+        const float alpha = __builtin_amdgcn_exp2f(m - mref);
+        float rs = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[kt][i] = __builtin_amdgcn_exp2f(x[kt][i] - mref);
+                rs += x[kt][i];
+            }
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);
+        l = l * alpha + rs;
+        m = mnew;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ot[mt][i] *= alpha;
+
+        // O^T += V^T P^T over the block's two 32-key steps
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+            split_bf16x2(x[2 * ks][0], x[2 * ks][1], h0, l0);
+            split_bf16x2(x[2 * ks][2], x[2 * ks][3], h1, l1);
+            split_bf16x2(x[2 * ks + 1][0], x[2 * ks + 1][1], h2, l2);
+            split_bf16x2(x[2 * ks + 1][2], x[2 * ks + 1][3], h3, l3);
+            const u32x4 phi = {h0, h1, h2, h3}, plo = {l0, l1, l2, l3};
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                const uint16_t *vp = &Vt[(16 * mt + n) * VS + 32 * ks + 4 * grp];
+                const u32x2 va = *reinterpret_cast<const u32x2 *>(vp);
+                const u32x2 vb = *reinterpret_cast<const u32x2 *>(vp + 16);
+                const u32x4 vf = {va.x, va.y, vb.x, vb.y};
+                ot[mt] = mfma(vf, phi, ot[mt]);
+                ot[mt] = mfma(vf, plo, ot[mt]);
+            }
+        }
+    }
+    if (!rvalid) return;
+
+    // lane (n, grp) holds columns 16 mt + 4 grp .. +3 of row n
+    if (a.n_split == 1) {
+        const size_t orow = (size_t)(lo + t) * a.Hq + hk * G + g;
+        const float inv = 1.f / l;
+        float *op = a.out + orow * D + 4 * grp;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            *reinterpret_cast<float4 *>(op + 16 * mt) =
+                make_float4(ot[mt][0] * inv, ot[mt][1] * inv, ot[mt][2] * inv, ot[mt][3] * inv);
+        if (grp == 0 && a.lse) a.lse[orow] = (m + log2f(l)) * LN2;
+    } else {
+        float *rec = a.ws + ((((size_t)b * a.Hkv + hk) * a.n_split + sp) * a.n_rg + rg) * PART;
+        const int rl = 16 * w + n;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            *reinterpret_cast<float4 *>(rec + rl * D + 16 * mt + 4 * grp) =
+                make_float4(ot[mt][0], ot[mt][1], ot[mt][2], ot[mt][3]);
+        if (grp == 0) {
+            rec[ROWS * D + rl] = m;
+            rec[ROWS * D + ROWS + rl] = l;
+        }
+    }
+}
+
+// Merge the context parts of each row: thread (row, part) owns 32 columns.
+__global__ __launch_bounds__(AT) void attn_merge_kernel(AttnArgs a) {
+    const int unit = blockIdx.x;
+    const int rg = unit % a.n_rg;
+    const int rest = unit / a.n_rg;
+    const int hk = rest % a.Hkv;
+    const int b = rest / a.Hkv;
+    const int tid = threadIdx.x;
+    int lo, N, c0, Lc;
+    int st = attn_request(a, b, lo, N, c0, Lc);
+    st = check_masks(a, st, lo, N);
+    if (st == GDN_TREE_S_BAD_OFFSETS) return;
+    const int G = a.G;
+    const int R = N * G;
+    if (ROWS * rg >= R) return;
+    if (st != GDN_TREE_S_OK) {
+        nan_rows(a, lo, hk, ROWS * rg, nan_end(a, rg, R));
+        return;
+    }
+    const int rl = tid >> 2, part = tid & 3;
+    const int r = ROWS * rg + rl;
+    if (r >= R) return;
+    const int t = r / G, g = r - t * G;
+    const size_t orow = (size_t)(lo + t) * a.Hq + hk * G + g;
+    float *op = a.out + orow * D + 32 * part;
+    const int nparts = Lc > 0 ? (Lc + a.split - 1) / a.split : 1;
+    const size_t stride = (size_t)a.n_rg * PART;   // between consecutive parts
+    const float *rec = a.ws + (((size_t)b * a.Hkv + hk) * a.n_split * a.n_rg + rg) * PART;
+    float M = -INFINITY;
+    for (int s = 0; s < nparts; ++s) M = fmaxf(M, rec[s * stride + ROWS * D + rl]);
+    float L = 0.f;
+    float4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < nparts; ++s) {
+        const float *rs = rec + s * stride;
+        const float wgt = __builtin_amdgcn_exp2f(rs[ROWS * D + rl] - M);
+        L += wgt * rs[ROWS * D + ROWS + rl];
+        const float4 *src = reinterpret_cast<const float4 *>(rs + rl * D + 32 * part);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 v = src[i];
+            acc[i].x += wgt * v.x;
+            acc[i].y += wgt * v.y;
+            acc[i].z += wgt * v.z;
+            acc[i].w += wgt * v.w;
+        }
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<float4 *>(op + 4 * i) = make_float4(acc[i].x * inv, acc[i].y * inv, acc[i].z * inv, acc[i].w * inv);
+    if (part == 0 && a.lse) a.lse[orow] = (M + log2f(L)) * LN2;
+}
+
+}  // namespace
+
+hipError_t launch_ancestry(const Args &a, hipStream_t stream) {
+    ancestry_kernel<<<dim3((a.B + 3) / 4), dim3(256), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
+    const int units = a.B * a.Hkv * a.n_split * a.n_rg;
+    attn_kernel<<<dim3(xcd_grid(units)), dim3(AT), 0, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.n_split == 1) return e;
+    attn_merge_kernel<<<dim3(a.B * a.Hkv * a.n_rg), dim3(AT), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

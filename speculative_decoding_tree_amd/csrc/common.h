@@ -35,6 +35,17 @@ struct Args {
     int32_t *kept;          // [B]
 };
 
+// Argument block of the tree-bias attention kernels.
+struct AttnArgs {
+    int B, Hq, Hkv, G, T, C, max_nodes, max_ctx, split, n_split, n_rg;
+    float scale_log2;                       // softmax scale times log2(e)
+    const uint16_t *q, *k_ctx, *v_ctx, *k_node, *v_node;
+    const int32_t *ctx_offset, *node_offset;
+    const uint64_t *anc_mask;
+    float *out, *lse, *ws;
+    int32_t *status;
+};
+
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 

@@ -15,6 +15,8 @@ hipError_t launch_accept_greedy(const Args &a, hipStream_t stream);
 hipError_t launch_accept_commit(const Args &a, hipStream_t stream);
 hipError_t launch_commit_replay(const Args &a, hipStream_t stream);
 hipError_t launch_budget_select(const Args &a, int budget, float threshold, hipStream_t stream);
+hipError_t launch_ancestry(const Args &a, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_verify_storeall(const Args &a, hipStream_t stream);
 hipError_t launch_commit_storeall(const Args &a, hipStream_t stream);
 

@@ -35,45 +35,12 @@
 // complete in order, so one level's writes are seen by the next level).
 #include "common.h"
 #include "launch.h"
+#include "mfma.h"
 
 namespace gdn {
 namespace {
 
 constexpr int NT = 256;
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Workgroup barrier that orders LDS only: outstanding global loads are not
-// waited for (HIP's __syncthreads fences global memory as well).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Two floats to a packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    bf16x2_t r;
-    r.x = (__bf16)a;
-    r.y = (__bf16)b;
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-// x = hi + lo + O(2^-16 |x|): hi = bf16(x), lo = bf16(x - hi) (x - hi is exact).
-__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t &hi, uint32_t &lo) {
-    hi = pack_bf16x2(a, b);
-    const float ha = __uint_as_float(hi << 16);
-    const float hb = __uint_as_float(hi & 0xffff0000u);
-    lo = pack_bf16x2(a - ha, b - hb);
-}
-
-__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
 
 // Coefficient table T:
 //   T[t][q], q < dep(t) - 1 : A = beta_t D_tj (k_t.k_j) for the ancestor j of t at

@@ -14,6 +14,10 @@ Tensor formats (row-major, on one GPU):
   out, U      float32 [T, Hv, 128];  anc_mask int64 [T] (uint64 bit patterns)
   path        int32 [B, max_nodes];  path_len, accept_node, status int32 [B]
   node_state  float32 [T, Hv, 128, 128]
+Tree-bias attention:
+  q           bfloat16 [T, Hq, 128];  k_ctx, v_ctx bfloat16 [C, Hkv, 128]
+  k_node, v_node bfloat16 [T, Hkv, 128];  ctx_offset int32 [B+1]
+  out         float32 [T, Hq, 128];  lse float32 [T, Hq]
 """
 from __future__ import annotations
 
@@ -32,7 +36,8 @@ HEAD_DIM = 128
 MAX_NODES = 64
 
 # status codes (include/gdn_tree.h)
-S_OK, S_BAD_OFFSETS, S_TOO_MANY, S_BAD_PARENT, S_BAD_PATH, S_BAD_ACCEPT, S_BAD_SLOT = range(7)
+(S_OK, S_BAD_OFFSETS, S_TOO_MANY, S_BAD_PARENT, S_BAD_PATH, S_BAD_ACCEPT, S_BAD_SLOT, S_BAD_CONTEXT,
+ S_BAD_MASK) = range(9)
 
 
 class GdnTreeError(RuntimeError):
@@ -45,6 +50,11 @@ class GdnTreeError(RuntimeError):
 
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("B", "Hv", "Hk", "d_k", "d_v", "T", "max_nodes", "n_slots")]
+
+
+class AttnDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "Hq", "Hkv", "head_dim", "T", "C", "max_nodes", "max_ctx",
+                                               "split")]
 
 
 _P = ctypes.c_void_p
@@ -60,6 +70,9 @@ _SIGS = {
     "gdn_tree_commit_replay": [ctypes.POINTER(Dims)] + [_P] * 13,
     "gdn_tree_budget_select": [ctypes.POINTER(Dims), _P, _P, _P, ctypes.c_int32, ctypes.c_float,
                                _P, _P, _P, _P, _P],
+    "gdn_tree_ancestry": [ctypes.POINTER(Dims)] + [_P] * 5,
+    "gdn_tree_attention": [ctypes.POINTER(AttnDims)] + [_P] * 8 + [ctypes.c_float, _P, _P, _P, ctypes.c_size_t,
+                                                                   _P, _P],
 }
 
 _lib = None
@@ -79,6 +92,8 @@ def lib() -> ctypes.CDLL:
             fn.restype = _I
         L.gdn_tree_state_bytes.argtypes = [ctypes.POINTER(Dims), _I]
         L.gdn_tree_state_bytes.restype = ctypes.c_size_t
+        L.gdn_tree_attention_workspace_bytes.argtypes = [ctypes.POINTER(AttnDims)]
+        L.gdn_tree_attention_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_tree_strerror.argtypes = [_I]
         L.gdn_tree_strerror.restype = ctypes.c_char_p
         L.gdn_tree_abi_version.argtypes = []
@@ -374,3 +389,60 @@ def budget_select(node_offset, parent, accept_prob, budget: int, threshold: floa
         _ptr(kept, "kept", _I32, (B,)), _ptr(status, "status", _I32, (B,)), _stream(stream))
     _check("gdn_tree_budget_select", rc)
     return survival, keep, kept, status
+
+
+def ancestry(node_offset, parent, max_nodes: int, anc_mask=None, status=None, stream=None):
+    """gdn_tree_ancestry.  Returns (anc_mask int64 [T], status)."""
+    B = int(node_offset.numel()) - 1
+    T = int(parent.numel())
+    dev = node_offset.device
+    anc_mask = anc_mask if anc_mask is not None else torch.empty((T,), dtype=torch.int64, device=dev)
+    status = status if status is not None else torch.empty((B,), dtype=torch.int32, device=dev)
+    dims = make_dims(B, 1, 1, T, max_nodes, 1)
+    rc = lib().gdn_tree_ancestry(
+        ctypes.byref(dims),
+        _ptr(node_offset, "node_offset", _I32, (B + 1,)), _ptr(parent, "parent", _I32, (T,)),
+        _ptr(anc_mask, "anc_mask", _U64, (T,)), _ptr(status, "status", _I32, (B,)), _stream(stream))
+    _check("gdn_tree_ancestry", rc)
+    return anc_mask, status
+
+
+def make_attn_dims(B, Hq, Hkv, T, C, max_nodes, max_ctx, split=None, head_dim=HEAD_DIM) -> AttnDims:
+    split = max(1, int(max_ctx)) if split is None else int(split)
+    return AttnDims(int(B), int(Hq), int(Hkv), int(head_dim), int(T), int(C), int(max_nodes), int(max_ctx), split)
+
+
+def attention_workspace_bytes(dims: AttnDims) -> int:
+    return int(lib().gdn_tree_attention_workspace_bytes(ctypes.byref(dims)))
+
+
+def attention(q, k_ctx, v_ctx, ctx_offset, k_node, v_node, node_offset, anc_mask, scale: float,
+              max_nodes: int, max_ctx: int, split: Optional[int] = None, out=None, lse=None, workspace=None,
+              status=None, stream=None):
+    """gdn_tree_attention.  Returns (out, lse, status).  A workspace is allocated
+    when the context is split (split < max_ctx) and none is given."""
+    B = int(node_offset.numel()) - 1
+    T, Hq = int(q.shape[0]), int(q.shape[1])
+    C, Hkv = int(k_ctx.shape[0]), int(k_ctx.shape[1])
+    dev = q.device
+    dims = make_attn_dims(B, Hq, Hkv, T, C, max_nodes, max_ctx, split)
+    out = out if out is not None else torch.empty((T, Hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    lse = lse if lse is not None else torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    status = status if status is not None else torch.empty((B,), dtype=torch.int32, device=dev)
+    need = attention_workspace_bytes(dims)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = int(workspace.numel() * workspace.element_size()) if workspace is not None else 0
+    rc = lib().gdn_tree_attention(
+        ctypes.byref(dims),
+        _ptr(q, "q", _B16, (T, Hq, HEAD_DIM)),
+        _ptr(k_ctx, "k_ctx", _B16, (C, Hkv, HEAD_DIM)), _ptr(v_ctx, "v_ctx", _B16, (C, Hkv, HEAD_DIM)),
+        _ptr(ctx_offset, "ctx_offset", _I32, (B + 1,)),
+        _ptr(k_node, "k_node", _B16, (T, Hkv, HEAD_DIM)), _ptr(v_node, "v_node", _B16, (T, Hkv, HEAD_DIM)),
+        _ptr(node_offset, "node_offset", _I32, (B + 1,)), _ptr(anc_mask, "anc_mask", _U64, (T,)),
+        ctypes.c_float(scale),
+        _ptr(out, "out", _F32, (T, Hq, HEAD_DIM)), _ptr(lse, "lse", _F32, (T, Hq)),
+        ws_ptr, ctypes.c_size_t(ws_bytes), _ptr(status, "status", _I32, (B,)), _stream(stream))
+    _check("gdn_tree_attention", rc)
+    return out, lse, status

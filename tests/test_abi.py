@@ -14,7 +14,8 @@ def test_library_exports_every_declared_symbol():
     names = G.declared_symbols()
     assert {"gdn_tree_verify", "gdn_tree_commit", "gdn_tree_accepted_path", "gdn_tree_verify_storeall",
             "gdn_tree_commit_storeall", "gdn_tree_state_bytes", "gdn_tree_strerror",
-            "gdn_tree_abi_version", "gdn_tree_accept_greedy", "gdn_tree_accept_commit", "gdn_tree_commit_replay", "gdn_tree_budget_select"} <= set(names)
+            "gdn_tree_abi_version", "gdn_tree_accept_greedy", "gdn_tree_accept_commit", "gdn_tree_commit_replay", "gdn_tree_budget_select",
+            "gdn_tree_ancestry", "gdn_tree_attention", "gdn_tree_attention_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert G.abi_version() == 1
@@ -24,7 +25,8 @@ def test_header_constants_match_binding():
     text = open(G.HEADER).read()
     for name, val in [("GDN_TREE_S_BAD_OFFSETS", G.S_BAD_OFFSETS), ("GDN_TREE_S_TOO_MANY", G.S_TOO_MANY),
                       ("GDN_TREE_S_BAD_PARENT", G.S_BAD_PARENT), ("GDN_TREE_S_BAD_PATH", G.S_BAD_PATH),
-                      ("GDN_TREE_S_BAD_ACCEPT", G.S_BAD_ACCEPT), ("GDN_TREE_S_BAD_SLOT", G.S_BAD_SLOT)]:
+                      ("GDN_TREE_S_BAD_ACCEPT", G.S_BAD_ACCEPT), ("GDN_TREE_S_BAD_SLOT", G.S_BAD_SLOT),
+                      ("GDN_TREE_S_BAD_CONTEXT", G.S_BAD_CONTEXT), ("GDN_TREE_S_BAD_MASK", G.S_BAD_MASK)]:
         assert f"#define {name} {val}" in text
 
 
@@ -34,8 +36,13 @@ def test_status_codes_agree_with_oracle_numbers():
             O.STATUS_BAD_ACCEPT, O.STATUS_BAD_SLOT) == (1, 2, 3, 4, 5, 6)
 
 
+def test_attention_status_codes_agree_with_oracle_numbers():
+    from oracle import tree_attention as A
+    assert (A.STATUS_BAD_CONTEXT, A.STATUS_BAD_MASK) == (G.S_BAD_CONTEXT, G.S_BAD_MASK) == (7, 8)
+
+
 def test_strerror_never_null():
-    for c in range(-8, 9):
+    for c in range(-9, 10):
         assert isinstance(G.strerror(c), str) and G.strerror(c)
 
 
@@ -109,3 +116,47 @@ def test_misaligned_pointer_rejected():
     args = [odd, None, ok, ok, ok, ok, ok, ok, ok, ok, ok, None, None, None]
     assert L.gdn_tree_verify(ctypes.byref(d), *args) == -7
     assert "16-byte" in G.strerror(-7)
+
+
+ATTN_NULLS = [None] * 8 + [ctypes.c_float(0.1), None, None, None, ctypes.c_size_t(0), None, None]
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("Hq", 0, -2), ("Hkv", 3, -2), ("T", -1, -2), ("C", -1, -2), ("B", -1, -2), ("split", 0, -2),
+    ("max_ctx", -1, -2), ("max_ctx", (1 << 30) + 1, -2), ("head_dim", 64, -3), ("max_nodes", 0, -4),
+    ("max_nodes", 65, -4),
+])
+def test_attention_host_validation_rejects_dims(field, value, code):
+    L = G.lib()
+    d = G.make_attn_dims(4, 32, 8, 20, 100, 8, 50)
+    setattr(d, field, value)
+    assert L.gdn_tree_attention(ctypes.byref(d), *ATTN_NULLS) == code
+    assert G.attention_workspace_bytes(d) == 0
+
+
+def test_attention_host_validation_pointers_scale_workspace():
+    L = G.lib()
+    d = G.make_attn_dims(4, 32, 8, 20, 100, 8, 50)
+    assert L.gdn_tree_attention(None, *ATTN_NULLS) == -1
+    assert L.gdn_tree_attention(ctypes.byref(d), *ATTN_NULLS) == -1
+    ok = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10008)
+    good = [ok, ok, ok, ok, ok, ok, ok, ok]
+    tail = [ok, ok, None, ctypes.c_size_t(0), None, None]
+    assert L.gdn_tree_attention(ctypes.byref(d), *good, ctypes.c_float(float("inf")), *tail) == -2
+    bad_align = [ok, odd, ok, ok, ok, ok, ok, ok]
+    assert L.gdn_tree_attention(ctypes.byref(d), *bad_align, ctypes.c_float(0.1), *tail) == -7
+    split = G.make_attn_dims(4, 32, 8, 20, 100, 8, 50, split=16)      # 4 context parts -> workspace needed
+    need = G.attention_workspace_bytes(split)
+    assert need == 4 * 8 * 4 * 1 * 64 * 130 * 4      # B, Hkv, 4 parts, 1 row group (8 nodes x 4 heads), rows, D+2 floats
+    assert L.gdn_tree_attention(ctypes.byref(split), *good, ctypes.c_float(0.1), *tail) == -8
+    small = [ok, ok, ok, ctypes.c_size_t(need - 4), None, None]
+    assert L.gdn_tree_attention(ctypes.byref(split), *good, ctypes.c_float(0.1), *small) == -8
+    assert L.gdn_tree_ancestry(None, None, None, None, None, None) == -1
+
+
+def test_attention_empty_batch_is_a_no_op():
+    L = G.lib()
+    d = G.make_attn_dims(0, 32, 8, 0, 0, 8, 0)
+    assert L.gdn_tree_attention(ctypes.byref(d), *ATTN_NULLS) == 0
+    assert G.attention_workspace_bytes(G.make_attn_dims(4, 32, 8, 20, 100, 8, 50)) == 0   # one pass

@@ -1,0 +1,229 @@
+"""GPU parity of the tree-bias attention path through the C ABI against the fp64 oracle.
+
+Bar: ancestry masks and statuses bit-exact; out row-normwise relative error
+<= ATTN_TOL and |lse - lse_ref| <= ATTN_TOL.  The tolerance follows from the
+arithmetic: q.k products of bf16 inputs are exact in fp32, softmax weights
+enter the value product as bf16 hi + lo (relative error ~2^-17 = 7.6e-6 per
+weight, random in sign), and what remains is fp32 accumulation over at most
+max_ctx + 64 keys (~sqrt(4k) * 2^-24 = 4e-6 relative to sum |p v|).  1e-4
+leaves a margin of ~20x over the errors these inputs show (~5e-6).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import gdn_oracle as O
+from oracle import tree_attention as A
+from helpers import anc_u64, host, rowwise_rel_err
+
+import speculative_decoding_tree_amd.gdn_tree as G
+
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = 1e-4
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X visible to torch"
+    return torch.device("cuda:0")
+
+
+def upload_attn(wl):
+    d = _dev()
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(d).view(torch.bfloat16)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(d)
+    return dict(q=bf(wl.q), k_ctx=bf(wl.k_ctx), v_ctx=bf(wl.v_ctx), k_node=bf(wl.k_node), v_node=bf(wl.v_node),
+                ctx_offset=i32(wl.ctx_offset), node_offset=i32(wl.node_offset), parent=i32(wl.parent))
+
+
+def run_attn(wl, split=None, max_nodes=None, max_ctx=None, anc=None):
+    d = upload_attn(wl)
+    mn = max_nodes or max(1, wl.max_nodes)
+    mc = wl.max_ctx if max_ctx is None else max_ctx
+    if anc is None:
+        anc, ast = G.ancestry(d["node_offset"], d["parent"], max_nodes=mn)
+    out, lse, st = G.attention(d["q"], d["k_ctx"], d["v_ctx"], d["ctx_offset"], d["k_node"], d["v_node"],
+                               d["node_offset"], anc, wl.scale, max_nodes=mn, max_ctx=mc, split=split)
+    torch.cuda.synchronize()
+    return host(out), host(lse), host(st), d
+
+
+def oracle_attn_sampled(wl, reqs):
+    """Oracle rows of the sampled requests only, converting just their slices."""
+    f = lambda x: W.bf16_bits_to_f32(x).astype(np.float64)
+    out = np.full((wl.T, wl.Hq, 128), np.nan)
+    lse = np.full((wl.T, wl.Hq), np.nan)
+    for b in reqs:
+        lo, hi = int(wl.node_offset[b]), int(wl.node_offset[b + 1])
+        c0, c1 = int(wl.ctx_offset[b]), int(wl.ctx_offset[b + 1])
+        out[lo:hi], lse[lo:hi] = A.tree_attention_request(f(wl.q[lo:hi]), f(wl.k_ctx[c0:c1]), f(wl.v_ctx[c0:c1]),
+                                                          f(wl.k_node[lo:hi]), f(wl.v_node[lo:hi]),
+                                                          wl.parent[lo:hi], wl.scale)
+    return out, lse
+
+
+def oracle_attn(wl, requests=None, max_nodes=None, max_ctx=None):
+    f = lambda x: W.bf16_bits_to_f32(x).astype(np.float64)
+    return A.tree_attention_batch(f(wl.q), f(wl.k_ctx), f(wl.v_ctx), wl.ctx_offset, f(wl.k_node), f(wl.v_node),
+                                  wl.node_offset, wl.parent, wl.Hq, wl.Hkv, wl.scale,
+                                  max_nodes=max_nodes or max(1, wl.max_nodes),
+                                  max_ctx=wl.max_ctx if max_ctx is None else max_ctx, requests=requests)
+
+
+def rows_of(wl, reqs):
+    return np.concatenate([np.arange(wl.node_offset[b], wl.node_offset[b + 1]) for b in reqs] +
+                          [np.zeros(0, int)]).astype(int)
+
+
+def compare(wl, out, lse, ref_out, ref_lse, reqs):
+    rows = rows_of(wl, reqs)
+    e = rowwise_rel_err(out[rows], ref_out[rows])
+    el = float(np.abs(lse[rows] - ref_lse[rows]).max()) if rows.size else 0.0
+    print(f"{wl.name}: out row-normwise rel err {e:.2e}, lse abs err {el:.2e}")
+    assert e <= ATTN_TOL
+    assert el <= ATTN_TOL
+
+
+# ---- ancestry ----------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c3_b16", "c5"])
+def test_ancestry_bit_exact(name):
+    wl = W.make_c5() if name == "c5" else W.make_c3(16)
+    d = _dev()
+    no = torch.from_numpy(wl.node_offset).to(d)
+    par = torch.from_numpy(wl.parent).to(d)
+    anc, st = G.ancestry(no, par, max_nodes=wl.max_nodes)
+    ref = np.concatenate([np.array(O.ancestry(wl.parents_of(b)), dtype=np.uint64) for b in range(wl.B)])
+    assert np.array_equal(anc_u64(anc), ref)
+    assert (host(st) == 0).all()
+
+
+def test_ancestry_matches_verify_masks():
+    wl = W.make_custom([W.random_tree(np.random.default_rng(4), 40) for _ in range(6)], [0] * 6, Hv=4, Hk=2)
+    d = _dev()
+    from helpers import upload
+    u = upload(wl)
+    _, _, anc_v, _ = G.verify(u["S0"], u["q"], u["k"], u["v"], u["g"], u["beta"], u["node_offset"], u["parent"],
+                              max_nodes=wl.max_nodes)
+    anc_a, _ = G.ancestry(u["node_offset"], u["parent"], max_nodes=wl.max_nodes)
+    assert np.array_equal(anc_u64(anc_v), anc_u64(anc_a))
+
+
+def test_ancestry_statuses():
+    d = _dev()
+    # request 0 ok (chain), 1 bad parent (local parent[1] = 1), 2 too many (65 roots), 3 ends beyond T
+    no = torch.tensor([0, 3, 6, 71, 72], dtype=torch.int32, device=d)
+    par_h = np.array([-1, 0, 1, -1, 1, 1] + [-1] * 65, np.int32)
+    par = torch.from_numpy(par_h).to(d)
+    anc = torch.full((71,), -7, dtype=torch.int64, device=d)
+    anc, st = G.ancestry(no, par, max_nodes=64, anc_mask=anc)
+    st = host(st)
+    assert list(st) == [O.STATUS_OK, O.STATUS_BAD_PARENT, O.STATUS_TOO_MANY_NODES, O.STATUS_BAD_OFFSETS]
+    a = anc_u64(anc)
+    assert list(a[:3]) == [1, 3, 7]
+    assert (a[3:] == 0).all()
+
+
+# ---- attention -----------------------------------------------------------------
+
+@pytest.mark.parametrize("split", [None, 64, 100, 1])
+def test_attention_small_full(split):
+    wl = W.make_attn_small(0)
+    out, lse, st, _ = run_attn(wl, split=split)
+    ref_out, ref_lse, ref_st = oracle_attn(wl)
+    assert np.array_equal(st, ref_st)
+    compare(wl, out, lse, ref_out, ref_lse, range(wl.B))
+
+
+def test_attention_split_agrees_with_one_pass():
+    wl = W.make_attn_small(3)
+    o1, l1, _, _ = run_attn(wl)
+    o2, l2, _, _ = run_attn(wl, split=65)
+    rows = rows_of(wl, range(wl.B))
+    assert rowwise_rel_err(o2[rows], o1[rows]) <= ATTN_TOL
+    assert np.abs(l2[rows] - l1[rows]).max() <= ATTN_TOL
+
+
+def test_attention_no_context_at_all():
+    parents = [W.chain(4), W.root_branch(), np.array([-1], np.int32)]
+    wl = W.make_attn(parents, [0, 0, 0], Hq=4, Hkv=1, seed=9, name="attn_noctx")
+    out, lse, st, _ = run_attn(wl)
+    ref_out, ref_lse, ref_st = oracle_attn(wl)
+    assert np.array_equal(st, ref_st)
+    compare(wl, out, lse, ref_out, ref_lse, range(wl.B))
+    # a root with no context sees only itself: its output is its own value, exactly representable
+    r = int(wl.node_offset[2])
+    np.testing.assert_allclose(out[r], np.repeat(W.bf16_bits_to_f32(wl.v_node[r]), 4, axis=0), rtol=0, atol=1e-6)
+
+
+def test_attention_gqa_groups_and_wide_group():
+    # G = 16 query heads per kv head: 64 nodes x 16 = 1024 rows = 16 row groups
+    rng = np.random.default_rng(12)
+    parents = [W.random_tree(rng, 64), W.chain(7)]
+    wl = W.make_attn(parents, [300, 129], Hq=16, Hkv=1, seed=13, name="attn_g16")
+    for split in (None, 128):
+        out, lse, st, _ = run_attn(wl, split=split)
+        ref_out, ref_lse, _ = oracle_attn(wl)
+        compare(wl, out, lse, ref_out, ref_lse, range(wl.B))
+
+
+@pytest.mark.parametrize("split", [None, 1024])
+def test_attention_full_size_sampled(split):
+    wl = W.make_attn_c5(0)
+    out, lse, st, _ = run_attn(wl, split=split)
+    assert (st == 0).all()
+    kinds = np.array(wl.kinds)
+    lens = np.diff(wl.ctx_offset)
+    reqs = sorted({int(np.flatnonzero(kinds == k)[0]) for k in W.C5_KINDS} |
+                  {int(np.argmax(lens)), int(np.argmin(lens)), wl.B - 1})
+    ref_out, ref_lse = oracle_attn_sampled(wl, reqs)
+    compare(wl, out, lse, ref_out, ref_lse, reqs)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def test_attention_deterministic():
+    wl = W.make_attn_small(5)
+    o1, l1, _, d = run_attn(wl, split=64)
+    o2, l2, _, _ = run_attn(wl, split=64)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("split", [None, 50])
+def test_attention_device_errors(split):
+    # request 0 ok, 1 bad mask, 2 context longer than max_ctx, 3 too many nodes, 4 bad node offsets
+    parents = [W.chain(3), W.chain(3), W.chain(2), np.full(66, -1, np.int32), W.chain(2)]
+    wl = W.make_attn(parents, [40, 40, 120, 10, 10], Hq=4, Hkv=2, seed=21, name="attn_err")
+    d = upload_attn(wl)
+    anc, _ = G.ancestry(d["node_offset"], d["parent"], max_nodes=64)
+    a = anc_u64(anc).copy()
+    a[wl.node_offset[1] + 1] = 0b100            # node 1 of request 1 lacks its own bit
+    anc_bad = torch.from_numpy(a.view(np.int64)).to(anc.device)
+    no = wl.node_offset.copy()
+    no_t = torch.from_numpy(no).to(anc.device)
+    no_t[5] = no_t[4] - 1                        # request 4 ends before it starts
+    out = torch.full((wl.T, wl.Hq, 128), 7.0, device=anc.device)
+    o, l, st = G.attention(d["q"], d["k_ctx"], d["v_ctx"], d["ctx_offset"], d["k_node"], d["v_node"], no_t,
+                           anc_bad, wl.scale, max_nodes=64, max_ctx=100, split=split, out=out)
+    torch.cuda.synchronize()
+    st, o = host(st), host(o)
+    assert list(st) == [0, A.STATUS_BAD_MASK, A.STATUS_BAD_CONTEXT, O.STATUS_TOO_MANY_NODES, O.STATUS_BAD_OFFSETS]
+    for b in (1, 2, 3):
+        assert np.isnan(o[wl.node_offset[b]:wl.node_offset[b + 1]]).all()
+    assert (o[wl.node_offset[4]:] == 7.0).all()          # bad offsets: untouched
+    ref_out, ref_lse, _ = oracle_attn(wl, requests={0}, max_nodes=64, max_ctx=100)
+    compare(wl, o, host(l), ref_out, ref_lse, [0])
+
+
+def test_attention_host_errors():
+    wl = W.make_attn_small(0)
+    d = upload_attn(wl)
+    anc, _ = G.ancestry(d["node_offset"], d["parent"], max_nodes=64)
+    args = (d["q"], d["k_ctx"], d["v_ctx"], d["ctx_offset"], d["k_node"], d["v_node"], d["node_offset"], anc)
+    with pytest.raises(G.GdnTreeError) as e:
+        G.attention(*args, float("nan"), max_nodes=64, max_ctx=wl.max_ctx)
+    assert e.value.code == -2
+    ws = torch.empty((16,), dtype=torch.uint8, device=anc.device)
+    with pytest.raises(G.GdnTreeError) as e:
+        G.attention(*args, wl.scale, max_nodes=64, max_ctx=wl.max_ctx, split=32, workspace=ws)
+    assert e.value.code == -8

@@ -457,10 +457,27 @@ class AttnWorkload:
         return bf16_bits_to_f32(getattr(self, name))
 
 
+def _bf16_normal(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
+    """N(0, 1) draws rounded to bf16 bits (nearest even), produced in chunks so
+    that multi-GB arrays need no float64 or uint64 temporaries."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for i in range(0, n, chunk):
+        m = min(chunk, n - i)
+        bits = rng.standard_normal(m, dtype=np.float32).view(np.uint32)
+        out[i:i + m] = ((bits + np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    return out.reshape(shape)
+
+
+CTX_POOL = 32768
+
+
 def make_attn(parents: List[np.ndarray], ctx_lens: List[int], Hq: int = 32, Hkv: int = 8, d: int = 128,
               seed: int = 0, name: str = "attn", kinds=None) -> AttnWorkload:
-    """q, k, v ~ N(0, 1) rounded to bf16, context keys/values likewise; scale 1/sqrt(d).
-    Draw order: q, k_node, v_node, k_ctx, v_ctx."""
+    """q, k, v ~ N(0, 1) rounded to bf16; context keys/values are rows of a pool
+    of min(C, CTX_POOL) such rows per array (all of them, in order, when C fits;
+    else drawn with replacement); scale 1/sqrt(d).  Draw order: q, k_node,
+    v_node, pool row choice, k pool, v pool."""
     rng = np.random.default_rng(seed)
     sizes = [len(p) for p in parents]
     node_offset = np.zeros(len(parents) + 1, dtype=np.int32)
@@ -469,12 +486,16 @@ def make_attn(parents: List[np.ndarray], ctx_lens: List[int], Hq: int = 32, Hkv:
     ctx_offset[1:] = np.cumsum(ctx_lens)
     T, C = int(node_offset[-1]), int(ctx_offset[-1])
     parent = np.concatenate([np.asarray(p, dtype=np.int32) for p in parents]) if T else np.zeros(0, np.int32)
-    bf = lambda shape: f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    bf = lambda shape: _bf16_normal(rng, shape)
     q = bf((T, Hq, d))
     k_node = bf((T, Hkv, d))
     v_node = bf((T, Hkv, d))
-    k_ctx = bf((C, Hkv, d))
-    v_ctx = bf((C, Hkv, d))
+    # context rows: up to CTX_POOL distinct rows; longer caches reuse pool rows
+    # drawn with replacement (drawing every row of a multi-GB cache is too slow)
+    P = min(C, CTX_POOL)
+    idx = np.arange(C) if C <= P else rng.integers(0, P, size=C)
+    k_ctx = bf((P, Hkv, d))[idx]
+    v_ctx = bf((P, Hkv, d))[idx]
     return AttnWorkload(name, len(parents), Hq, Hkv, d, node_offset, parent, ctx_offset, q, k_ctx, v_ctx,
                         k_node, v_node, 1.0 / float(np.sqrt(d)), kinds)
 
