@@ -275,7 +275,8 @@ typedef struct gdn_tree_attn_dims {
  * caller-owned device workspace of gdn_tree_attention_workspace_bytes(dims)
  * bytes (16-byte aligned; contents need no initialisation).  Otherwise
  * workspace may be NULL.  q, k_ctx, v_ctx, k_node, v_node and out must be
- * 16-byte aligned.  scale must be finite.
+ * 16-byte aligned.  scale must be finite and positive.  max_ctx * Hkv * 128
+ * must stay below 2^31 (GDN_TREE_E_SIZE otherwise).
  * Device errors: bad node offsets (1) write nothing for the request; too
  * many nodes (2), a bad context range (7) or a malformed mask (8) give NaN
  * rows in out and lse.

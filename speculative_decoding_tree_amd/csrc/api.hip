@@ -312,7 +312,9 @@ int gdn_tree_attention(const gdn_tree_attn_dims *dims, const uint16_t *q, const 
     int n_split, n_rg;
     int rc = check_attn_dims(dims, n_split, n_rg);
     if (rc != GDN_TREE_OK || dims->B == 0) return rc;
-    if (!isfinite(scale)) return GDN_TREE_E_DIMS;
+    if (!isfinite(scale) || !(scale > 0.f)) return GDN_TREE_E_DIMS;
+    // per-request key/value offsets are 32-bit element counts in the kernel
+    if ((long long)dims->max_ctx * dims->Hkv * GDN_TREE_HEAD_DIM >= (1ll << 31)) return GDN_TREE_E_SIZE;
     if (!node_offset || !ctx_offset) return GDN_TREE_E_NULL;
     if (dims->T > 0 && (!q || !k_node || !v_node || !anc_mask || !out)) return GDN_TREE_E_NULL;
     if (dims->C > 0 && (!k_ctx || !v_ctx)) return GDN_TREE_E_NULL;

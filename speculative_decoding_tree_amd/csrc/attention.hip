@@ -76,11 +76,27 @@ __global__ __launch_bounds__(256) void ancestry_kernel(Args a) {
 
 constexpr int AT = 256;              // threads per workgroup
 constexpr int KB = 64;               // keys per staged block
-constexpr int KS = D + 8;            // K block row stride (bf16 elements; 272 bytes)
-constexpr int VS = KB + 8;           // transposed V row stride (bf16 elements; 144 bytes)
+// K and V blocks sit in LDS row-major (one 256-byte row per key) with the
+// sixteen 16-byte chunks of a row permuted by an XOR with a function of the
+// row, so that the fragment reads below hit distinct banks.
+__device__ __forceinline__ int k_at(int row, int c) { return row * D + 8 * (c ^ (row & 15)); }
+__device__ __forceinline__ int v_at(int row, int c) { return row * D + 8 * (c ^ ((row & 7) << 1)); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4a + b receives
+// element b of the 8 bytes addressed by lanes a, 4 + a, 8 + a, 12 + a.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
 constexpr int ROWS = 64;             // query rows per workgroup
 constexpr int PART = ROWS * (D + 2); // floats per partial record: O rows, then max, then sum
 constexpr float LN2 = 0.6931471805599453f;
+// The running max of a row is only moved when a block raises it by more than
+// this many powers of two; until then probabilities stay below 2^RESCALE.
+constexpr float RESCALE = 8.f;
 
 // Request checks shared by both kernels: offsets, node count, context range.
 __device__ __forceinline__ int attn_request(const AttnArgs &a, int b, int &lo, int &N, int &c0, int &Lc) {
@@ -130,8 +146,8 @@ __device__ __forceinline__ int nan_end(const AttnArgs &a, int rg, int R) {
 }
 
 __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void attn_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[KB * D];
 
     const int n_units = a.B * a.Hkv * a.n_split * a.n_rg;
     const int unit = xcd_unit(blockIdx.x, n_units);
@@ -164,9 +180,12 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void at
     const int nblk = nctx + (sp == 0 ? 1 : 0);   // the draft nodes' own block goes with the first part
 
     // ---- this lane's query row (MFMA B column n) ----
-    const int r = row0 + 16 * w + n;
+    // Row tile wr of the group goes to wave (wr + unit) % 4, so that groups
+    // with a single tile do not all compute on the same wave slot.
+    const int wr = (w - unit) & 3;
+    const int r = row0 + 16 * wr + n;
     const bool rvalid = r < R;
-    const bool active = row0 + 16 * w < R;
+    const bool active = row0 + 16 * wr < R;
     int t = 0, g = 0;
     if (rvalid) {
         t = r / G;
@@ -183,11 +202,13 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void at
         for (int s = 0; s < 4; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
     }
 
-    // ---- staging: thread (kk, kpart) moves K row kk, columns 32 kpart .. +31;
-    //      thread (kp, vpart) moves V rows 2kp, 2kp+1, columns 16 vpart .. +15 ----
-    const int kk = tid >> 2, kpart = tid & 3;
-    const int kp = tid >> 3, vpart = tid & 7;
-    const size_t kvrow = (size_t)a.Hkv * D;
+    // ---- staging: 16 lanes per row and 16-byte chunk c = tid % 16, so each
+    //      load instruction reads whole rows; thread tid moves rows 16q + tid / 16
+    //      of K and of V, q = 0..3. ----
+    const int cch = tid & 15, srow = tid >> 4;
+    // per-request bases are workgroup-uniform; lanes add 32-bit element offsets
+    // (a request's context is below 2^30 elements per array, checked on the host)
+    const uint32_t kvrow = (uint32_t)a.Hkv * D;
     const uint16_t *kctx = a.k_ctx + ((size_t)c0 * a.Hkv + hk) * D;
     const uint16_t *vctx = a.v_ctx + ((size_t)c0 * a.Hkv + hk) * D;
     const uint16_t *knode = a.k_node + ((size_t)lo * a.Hkv + hk) * D;
@@ -200,30 +221,24 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void at
         const int first = nodeb ? 0 : k0 + KB * blk;
         const uint16_t *kb = nodeb ? knode : kctx;
         const uint16_t *vb = nodeb ? vnode : vctx;
-        const uint16_t *ks = kb + (size_t)min(first + kk, last) * kvrow + 32 * kpart;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kst[c] = *reinterpret_cast<const u32x4 *>(ks + 8 * c);
-        const uint16_t *v0 = vb + (size_t)min(first + 2 * kp, last) * kvrow + 16 * vpart;
-        const uint16_t *v1 = vb + (size_t)min(first + 2 * kp + 1, last) * kvrow + 16 * vpart;
-        vst[0] = *reinterpret_cast<const u32x4 *>(v0);
-        vst[1] = *reinterpret_cast<const u32x4 *>(v0 + 8);
-        vst[2] = *reinterpret_cast<const u32x4 *>(v1);
-        vst[3] = *reinterpret_cast<const u32x4 *>(v1 + 8);
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t off = (uint32_t)min(first + 16 * q + srow, last) * kvrow + 8 * cch;
+            kst[q] = *reinterpret_cast<const u32x4 *>(kb + off);
+            vst[q] = *reinterpret_cast<const u32x4 *>(vb + off);
+        }
     };
     auto store_block = [&]() {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4 *>(&Ks[kk * KS + 32 * kpart + 8 * c]) = kst[c];
-        // column d = 16 vpart + e of keys 2kp (low half) and 2kp + 1 (high half)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const uint32_t w0 = vst[e >> 3][(e & 7) >> 1];
-            const uint32_t w1 = vst[2 + (e >> 3)][(e & 7) >> 1];
-            const uint32_t pair = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
-            *reinterpret_cast<uint32_t *>(&Vt[(16 * vpart + e) * VS + 2 * kp]) = pair;
+        for (int q = 0; q < 4; ++q) {
+            *reinterpret_cast<u32x4 *>(&Ks[k_at(16 * q + srow, cch)]) = kst[q];
+            *reinterpret_cast<u32x4 *>(&Vs[v_at(16 * q + srow, cch)]) = vst[q];
         }
     };
 
-    float m = -INFINITY, l = 0.f;   // running max (log2 units) and sum of row n
+    // running max of row n (log2 units, the same in the row's four lanes) and
+    // this lane's share of the row's sum (reduced over the lanes at the end)
+    float m = -INFINITY, l = 0.f;
     f32x4 ot[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -236,53 +251,70 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void at
         if (blk + 1 < nblk) load_block(blk + 1);
         if (!active) continue;
         const bool nodeb = blk >= nctx;
-        const int kfirst = k0 + KB * blk;
+        const int rem = k1 - (k0 + KB * blk);   // context keys left from this block on
 
-        // scores S^T for keys 16 kt + 4 grp + i of row n
+        // scores S^T for keys 16 kt + 4 grp + i of row n (raw q.k)
+        // K fragments of step j = 4 kt + s are read KPF steps ahead
         f32x4 sc[4];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < 4; ++kt) sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        constexpr int KPF = 4;
+        u32x4 kf[KPF];
+        auto kload = [&](int j) {   // row 16 kt + n, chunk 4 s + grp
+            kf[j % KPF] = *reinterpret_cast<const u32x4 *>(&Ks[k_at(16 * (j >> 2) + n, 4 * (j & 3) + grp)]);
+        };
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const u32x4 kf = *reinterpret_cast<const u32x4 *>(&Ks[(16 * kt + n) * KS + 32 * s + 8 * grp]);
-                sc[kt] = mfma(kf, qf[s], sc[kt]);
-            }
+        for (int j = 0; j < KPF; ++j) kload(j);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const u32x4 k = kf[j % KPF];
+            if (j + KPF < 16) kload(j + KPF);
+            sc[j >> 2] = mfma(k, qf[j & 3], sc[j >> 2]);
         }
         float x[4][4];
-        float mb = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[kt][i] = sc[kt][i];
+        if (nodeb || rem < KB) {   // the last context block and the nodes' block: hide keys row n may not see
+            const uint64_t vis = nodeb ? anc_row : ((1ull << rem) - 1ull);
+            const uint64_t vl = vis >> (4 * grp);   // bit 16 kt + i: key 16 kt + 4 grp + i
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!((vl >> (16 * kt + i)) & 1ull)) x[kt][i] = -INFINITY;
+        }
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, x[kt][i]);
+        mloc *= a.scale_log2;   // the scale is positive: max commutes with it
+        if (__ballot(mloc > m + RESCALE)) {   // some row grew past the margin: exact row max
+            float mb = fmaxf(mloc, __shfl_xor(mloc, 16));
+            mb = fmaxf(mb, __shfl_xor(mb, 32));
+            const float mnew = fmaxf(m, mb);
+            const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+            l *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ot[mt][i] *= alpha;
+            m = mnew;
+        }
+        const float mneg = m == -INFINITY ? 0.f : -m;   // a row with nothing visible yet keeps p = 0
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = 16 * kt + 4 * grp + i;
-                const bool ok = nodeb ? ((anc_row >> key) & 1ull) != 0ull : kfirst + key < k1;
-                x[kt][i] = ok ? sc[kt][i] * a.scale_log2 : -INFINITY;
-                mb = fmaxf(mb, x[kt][i]);
+                x[kt][i] = __builtin_amdgcn_exp2f(fmaf(x[kt][i], a.scale_log2, mneg));
+                l += x[kt][i];
             }
-        mb = fmaxf(mb, __shfl_xor(mb, 16));
-        mb = fmaxf(mb, __shfl_xor(mb, 32));
-        const float mnew = fmaxf(m, mb);
-        const float mref = mnew == -INFINITY ? 0.f : mnew;   // a row with nothing visible yet keeps p = 0
-        const float alpha = __builtin_amdgcn_exp2f(m - mref);
-        float rs = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[kt][i] = __builtin_amdgcn_exp2f(x[kt][i] - mref);
-                rs += x[kt][i];
-            }
-        rs += __shfl_xor(rs, 16);
-        rs += __shfl_xor(rs, 32);
-        l = l * alpha + rs;
-        m = mnew;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ot[mt][i] *= alpha;
 
-        // O^T += V^T P^T over the block's two 32-key steps
+        // O^T += V^T P^T over the block's two 32-key steps; the V^T fragments
+        // of step j = 8 ks + mt are read PF steps ahead of their MFMAs
+        u32x4 phi[2], plo[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
@@ -290,18 +322,35 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void at
             split_bf16x2(x[2 * ks][2], x[2 * ks][3], h1, l1);
             split_bf16x2(x[2 * ks + 1][0], x[2 * ks + 1][1], h2, l2);
             split_bf16x2(x[2 * ks + 1][2], x[2 * ks + 1][3], h3, l3);
-            const u32x4 phi = {h0, h1, h2, h3}, plo = {l0, l1, l2, l3};
+            phi[ks] = u32x4{h0, h1, h2, h3};
+            plo[ks] = u32x4{l0, l1, l2, l3};
+        }
+        constexpr int PF = 4;
+        u32x4 vf[PF];
+        // lane s = n of group grp addresses key 32 ks + 16 h + 4 grp + s / 4,
+        // columns 16 mt + 4 (s % 4) .. +3, and receives column 16 mt + n of
+        // keys 32 ks + 16 h + 4 grp + e, e = 0..3 (k-slots 4h .. 4h+3)
+        const int vsub = 4 * (n & 1);   // element offset inside the 16-byte chunk
+        auto vload = [&](int j) {
+            const int ks = j >> 3, mt = j & 7;
+            const int c = 2 * mt + ((n & 3) >> 1);
+            const int r0 = 32 * ks + 4 * grp + (n >> 2);
+            const u32x2 va = lds_read_tr16(&Vs[v_at(r0, c) + vsub]);
+            const u32x2 vb = lds_read_tr16(&Vs[v_at(r0 + 16, c) + vsub]);
+            vf[j % PF] = u32x4{va.x, va.y, vb.x, vb.y};
+        };
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const uint16_t *vp = &Vt[(16 * mt + n) * VS + 32 * ks + 4 * grp];
-                const u32x2 va = *reinterpret_cast<const u32x2 *>(vp);
-                const u32x2 vb = *reinterpret_cast<const u32x2 *>(vp + 16);
-                const u32x4 vf = {va.x, va.y, vb.x, vb.y};
-                ot[mt] = mfma(vf, phi, ot[mt]);
-                ot[mt] = mfma(vf, plo, ot[mt]);
-            }
+        for (int j = 0; j < PF; ++j) vload(j);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const u32x4 v = vf[j % PF];
+            if (j + PF < 16) vload(j + PF);
+            ot[j & 7] = mfma(v, phi[j >> 3], ot[j & 7]);
+            ot[j & 7] = mfma(v, plo[j >> 3], ot[j & 7]);
         }
     }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
     if (!rvalid) return;
 
     // lane (n, grp) holds columns 16 mt + 4 grp .. +3 of row n
@@ -316,7 +365,7 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void at
         if (grp == 0 && a.lse) a.lse[orow] = (m + log2f(l)) * LN2;
     } else {
         float *rec = a.ws + ((((size_t)b * a.Hkv + hk) * a.n_split + sp) * a.n_rg + rg) * PART;
-        const int rl = 16 * w + n;
+        const int rl = 16 * wr + n;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
             *reinterpret_cast<float4 *>(rec + rl * D + 16 * mt + 4 * grp) =

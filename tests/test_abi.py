@@ -144,6 +144,9 @@ def test_attention_host_validation_pointers_scale_workspace():
     good = [ok, ok, ok, ok, ok, ok, ok, ok]
     tail = [ok, ok, None, ctypes.c_size_t(0), None, None]
     assert L.gdn_tree_attention(ctypes.byref(d), *good, ctypes.c_float(float("inf")), *tail) == -2
+    assert L.gdn_tree_attention(ctypes.byref(d), *good, ctypes.c_float(-0.1), *tail) == -2
+    big = G.make_attn_dims(4, 2, 1, 20, 100, 8, 1 << 24)                # 2^24 x 1 x 128 = 2^31 elements
+    assert L.gdn_tree_attention(ctypes.byref(big), *good, ctypes.c_float(0.1), *tail) == -6
     bad_align = [ok, odd, ok, ok, ok, ok, ok, ok]
     assert L.gdn_tree_attention(ctypes.byref(d), *bad_align, ctypes.c_float(0.1), *tail) == -7
     split = G.make_attn_dims(4, 32, 8, 20, 100, 8, 50, split=16)      # 4 context parts -> workspace needed
