@@ -34,8 +34,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "verified tree-nodes/s (all heads) + commits/s at batch 256; % HBM peak"
 D = 128
-KERNEL_SOURCES = ("speculative_decoding_tree_amd/csrc/common.h", "speculative_decoding_tree_amd/csrc/verify.hip",
-                  "speculative_decoding_tree_amd/csrc/commit.hip")
+KERNEL_SOURCES = ("speculative_decoding_tree_amd/csrc/common.h", "speculative_decoding_tree_amd/csrc/mfma.h",
+                  "speculative_decoding_tree_amd/csrc/verify.hip", "speculative_decoding_tree_amd/csrc/commit.hip",
+                  "speculative_decoding_tree_amd/csrc/attention.hip")
 
 
 def kernel_source_sha() -> str:
@@ -274,6 +275,8 @@ def attention_row(args, stream):
         key = "one_pass" if split is None else f"split_{split}"
         res[key] = {"avg_us": t, "alg_bytes": nbytes, "alg_GBps": nbytes / (t * 1e-6) / 1e9,
                     "hbm_frac": nbytes / (t * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        if split is None:
+            res[key]["hbm_traffic_bytes"] = measured_traffic("c5_mixed_b256", "gdn_tree_attention")
     assert (st.cpu().numpy() == 0).all()
     return res
 
