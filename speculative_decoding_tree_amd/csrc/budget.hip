@@ -63,6 +63,7 @@ __device__ __forceinline__ uint64_t node_key(float s, int dep, int t) {
 }
 
 constexpr int SEL_T = 1024;
+constexpr int SEL_KPT = 8;   // keys a thread keeps in registers across the passes (T <= 8192)
 
 __global__ __launch_bounds__(SEL_T) void select_kernel(Args a, int budget, float threshold) {
     __shared__ uint32_t hist[256];
@@ -76,6 +77,13 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(Args a, int budget, float
     // budget-th smallest key (1-based); none when budget <= 0, all when budget >= T
     uint64_t kth = 0;
     const bool all = budget >= T;
+    const bool cached = T <= SEL_T * SEL_KPT;
+    uint64_t kc[SEL_KPT];
+#pragma unroll
+    for (int j = 0; j < SEL_KPT; ++j) {
+        const int t = tid + j * SEL_T;
+        kc[j] = (cached && t < T) ? node_key(surv[t], dep[t], t) : ~0ull;
+    }
     if (budget > 0 && !all) {
         if (tid == 0) {
             s_prefix = 0;
@@ -88,20 +96,51 @@ __global__ __launch_bounds__(SEL_T) void select_kernel(Args a, int budget, float
             for (int i = tid; i < 256; i += SEL_T) hist[i] = 0;
             __syncthreads();
             const uint64_t prefix = s_prefix;
-            for (int t = tid; t < T; t += SEL_T) {
-                const uint64_t key = node_key(surv[t], dep[t], t);
-                if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xff], 1u);
+            if (cached) {
+#pragma unroll
+                for (int j = 0; j < SEL_KPT; ++j)
+                    if (tid + j * SEL_T < T && (kc[j] & hi_mask) == prefix)
+                        atomicAdd(&hist[(kc[j] >> shift) & 0xff], 1u);
+            } else {
+                for (int t = tid; t < T; t += SEL_T) {
+                    const uint64_t key = node_key(surv[t], dep[t], t);
+                    if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xff], 1u);
+                }
             }
             __syncthreads();
-            if (tid == 0) {
-                int r = s_rank;
-                int d = 0;
-                for (; d < 256; ++d) {
-                    if ((int)hist[d] >= r) break;
-                    r -= hist[d];
+            if (tid < 64) {
+                // wave 0 finds the digit holding the rank: lane l sums bins 4l .. 4l+3,
+                // an inclusive scan over lanes gives each lane's cumulative count, and
+                // the first lane whose cumulative count reaches the rank owns the digit
+                const int r = s_rank;
+                const uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2],
+                               h3 = hist[4 * tid + 3];
+                int incl = (int)(h0 + h1 + h2 + h3);
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int up = __shfl_up(incl, off);
+                    if (tid >= off) incl += up;
                 }
-                s_rank = r;
-                s_prefix = prefix | ((uint64_t)d << shift);
+                const int excl = incl - (int)(h0 + h1 + h2 + h3);
+                const unsigned long long hit = __ballot(incl >= r);
+                const int owner = __ffsll((long long)hit) - 1;   // r <= total, so some lane hits
+                if (tid == owner) {
+                    int rr = r - excl, d = 4 * tid;
+                    if ((int)h0 < rr) {
+                        rr -= h0;
+                        ++d;
+                        if ((int)h1 < rr) {
+                            rr -= h1;
+                            ++d;
+                            if ((int)h2 < rr) {
+                                rr -= h2;
+                                ++d;
+                            }
+                        }
+                    }
+                    s_rank = rr;
+                    s_prefix = prefix | ((uint64_t)d << shift);
+                }
             }
             __syncthreads();
         }

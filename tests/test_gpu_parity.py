@@ -420,3 +420,22 @@ def test_budget_select_invalid_request_and_full_batch():
     ok = ~np.isnan(so)
     assert np.array_equal(sh[ok].view(np.uint32), so[ok].view(np.uint32))
     assert np.array_equal(host(keep), ko) and np.array_equal(host(kept), co) and np.array_equal(host(st), sto)
+
+
+@pytest.mark.parametrize("budget_frac", [0.1, 0.6])
+def test_budget_select_more_nodes_than_register_cache(budget_frac):
+    # 160 random 64-node trees: 10240 nodes, more than the 8192 keys the select
+    # kernel keeps in registers, so every radix pass re-reads them
+    rng = np.random.default_rng(31)
+    parents = [W.random_tree(rng, 64) for _ in range(160)]
+    wl = W.make_custom(parents, [0] * len(parents), Hv=1, Hk=1, seed=32)
+    assert wl.T > 8192
+    p = W.acceptance_probs(wl, seed=33)
+    budget = int(budget_frac * wl.T)
+    so, ko, co, sto = O.budget_select(wl.node_offset, wl.parent, p, budget, 0.02)
+    d = upload(wl)
+    s, keep, kept, st = G.budget_select(d["node_offset"], d["parent"], torch.from_numpy(p).cuda(), budget, 0.02,
+                                        max_nodes=wl.max_nodes)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(keep), ko) and np.array_equal(host(kept), co) and np.array_equal(host(st), sto)
