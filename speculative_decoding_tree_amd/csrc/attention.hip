@@ -11,20 +11,23 @@
 // gfx950 layout.  A workgroup (4 wave64) owns 64 query rows of one
 // (request, kv-head): row r = (node r / G, query head hk G + r % G), so the
 // G query heads of a node sit in neighbouring rows and every row of the
-// workgroup shares the same keys.  Wave w owns rows 16w .. 16w+15.  Keys go
-// through LDS 64 at a time: K rows as they are, V transposed ([d][key]) so
-// that a lane can hold eight keys of one column.  Per block and wave:
+// workgroup shares the same keys.  Each group of 16 rows is owned by one
+// wave.  Keys go through LDS 64 at a time, K and V rows as they are in
+// memory, their 16-byte chunks permuted per row (XOR) so that fragment reads
+// hit distinct banks.  Per block and wave:
 //   S^T = K Q^T          (v_mfma_f32_16x16x32_bf16; A = K rows from LDS,
 //                         B = the wave's Q rows, loaded once into registers)
 // leaves lane (n, grp) with keys 16kt + 4grp + i of query row n, so the
-// online-softmax statistics of row n live in lane n (reduced over the four
-// lane groups with two xor shuffles), and the probabilities are already laid
-// out as the B operand of
-//   O^T += V^T P^T       (A = V^T from LDS; k-slot 8grp + e holds key
-//                         32ks + 16(e/4) + 4grp + e%4, the same key in both)
+// online-softmax statistics of row n live in the four lanes of row n, and
+// the probabilities are already laid out as the B operand of
+//   O^T += V^T P^T       (A = V^T, read from the row-major V block with the
+//                         transposing LDS read ds_read_b64_tr_b16; k-slot
+//                         8grp + e holds key 32ks + 16(e/4) + 4grp + e%4 in both)
 // with P split into bf16 hi + lo (two MFMAs, ~16 mantissa bits), so no
-// register moves between lanes.  Global loads of the next block are issued
-// before the current block is computed.
+// register moves between lanes.  Blocks wholly inside the context skip the
+// mask; a row's running max only moves when a block raises it by more than
+// 2^8, so most blocks need no cross-lane reduction.  Global loads of the next
+// block are issued before the current block is computed.
 //
 // When a request's context is split over several workgroups, each writes an
 // unnormalised partial (O, running max, sum) to the workspace and a second
