@@ -47,6 +47,13 @@ bool any_misaligned(Ps... ps) {
     return (misaligned((const void *)ps) || ...);
 }
 
+// Query rows per attention workgroup: 128 (two 16-row tiles per wave, so each
+// K/V fragment read from LDS serves 32 rows) once a request can have more
+// than 64 rows, else 64.
+int attn_rows_wg(const gdn_tree_attn_dims *d) {
+    return (long long)d->max_nodes * (d->Hq / d->Hkv) > 64 ? 128 : 64;
+}
+
 // Attention dims; also derives the launch shape.  Returns a GDN_TREE_* code.
 int check_attn_dims(const gdn_tree_attn_dims *d, int &n_split, int &n_rg) {
     n_split = 1;
@@ -59,7 +66,8 @@ int check_attn_dims(const gdn_tree_attn_dims *d, int &n_split, int &n_rg) {
     if (d->max_nodes < 1 || d->max_nodes > GDN_TREE_MAX_NODES) return GDN_TREE_E_MAX_NODES;
     if (d->max_ctx < 0 || d->max_ctx > (1 << 30) || d->split < 1) return GDN_TREE_E_DIMS;
     const long long G = d->Hq / d->Hkv;
-    n_rg = (int)((d->max_nodes * G + 63) / 64);
+    const int rows_wg = attn_rows_wg(d);
+    n_rg = (int)((d->max_nodes * G + rows_wg - 1) / rows_wg);
     n_split = d->max_ctx > d->split ? (int)(((long long)d->max_ctx + d->split - 1) / d->split) : 1;
     const long long units = (long long)d->B * d->Hkv * n_split * n_rg;
     if (units > (long long)INT_MAX - 8) return GDN_TREE_E_SIZE;
@@ -71,7 +79,8 @@ int check_attn_dims(const gdn_tree_attn_dims *d, int &n_split, int &n_rg) {
 
 size_t attn_workspace(const gdn_tree_attn_dims *d, int n_split, int n_rg) {
     if (n_split <= 1) return 0;
-    return (size_t)d->B * d->Hkv * n_split * n_rg * 64u * (GDN_TREE_HEAD_DIM + 2) * sizeof(float);
+    return (size_t)d->B * d->Hkv * n_split * n_rg * (size_t)attn_rows_wg(d) * (GDN_TREE_HEAD_DIM + 2) *
+           sizeof(float);
 }
 
 int finish(hipError_t e) { return e == hipSuccess ? GDN_TREE_OK : GDN_TREE_E_LAUNCH; }
@@ -333,6 +342,7 @@ int gdn_tree_attention(const gdn_tree_attn_dims *dims, const uint16_t *q, const 
     a.split = dims->split;
     a.n_split = n_split;
     a.n_rg = n_rg;
+    a.rows_wg = attn_rows_wg(dims);
     a.scale_log2 = scale * 1.4426950408889634f;
     a.q = q;
     a.k_ctx = k_ctx;

@@ -94,8 +94,10 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
         (__attribute__((address_space(3))) v4i16 *)(p));
     return __builtin_bit_cast(u32x2, r);
 }
-constexpr int ROWS = 64;             // query rows per workgroup
-constexpr int PART = ROWS * (D + 2); // floats per partial record: O rows, then max, then sum
+// A workgroup owns rows_wg = 64 TPW query rows (TPW 16-row tiles per wave); a
+// partial record of a split context holds rows_wg rows of O, then the
+// rows' running max, then their sums.
+__host__ __device__ __forceinline__ size_t part_floats(int rows_wg) { return (size_t)rows_wg * (D + 2); }
 constexpr float LN2 = 0.6931471805599453f;
 // The running max of a row is only moved when a block raises it by more than
 // this many powers of two; until then probabilities stay below 2^RESCALE.
@@ -142,13 +144,15 @@ __device__ void nan_rows(const AttnArgs &a, int lo, int hk, int r_begin, int r_e
 }
 
 // Rows a workgroup of row group rg answers for when the request is invalid:
-// its 64 rows, and for the last group every row beyond (a request with more
+// its own rows, and for the last group every row beyond (a request with more
 // nodes than max_nodes has rows no group was sized for).
 __device__ __forceinline__ int nan_end(const AttnArgs &a, int rg, int R) {
-    return rg == a.n_rg - 1 ? R : min(R, ROWS * (rg + 1));
+    return rg == a.n_rg - 1 ? R : min(R, a.rows_wg * (rg + 1));
 }
 
-__global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void attn_kernel(AttnArgs a) {
+template <int TPW>
+__global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3 : 2))) void attn_kernel(AttnArgs a) {
+    constexpr int ROWS = 64 * TPW;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * D];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[KB * D];
 
@@ -182,28 +186,33 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void at
     const int nctx = k1 > k0 ? (k1 - k0 + KB - 1) / KB : 0;
     const int nblk = nctx + (sp == 0 ? 1 : 0);   // the draft nodes' own block goes with the first part
 
-    // ---- this lane's query row (MFMA B column n) ----
-    // Row tile wr of the group goes to wave (wr + unit) % 4, so that groups
-    // with a single tile do not all compute on the same wave slot.
+    // ---- this lane's query rows (MFMA B column n), one per tile ----
+    // Row slot wr of the group goes to wave (wr + unit) % 4, so that groups
+    // with a single slot do not all compute on the same wave slot.
     const int wr = (w - unit) & 3;
-    const int r = row0 + 16 * wr + n;
-    const bool rvalid = r < R;
-    const bool active = row0 + 16 * wr < R;
-    int t = 0, g = 0;
-    if (rvalid) {
-        t = r / G;
-        g = r - t * G;
-    }
-    const uint64_t anc_row = rvalid ? a.anc_mask[lo + t] : 0ull;
-    u32x4 qf[4];
-    if (rvalid) {
-        const uint16_t *qp = a.q + ((size_t)(lo + t) * a.Hq + hk * G + g) * D + 8 * grp;
+    int t[TPW], g[TPW];
+    bool rvalid[TPW], tact[TPW];   // tact: the tile has a valid row (wave-uniform)
+    uint64_t anc_row[TPW];
+    u32x4 qf[TPW][4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const u32x4 *>(qp + 32 * s);
-    } else {
+    for (int tt = 0; tt < TPW; ++tt) {
+        const int rb = row0 + 16 * (TPW * wr + tt);
+        const int r = rb + n;
+        tact[tt] = rb < R;
+        rvalid[tt] = r < R;
+        t[tt] = rvalid[tt] ? r / G : 0;
+        g[tt] = rvalid[tt] ? r - t[tt] * G : 0;
+        anc_row[tt] = rvalid[tt] ? a.anc_mask[lo + t[tt]] : 0ull;
+        if (rvalid[tt]) {
+            const uint16_t *qp = a.q + ((size_t)(lo + t[tt]) * a.Hq + hk * G + g[tt]) * D + 8 * grp;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qf[s] = u32x4{0u, 0u, 0u, 0u};
+            for (int s = 0; s < 4; ++s) qf[tt][s] = *reinterpret_cast<const u32x4 *>(qp + 32 * s);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) qf[tt][s] = u32x4{0u, 0u, 0u, 0u};
+        }
     }
+    const bool active = tact[0];
 
     // ---- staging: 16 lanes per row and 16-byte chunk c = tid % 16, so each
     //      load instruction reads whole rows; thread tid moves rows 16q + tid / 16
@@ -241,10 +250,15 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void at
 
     // running max of row n (log2 units, the same in the row's four lanes) and
     // this lane's share of the row's sum (reduced over the lanes at the end)
-    float m = -INFINITY, l = 0.f;
-    f32x4 ot[8];
+    float m[TPW], l[TPW];
+    f32x4 ot[TPW][8];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) ot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < TPW; ++tt) {
+        m[tt] = -INFINITY;
+        l[tt] = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) ot[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     load_block(0);
     for (int blk = 0; blk < nblk; ++blk) {
@@ -256,11 +270,14 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void at
         const bool nodeb = blk >= nctx;
         const int rem = k1 - (k0 + KB * blk);   // context keys left from this block on
 
-        // scores S^T for keys 16 kt + 4 grp + i of row n (raw q.k)
-        // K fragments of step j = 4 kt + s are read KPF steps ahead
-        f32x4 sc[4];
+        // scores S^T for keys 16 kt + 4 grp + i of row n (raw q.k); each K
+        // fragment serves every tile of the wave; fragments of step
+        // j = 4 kt + s are read KPF steps ahead
+        f32x4 sc[TPW][4];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) sc[tt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         constexpr int KPF = 4;
         u32x4 kf[KPF];
         auto kload = [&](int j) {   // row 16 kt + n, chunk 4 s + grp
@@ -272,62 +289,70 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void at
         for (int j = 0; j < 16; ++j) {
             const u32x4 k = kf[j % KPF];
             if (j + KPF < 16) kload(j + KPF);
-            sc[j >> 2] = mfma(k, qf[j & 3], sc[j >> 2]);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+                if (tt == 0 || tact[tt]) sc[tt][j >> 2] = mfma(k, qf[tt][j & 3], sc[tt][j >> 2]);
         }
-        float x[4][4];
+
+        // softmax per tile; P in bf16 hi + lo as the B operand of the value product
+        u32x4 phi[TPW][2], plo[TPW][2];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[kt][i] = sc[kt][i];
-        if (nodeb || rem < KB) {   // the last context block and the nodes' block: hide keys row n may not see
-            const uint64_t vis = nodeb ? anc_row : ((1ull << rem) - 1ull);
-            const uint64_t vl = vis >> (4 * grp);   // bit 16 kt + i: key 16 kt + 4 grp + i
+        for (int tt = 0; tt < TPW; ++tt) {
+            float x[4][4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (!((vl >> (16 * kt + i)) & 1ull)) x[kt][i] = -INFINITY;
-        }
-        float mloc = -INFINITY;
+                for (int i = 0; i < 4; ++i) x[kt][i] = sc[tt][kt][i];
+            if (nodeb || rem < KB) {   // the last context block and the nodes' block: hide keys row n may not see
+                const uint64_t vis = nodeb ? anc_row[tt] : ((1ull << rem) - 1ull);
+                const uint64_t vl = vis >> (4 * grp);   // bit 16 kt + i: key 16 kt + 4 grp + i
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+                for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, x[kt][i]);
-        mloc *= a.scale_log2;   // the scale is positive: max commutes with it
-        if (__ballot(mloc > m + RESCALE)) {   // some row grew past the margin: exact row max
-            float mb = fmaxf(mloc, __shfl_xor(mloc, 16));
-            mb = fmaxf(mb, __shfl_xor(mb, 32));
-            const float mnew = fmaxf(m, mb);
-            const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
-            l *= alpha;
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ot[mt][i] *= alpha;
-            m = mnew;
-        }
-        const float mneg = m == -INFINITY ? 0.f : -m;   // a row with nothing visible yet keeps p = 0
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[kt][i] = __builtin_amdgcn_exp2f(fmaf(x[kt][i], a.scale_log2, mneg));
-                l += x[kt][i];
+                    for (int i = 0; i < 4; ++i)
+                        if (!((vl >> (16 * kt + i)) & 1ull)) x[kt][i] = -INFINITY;
             }
-
-        // O^T += V^T P^T over the block's two 32-key steps; the V^T fragments
-        // of step j = 8 ks + mt are read PF steps ahead of their MFMAs
-        u32x4 phi[2], plo[2];
+            float mloc = -INFINITY;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-            split_bf16x2(x[2 * ks][0], x[2 * ks][1], h0, l0);
-            split_bf16x2(x[2 * ks][2], x[2 * ks][3], h1, l1);
-            split_bf16x2(x[2 * ks + 1][0], x[2 * ks + 1][1], h2, l2);
-            split_bf16x2(x[2 * ks + 1][2], x[2 * ks + 1][3], h3, l3);
-            phi[ks] = u32x4{h0, h1, h2, h3};
-            plo[ks] = u32x4{l0, l1, l2, l3};
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, x[kt][i]);
+            mloc *= a.scale_log2;   // the scale is positive: max commutes with it
+            if (__ballot(mloc > m[tt] + RESCALE)) {   // some row grew past the margin: exact row max
+                float mb = fmaxf(mloc, __shfl_xor(mloc, 16));
+                mb = fmaxf(mb, __shfl_xor(mb, 32));
+                const float mnew = fmaxf(m[tt], mb);
+                const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[tt] - mnew);
+                l[tt] *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ot[tt][mt][i] *= alpha;
+                m[tt] = mnew;
+            }
+            const float mneg = m[tt] == -INFINITY ? 0.f : -m[tt];   // nothing visible yet: p = 0
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[kt][i] = __builtin_amdgcn_exp2f(fmaf(x[kt][i], a.scale_log2, mneg));
+                    l[tt] += x[kt][i];
+                }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+                split_bf16x2(x[2 * ks][0], x[2 * ks][1], h0, l0);
+                split_bf16x2(x[2 * ks][2], x[2 * ks][3], h1, l1);
+                split_bf16x2(x[2 * ks + 1][0], x[2 * ks + 1][1], h2, l2);
+                split_bf16x2(x[2 * ks + 1][2], x[2 * ks + 1][3], h3, l3);
+                phi[tt][ks] = u32x4{h0, h1, h2, h3};
+                plo[tt][ks] = u32x4{l0, l1, l2, l3};
+            }
         }
+
+        // O^T += V^T P^T over the block's two 32-key steps; each V^T fragment
+        // serves every tile; fragments of step j = 8 ks + mt are read PF
+        // steps ahead of their MFMAs
         constexpr int PF = 4;
         u32x4 vf[PF];
         // lane s = n of group grp addresses key 32 ks + 16 h + 4 grp + s / 4,
@@ -348,34 +373,44 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(3))) void at
         for (int j = 0; j < 16; ++j) {
             const u32x4 v = vf[j % PF];
             if (j + PF < 16) vload(j + PF);
-            ot[j & 7] = mfma(v, phi[j >> 3], ot[j & 7]);
-            ot[j & 7] = mfma(v, plo[j >> 3], ot[j & 7]);
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+                if (tt == 0 || tact[tt]) {
+                    ot[tt][j & 7] = mfma(v, phi[tt][j >> 3], ot[tt][j & 7]);
+                    ot[tt][j & 7] = mfma(v, plo[tt][j >> 3], ot[tt][j & 7]);
+                }
         }
     }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (!rvalid) return;
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        l[tt] += __shfl_xor(l[tt], 16);
+        l[tt] += __shfl_xor(l[tt], 32);
+    }
 
-    // lane (n, grp) holds columns 16 mt + 4 grp .. +3 of row n
-    if (a.n_split == 1) {
-        const size_t orow = (size_t)(lo + t) * a.Hq + hk * G + g;
-        const float inv = 1.f / l;
-        float *op = a.out + orow * D + 4 * grp;
+    // lane (n, grp) holds columns 16 mt + 4 grp .. +3 of its rows
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-            *reinterpret_cast<float4 *>(op + 16 * mt) =
-                make_float4(ot[mt][0] * inv, ot[mt][1] * inv, ot[mt][2] * inv, ot[mt][3] * inv);
-        if (grp == 0 && a.lse) a.lse[orow] = (m + log2f(l)) * LN2;
-    } else {
-        float *rec = a.ws + ((((size_t)b * a.Hkv + hk) * a.n_split + sp) * a.n_rg + rg) * PART;
-        const int rl = 16 * wr + n;
+    for (int tt = 0; tt < TPW; ++tt) {
+        if (!rvalid[tt]) continue;
+        if (a.n_split == 1) {
+            const size_t orow = (size_t)(lo + t[tt]) * a.Hq + hk * G + g[tt];
+            const float inv = 1.f / l[tt];
+            float *op = a.out + orow * D + 4 * grp;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-            *reinterpret_cast<float4 *>(rec + rl * D + 16 * mt + 4 * grp) =
-                make_float4(ot[mt][0], ot[mt][1], ot[mt][2], ot[mt][3]);
-        if (grp == 0) {
-            rec[ROWS * D + rl] = m;
-            rec[ROWS * D + ROWS + rl] = l;
+            for (int mt = 0; mt < 8; ++mt)
+                *reinterpret_cast<float4 *>(op + 16 * mt) = make_float4(ot[tt][mt][0] * inv, ot[tt][mt][1] * inv,
+                                                                        ot[tt][mt][2] * inv, ot[tt][mt][3] * inv);
+            if (grp == 0 && a.lse) a.lse[orow] = (m[tt] + log2f(l[tt])) * LN2;
+        } else {
+            float *rec = a.ws + ((((size_t)b * a.Hkv + hk) * a.n_split + sp) * a.n_rg + rg) * part_floats(ROWS);
+            const int rl = 16 * (TPW * wr + tt) + n;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+                *reinterpret_cast<float4 *>(rec + rl * D + 16 * mt + 4 * grp) =
+                    make_float4(ot[tt][mt][0], ot[tt][mt][1], ot[tt][mt][2], ot[tt][mt][3]);
+            if (grp == 0) {
+                rec[ROWS * D + rl] = m[tt];
+                rec[ROWS * D + ROWS + rl] = l[tt];
+            }
         }
     }
 }
@@ -394,14 +429,17 @@ __global__ __launch_bounds__(AT) void attn_merge_kernel(AttnArgs a) {
     if (st == GDN_TREE_S_BAD_OFFSETS) return;
     const int G = a.G;
     const int R = N * G;
+    const int ROWS = a.rows_wg;
     if (ROWS * rg >= R) return;
     if (st != GDN_TREE_S_OK) {
         nan_rows(a, lo, hk, ROWS * rg, nan_end(a, rg, R));
         return;
     }
-    const int rl = tid >> 2, part = tid & 3;
+    const int part = tid & 3;
+    const size_t PART = part_floats(ROWS);
+  for (int rl = tid >> 2; rl < ROWS; rl += AT / 4) {
     const int r = ROWS * rg + rl;
-    if (r >= R) return;
+    if (r >= R) break;
     const int t = r / G, g = r - t * G;
     const size_t orow = (size_t)(lo + t) * a.Hq + hk * G + g;
     float *op = a.out + orow * D + 32 * part;
@@ -433,6 +471,7 @@ __global__ __launch_bounds__(AT) void attn_merge_kernel(AttnArgs a) {
     for (int i = 0; i < 8; ++i)
         *reinterpret_cast<float4 *>(op + 4 * i) = make_float4(acc[i].x * inv, acc[i].y * inv, acc[i].z * inv, acc[i].w * inv);
     if (part == 0 && a.lse) a.lse[orow] = (M + log2f(L)) * LN2;
+  }
 }
 
 }  // namespace
@@ -444,7 +483,10 @@ hipError_t launch_ancestry(const Args &a, hipStream_t stream) {
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
     const int units = a.B * a.Hkv * a.n_split * a.n_rg;
-    attn_kernel<<<dim3(xcd_grid(units)), dim3(AT), 0, stream>>>(a);
+    if (a.rows_wg == 128)
+        attn_kernel<2><<<dim3(xcd_grid(units)), dim3(AT), 0, stream>>>(a);
+    else
+        attn_kernel<1><<<dim3(xcd_grid(units)), dim3(AT), 0, stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;
     attn_merge_kernel<<<dim3(a.B * a.Hkv * a.n_rg), dim3(AT), 0, stream>>>(a);

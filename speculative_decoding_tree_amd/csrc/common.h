@@ -38,6 +38,7 @@ struct Args {
 // Argument block of the tree-bias attention kernels.
 struct AttnArgs {
     int B, Hq, Hkv, G, T, C, max_nodes, max_ctx, split, n_split, n_rg;
+    int rows_wg;                            // query rows per workgroup (64 or 128)
     float scale_log2;                       // softmax scale times log2(e)
     const uint16_t *q, *k_ctx, *v_ctx, *k_node, *v_node;
     const int32_t *ctx_offset, *node_offset;
