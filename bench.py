@@ -281,6 +281,39 @@ def attention_row(args, stream):
     return res
 
 
+def batch_one_row(args, stream):
+    """Latency of one verify + accepted-path + commit step at batch one: the
+    6-node root-branch tree of one request, 32 value / 16 key heads (the
+    shape of the batch-one decode gate the pages report)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from speculative_decoding_tree_amd import gdn_tree as G
+    wl = W.make_c3(B=1)
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    S0, q, k, v, g, beta = f32(wl.S0), bf(wl.q), bf(wl.k), bf(wl.v), f32(wl.g), f32(wl.beta)
+    off, par, acc = i32(wl.node_offset), i32(wl.parent), i32(wl.accept_node)
+    mn = wl.max_nodes
+    out = torch.empty((wl.T, wl.Hv, D), dtype=torch.float32, device=dev)
+    U = torch.empty_like(out)
+    anc = torch.empty((wl.T,), dtype=torch.int64, device=dev)
+    st = torch.empty((1,), dtype=torch.int32, device=dev)
+    path = torch.empty((1, mn), dtype=torch.int32, device=dev)
+    plen = torch.empty((1,), dtype=torch.int32, device=dev)
+    S1 = torch.empty_like(S0)
+
+    def step(i):
+        G.verify(S0, q, k, v, g, beta, off, par, max_nodes=mn, out=out, U=U, anc_mask=anc, status=st, stream=stream)
+        G.accepted_path(off, par, acc, max_nodes=mn, path=path, path_len=plen, status=st, stream=stream)
+        G.commit(S0, U, k, g, off, par, path, plen, max_nodes=mn, S_out=S1, status=st, stream=stream)
+
+    t = _time_launches(step, max(20, args.steps), stream)
+    return {"workload": "1 request, 6-node root-branch tree, Hv=32, Hk=16, d=128", "step_us": t}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +326,7 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=128, help="requests in the oracle sample")
     ap.add_argument("--no-next", action="store_true", help="skip the next-row measurements")
     ap.add_argument("--no-attention", action="store_true", help="skip the tree-bias attention measurement")
+    ap.add_argument("--no-batch-one", action="store_true", help="skip the batch-one latency measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -469,6 +503,8 @@ def main():
         result["next_rows"] = next_rows(args, wl, pools, mn, stream)
         if not args.no_attention:
             result["next_rows"]["tree_attention"] = attention_row(args, stream)
+        if not args.no_batch_one:
+            result["next_rows"]["batch_one"] = batch_one_row(args, stream)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
