@@ -102,23 +102,33 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
     const int n = lane & 15, grp = lane >> 4;
     const int c = 32 * w + 2 * n;   // this lane's column pair
 
+    // H0 depends only on (slot, head): its loads go out before the node
+    // offsets come back, so the state is in flight during that round trip.
+    const int slot = resolve_slot(a, b);
+    float2 hraw[4][8];
+    if (slot >= 0) {
+        const float *H = a.S0 + ((size_t)slot * a.Hv + h) * D * D + 8 * grp * D + c;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                hraw[s][e] = ld_stream2(H + (32 * s + e) * D);
+    }
     int lo, N;
     int st = check_offsets(a, b, lo, N);
     if (st == GDN_TREE_S_BAD_OFFSETS) {
         if (h == 0 && tid == 0 && a.status) a.status[b] = st;
         return;
     }
-    const int slot = resolve_slot(a, b);
     const uint32_t krow = (uint32_t)a.Hk * D;   // q/k row stride (elements)
     const uint16_t *kbase = a.k + ((size_t)lo * a.Hk + hk) * D;
     const uint16_t *qbase = a.q + ((size_t)lo * a.Hk + hk) * D;
     const uint16_t *vbase = a.v + ((size_t)lo * a.Hv + h) * D;   // + 32-bit per-lane offsets
     const uint32_t vrow = (uint32_t)a.Hv * D;
 
-    // ---- issue the unit's global reads: per-node scalars, H0, v ----
+    // ---- issue the unit's remaining global reads: per-node scalars, v, K, Q ----
     int p_mine = -1;
     float g_mine = 0.f, b_mine = 0.f;
-    float2 hraw[4][8];
     uint32_t vv[4];   // v of the current K tile's rows (the next tile's come with its A fragments)
     // A fragments of the first K and Q tiles and the K rows of this wave's gram
     // columns are issued with H0; later tiles are fetched one tile ahead.
@@ -131,14 +141,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
         p_mine = a.parent[lo + tc];
         g_mine = a.g[gi];
         b_mine = a.beta[gi];
-        if (slot >= 0) {
-            const float *H = a.S0 + ((size_t)slot * a.Hv + h) * D * D + 8 * grp * D + c;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    hraw[s][e] = ld_stream2(H + (32 * s + e) * D);
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)   // rows past N read the last row; their R rows are never used
             vv[i] = *reinterpret_cast<const uint32_t *>(vbase + ((uint32_t)min(4 * grp + i, N - 1) * vrow + c));
