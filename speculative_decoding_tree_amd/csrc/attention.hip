@@ -150,21 +150,13 @@ __device__ __forceinline__ int nan_end(const AttnArgs &a, int rg, int R) {
     return rg == a.n_rg - 1 ? R : min(R, a.rows_wg * (rg + 1));
 }
 
+// One unit: query rows [ROWS rg, ROWS (rg + 1)) of (request b, kv-head hk)
+// against context part sp (and, for part 0, the draft nodes).  Ks / Vs are
+// the workgroup's LDS block; rot only varies which wave takes which rows.
 template <int TPW>
-__global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3 : 2))) void attn_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int sp, int rg, int rot, uint16_t *Ks,
+                                          uint16_t *Vs) {
     constexpr int ROWS = 64 * TPW;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[KB * D];
-
-    const int n_units = a.B * a.Hkv * a.n_split * a.n_rg;
-    const int unit = xcd_unit(blockIdx.x, n_units);
-    if (unit >= n_units) return;
-    const int rg = unit % a.n_rg;   // row groups of one (request, kv-head, split) are neighbours
-    int rest = unit / a.n_rg;
-    const int sp = rest % a.n_split;
-    rest /= a.n_split;
-    const int hk = rest % a.Hkv;
-    const int b = rest / a.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, grp = lane >> 4;
 
     int lo, N, c0, Lc;
@@ -187,9 +179,9 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3
     const int nblk = nctx + (sp == 0 ? 1 : 0);   // the draft nodes' own block goes with the first part
 
     // ---- this lane's query rows (MFMA B column n), one per tile ----
-    // Row slot wr of the group goes to wave (wr + unit) % 4, so that groups
+    // Row slot wr of the group goes to wave (wr + rot) % 4, so that groups
     // with a single slot do not all compute on the same wave slot.
-    const int wr = (w - unit) & 3;
+    const int wr = (w - rot) & 3;
     int t[TPW], g[TPW];
     bool rvalid[TPW], tact[TPW];   // tact: the tile has a valid row (wave-uniform)
     uint64_t anc_row[TPW];
@@ -415,6 +407,161 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3
     }
 }
 
+// One workgroup per unit: unit = ((b Hkv + hk) n_split + sp) n_rg + rg, the
+// row groups of one (request, kv-head, part) neighbours on one XCD.
+template <int TPW>
+__global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3 : 2))) void attn_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[KB * D];
+    const int n_units = a.B * a.Hkv * a.n_split * a.n_rg;
+    const int unit = xcd_unit(blockIdx.x, n_units);
+    if (unit >= n_units) return;
+    const int rg = unit % a.n_rg;
+    int rest = unit / a.n_rg;
+    const int sp = rest % a.n_split;
+    rest /= a.n_split;
+    attn_unit<TPW>(a, rest / a.Hkv, rest % a.Hkv, sp, rg, unit, Ks, Vs);
+}
+
+// ---- scheduled launch: a resident grid working through a sorted unit list ----
+// Units differ several-fold in length (context length, row groups), and
+// workgroups are dispatched in order, so a grid of one workgroup per unit
+// leaves compute units idle behind long units.  Instead a grid that fits on
+// the chip at once walks one list of the units that do work, sorted by length
+// (longest first) and dealt out boustrophedon: position k of round r goes to
+// column r G + k (even r) or r G + G - 1 - k (odd r), which balances the
+// workgroups' totals.  Columns are laid out so that neighbouring list
+// positions (the row groups of one request and kv-head) run on one XCD at the
+// same time and share its L2.  Every workgroup builds the same list in LDS.
+constexpr int SCHED_ITEMS = 1024;    // (request, context part) items the list can hold
+constexpr int SCHED_BUCKETS = 64;    // length classes of the counting sort
+
+struct AttnSched {
+    int item[SCHED_ITEMS];        // scheduled items in list order: item | row groups << 16
+    int first[SCHED_ITEMS + 1];   // list position of each scheduled item's first unit
+    int info[SCHED_ITEMS];        // per item: units | row groups << 12 | bucket << 20
+    int base[SCHED_BUCKETS + 1];  // bucket starts, then running positions
+    int n_live;
+};
+
+// Units of item (request b, context part sp), their row groups, and the
+// item's length (blocks it streams).  Parts that do nothing contribute no
+// unit; a request with bad offsets or no rows keeps one unit for its status.
+__device__ __forceinline__ void sched_item(const AttnArgs &a, int b, int sp, int &cnt, int &nrg, int &len) {
+    int lo, N, c0, Lc;
+    const int st = attn_request(a, b, lo, N, c0, Lc);
+    cnt = 0;
+    nrg = 0;
+    len = 0;
+    if (st == GDN_TREE_S_BAD_OFFSETS || N == 0) {
+        cnt = sp == 0 ? 1 : 0;
+        return;
+    }
+    if (sp > 0 && (st != GDN_TREE_S_OK || sp * a.split >= Lc)) return;
+    nrg = min(a.n_rg, (N * a.G + a.rows_wg - 1) / a.rows_wg);
+    cnt = a.Hkv * nrg;
+    if (st == GDN_TREE_S_OK) {
+        const int k0 = sp * a.split, k1 = min(Lc, k0 + a.split);
+        len = (k1 > k0 ? (k1 - k0 + KB - 1) / KB : 0) + (sp == 0 ? 1 : 0);
+    }
+}
+
+// Lanes of the wave whose b-bit value v equals this lane's (nbits ballots).
+__device__ __forceinline__ uint64_t same_value(int v, int nbits) {
+    uint64_t eq = __ballot(1);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const uint64_t bal = __ballot((v >> bit) & 1);
+        eq &= ((v >> bit) & 1) ? bal : ~bal;
+    }
+    return eq;
+}
+
+// Wave 0 builds the list: a stable counting sort of the items by length class
+// (longest first), then the prefix of their unit counts.
+__device__ void build_sched(const AttnArgs &a, AttnSched &sc) {
+    const int lane = threadIdx.x & 63;
+    const int n_items = a.B * a.n_split;
+    const int lmax = (min(a.split, a.max_ctx) + KB - 1) / KB + 1;
+    int shift = 0;
+    while ((lmax >> shift) >= SCHED_BUCKETS) ++shift;
+    const uint64_t below = (1ull << lane) - 1ull;
+    sc.base[lane] = 0;
+    if (lane == 0) sc.base[SCHED_BUCKETS] = 0;
+    for (int i0 = 0; i0 < n_items; i0 += 64) {   // classes and counts
+        const int i = i0 + lane;
+        int cnt = 0, nrg = 0, len = 0;
+        if (i < n_items) sched_item(a, i / a.n_split, i % a.n_split, cnt, nrg, len);
+        const int bk = cnt > 0 ? SCHED_BUCKETS - 1 - min(len >> shift, SCHED_BUCKETS - 1) : SCHED_BUCKETS;
+        if (i < n_items) sc.info[i] = cnt | (nrg << 12) | (bk << 20);
+        const uint64_t eq = same_value(bk, 7);
+        if ((eq & below) == 0ull && bk < SCHED_BUCKETS) sc.base[bk] += __popcll(eq);
+    }
+    int c = sc.base[lane];   // exclusive scan of the 64 class counts
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int up = __shfl_up(incl, off);
+        if (lane >= off) incl += up;
+    }
+    sc.base[lane] = incl - c;
+    if (lane == 63) sc.n_live = incl;
+    for (int i0 = 0; i0 < n_items; i0 += 64) {   // stable scatter
+        const int i = i0 + lane;
+        const int inf = i < n_items ? sc.info[i] : (SCHED_BUCKETS << 20);
+        const int bk = inf >> 20;
+        const uint64_t eq = same_value(bk, 7);
+        if (bk < SCHED_BUCKETS) {
+            const int pos = sc.base[bk] + __popcll(eq & below);
+            sc.item[pos] = i | (((inf >> 12) & 0xff) << 16);
+            sc.first[pos] = inf & 0xfff;   // unit count for now
+        }
+        if ((eq & below) == 0ull && bk < SCHED_BUCKETS) sc.base[bk] += __popcll(eq);
+    }
+    const int n_live = sc.n_live;
+    int carry = 0;   // unit counts -> exclusive prefix
+    for (int p0 = 0; p0 < n_live; p0 += 64) {
+        const int p = p0 + lane;
+        const int v = p < n_live ? sc.first[p] : 0;
+        int incl2 = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int up = __shfl_up(incl2, off);
+            if (lane >= off) incl2 += up;
+        }
+        if (p < n_live) sc.first[p] = carry + incl2 - v;
+        carry += __shfl(incl2, 63);
+    }
+    if (lane == 0) sc.first[n_live] = carry;
+}
+
+template <int TPW>
+__global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3 : 2))) void attn_sched_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[KB * D];
+    __shared__ AttnSched sc;
+    if ((threadIdx.x >> 6) == 0) build_sched(a, sc);
+    lds_barrier();
+    const int n_live = sc.n_live, total = sc.first[n_live];
+    const int G = gridDim.x;   // a multiple of 8
+    const int col = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);   // this workgroup's column
+    for (int r = 0;; ++r) {
+        const int k = r * G + ((r & 1) ? G - 1 - col : col);
+        if (k >= total) break;
+        int lo = 0, hi = n_live - 1;   // the scheduled item holding position k
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sc.first[mid] <= k) lo = mid;
+            else hi = mid - 1;
+        }
+        const int it = sc.item[lo] & 0xffff, nrg = sc.item[lo] >> 16, j = k - sc.first[lo];
+        const int b = it / a.n_split, sp = it - b * a.n_split;
+        const int hk = nrg > 0 ? j / nrg : 0, rg = nrg > 0 ? j - hk * nrg : 0;
+        attn_unit<TPW>(a, b, hk, sp, rg, k, Ks, Vs);
+        lds_barrier();   // every wave is done with the LDS block before the next unit stores into it
+    }
+}
+
+
 // Merge the context parts of each row: thread (row, part) owns 32 columns.
 __global__ __launch_bounds__(AT) void attn_merge_kernel(AttnArgs a) {
     const int unit = blockIdx.x;
@@ -481,12 +628,39 @@ hipError_t launch_ancestry(const Args &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+namespace {
+// Compute units of the current device (cached per device; 0 if unknown).
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+}  // namespace
+
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
     const int units = a.B * a.Hkv * a.n_split * a.n_rg;
-    if (a.rows_wg == 128)
+    // resident workgroups: two per CU for 128-row units (registers), three for 64-row ones
+    const int resident = (((a.rows_wg == 128 ? 2 : 3) * cu_count()) / 8) * 8;
+    // the list packs row groups in 8 bits and an item's unit count in 12
+    const bool sched = resident >= 8 && (long long)a.B * a.n_split <= SCHED_ITEMS && a.n_rg < 256 &&
+                       a.Hkv * a.n_rg < 4096;
+    if (sched) {
+        const int grid = min(resident, xcd_grid(units));
+        if (a.rows_wg == 128)
+            attn_sched_kernel<2><<<dim3(grid), dim3(AT), 0, stream>>>(a);
+        else
+            attn_sched_kernel<1><<<dim3(grid), dim3(AT), 0, stream>>>(a);
+    } else if (a.rows_wg == 128) {
         attn_kernel<2><<<dim3(xcd_grid(units)), dim3(AT), 0, stream>>>(a);
-    else
+    } else {
         attn_kernel<1><<<dim3(xcd_grid(units)), dim3(AT), 0, stream>>>(a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;
     attn_merge_kernel<<<dim3(a.B * a.Hkv * a.n_rg), dim3(AT), 0, stream>>>(a);

@@ -182,6 +182,37 @@ def test_attention_full_size_sampled(split):
     assert np.isfinite(out).all() and np.isfinite(lse).all()
 
 
+def _many_small_requests(B, seed):
+    """B requests of 0-3 draft nodes (chains or roots) over 0-130 context keys."""
+    rng = np.random.default_rng(seed)
+    parents, ctx = [], []
+    for b in range(B):
+        n = int(rng.integers(0, 4))
+        parents.append(W.chain(n) if rng.integers(0, 2) else np.full(n, -1, np.int32))
+        ctx.append(int(rng.integers(0, 131)))
+    return W.make_attn(parents, ctx, Hq=4, Hkv=2, seed=seed, name=f"attn_many{B}")
+
+
+def test_attention_more_requests_than_the_schedule_holds():
+    # 1100 (request, part) items exceed the in-LDS unit list: one workgroup per unit
+    wl = _many_small_requests(1100, 31)
+    out, lse, st, _ = run_attn(wl, max_nodes=4)
+    ref_out, ref_lse, ref_st = oracle_attn(wl, max_nodes=4)
+    assert np.array_equal(st, ref_st)
+    compare(wl, out, lse, ref_out, ref_lse, range(wl.B))
+
+
+def test_attention_scheduled_and_per_unit_launches_agree():
+    # one pass: 600 items, scheduled list; split 64: 600 x 3 items, one workgroup per unit
+    wl = _many_small_requests(600, 32)
+    o1, l1, s1, _ = run_attn(wl, max_nodes=4)
+    o2, l2, s2, _ = run_attn(wl, max_nodes=4, split=64)
+    ref_out, ref_lse, ref_st = oracle_attn(wl, max_nodes=4)
+    assert np.array_equal(s1, ref_st) and np.array_equal(s2, ref_st)
+    compare(wl, o1, l1, ref_out, ref_lse, range(wl.B))
+    compare(wl, o2, l2, ref_out, ref_lse, range(wl.B))
+
+
 def test_attention_deterministic():
     wl = W.make_attn_small(5)
     o1, l1, _, d = run_attn(wl, split=64)
