@@ -250,7 +250,7 @@ typedef struct gdn_tree_attn_dims {
     int32_t C;         /* total committed-context rows = ctx_offset[B] (>= 0) */
     int32_t max_nodes; /* per-request node cap (1..64) */
     int32_t max_ctx;   /* per-request context cap (0 .. 2^30) */
-    int32_t split;     /* context keys per workgroup (>= 1); split >= max_ctx = one pass, no workspace */
+    int32_t split;     /* context keys per workgroup (>= 1); split >= max_ctx = one pass, no merge */
 } gdn_tree_attn_dims;
 
 /*
@@ -271,11 +271,13 @@ typedef struct gdn_tree_attn_dims {
  *   anc_mask       uint64 [T] as written by gdn_tree_ancestry
  *   out            float32 [T][Hq][128];  lse float32 [T][Hq] (may be NULL)
  * When split < max_ctx the context is cut into ceil(max_ctx / split) parts
- * handled by separate workgroups and merged by a second launch; that needs a
- * caller-owned device workspace of gdn_tree_attention_workspace_bytes(dims)
- * bytes (16-byte aligned; contents need no initialisation).  Otherwise
- * workspace may be NULL.  q, k_ctx, v_ctx, k_node, v_node and out must be
- * 16-byte aligned.  scale must be finite and positive.  max_ctx * Hkv * 128
+ * handled by separate workgroups and merged by a second launch.  Every call
+ * with B > 0 needs a caller-owned device workspace of
+ * gdn_tree_attention_workspace_bytes(dims) bytes (16-byte aligned; contents
+ * need no initialisation): 256 bytes of work-distribution counters, which the
+ * call zeroes on the stream itself, followed, for a split context, by the
+ * parts' partial results.  Calls that share a workspace must not overlap.
+ * q, k_ctx, v_ctx, k_node, v_node and out must be 16-byte aligned.  scale must be finite and positive.  max_ctx * Hkv * 128
  * must stay below 2^31 (GDN_TREE_E_SIZE otherwise).
  * Device errors: bad node offsets (1) write nothing for the request; too
  * many nodes (2), a bad context range (7) or a malformed mask (8) give NaN
@@ -287,8 +289,8 @@ int gdn_tree_attention(const gdn_tree_attn_dims *dims, const uint16_t *q, const 
                        float scale, float *out, float *lse, void *workspace, size_t workspace_bytes,
                        int32_t *status, void *stream);
 
-/* Workspace bytes gdn_tree_attention needs for dims (0 when split >= max_ctx
- * or dims are invalid).  Host only. */
+/* Workspace bytes gdn_tree_attention needs for dims: 256 for one pass, more
+ * when split < max_ctx; 0 when B = 0 or dims are invalid.  Host only. */
 size_t gdn_tree_attention_workspace_bytes(const gdn_tree_attn_dims *dims);
 
 /*

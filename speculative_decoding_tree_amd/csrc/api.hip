@@ -77,10 +77,12 @@ int check_attn_dims(const gdn_tree_attn_dims *d, int &n_split, int &n_rg) {
     return GDN_TREE_OK;
 }
 
+// Scheduling counters, then (split context only) one partial record per unit.
 size_t attn_workspace(const gdn_tree_attn_dims *d, int n_split, int n_rg) {
-    if (n_split <= 1) return 0;
-    return (size_t)d->B * d->Hkv * n_split * n_rg * (size_t)attn_rows_wg(d) * (GDN_TREE_HEAD_DIM + 2) *
-           sizeof(float);
+    const size_t header = gdn::ATTN_WS_HEADER_BYTES;
+    if (n_split <= 1) return header;
+    return header + (size_t)d->B * d->Hkv * n_split * n_rg * (size_t)attn_rows_wg(d) * (GDN_TREE_HEAD_DIM + 2) *
+                        sizeof(float);
 }
 
 int finish(hipError_t e) { return e == hipSuccess ? GDN_TREE_OK : GDN_TREE_E_LAUNCH; }
@@ -329,7 +331,7 @@ int gdn_tree_attention(const gdn_tree_attn_dims *dims, const uint16_t *q, const 
     if (dims->C > 0 && (!k_ctx || !v_ctx)) return GDN_TREE_E_NULL;
     if (any_misaligned(q, k_ctx, v_ctx, k_node, v_node, out)) return GDN_TREE_E_ALIGN;
     const size_t need = attn_workspace(dims, n_split, n_rg);
-    if (need > 0 && (!workspace || misaligned(workspace) || workspace_bytes < need)) return GDN_TREE_E_WORKSPACE;
+    if (!workspace || misaligned(workspace) || workspace_bytes < need) return GDN_TREE_E_WORKSPACE;
     gdn::AttnArgs a = {};
     a.B = dims->B;
     a.Hq = dims->Hq;

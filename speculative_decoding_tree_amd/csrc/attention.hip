@@ -393,7 +393,8 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int 
                                                                         ot[tt][mt][2] * inv, ot[tt][mt][3] * inv);
             if (grp == 0 && a.lse) a.lse[orow] = (m[tt] + log2f(l[tt])) * LN2;
         } else {
-            float *rec = a.ws + ((((size_t)b * a.Hkv + hk) * a.n_split + sp) * a.n_rg + rg) * part_floats(ROWS);
+            float *rec = a.ws + ATTN_WS_HEADER_BYTES / 4 +
+                         ((((size_t)b * a.Hkv + hk) * a.n_split + sp) * a.n_rg + rg) * part_floats(ROWS);
             const int rl = 16 * (TPW * wr + tt) + n;
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
@@ -427,12 +428,15 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3
 // Units differ several-fold in length (context length, row groups), and
 // workgroups are dispatched in order, so a grid of one workgroup per unit
 // leaves compute units idle behind long units.  Instead a grid that fits on
-// the chip at once walks one list of the units that do work, sorted by length
-// (longest first) and dealt out boustrophedon: position k of round r goes to
-// column r G + k (even r) or r G + G - 1 - k (odd r), which balances the
-// workgroups' totals.  Columns are laid out so that neighbouring list
-// positions (the row groups of one request and kv-head) run on one XCD at the
-// same time and share its L2.  Every workgroup builds the same list in LDS.
+// the chip at once works through one list of the units that do work, sorted
+// by length (longest first; every workgroup builds the same list in LDS).
+// The list is cut into chunks of 64 positions dealt boustrophedon to eight
+// sub-lists (chunk i to sub-list i % 16 or 15 - i % 16), and the workgroups
+// with blockIdx % 8 = x (one XCD under round-robin dispatch) take positions of
+// sub-list x from a counter in the workspace, longest first, as they become
+// free: the deal balances the sub-lists, the counter absorbs the workgroups'
+// differing speeds, and neighbouring positions (the row groups of one request
+// and kv-head) run on one XCD at the same time and share its L2.
 constexpr int SCHED_ITEMS = 1024;    // (request, context part) items the list can hold
 constexpr int SCHED_BUCKETS = 64;    // length classes of the counting sort
 
@@ -541,11 +545,15 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3
     __shared__ AttnSched sc;
     if ((threadIdx.x >> 6) == 0) build_sched(a, sc);
     lds_barrier();
+    __shared__ int ticket;
     const int n_live = sc.n_live, total = sc.first[n_live];
-    const int G = gridDim.x;   // a multiple of 8
-    const int col = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);   // this workgroup's column
-    for (int r = 0;; ++r) {
-        const int k = r * G + ((r & 1) ? G - 1 - col : col);
+    const int x = blockIdx.x & 7;   // sub-list
+    int *counter = reinterpret_cast<int *>(a.ws) + x;
+    for (;;) {
+        if (threadIdx.x == 0) ticket = atomicAdd(counter, 1);
+        lds_barrier();
+        const int tk = ticket, chunk = tk >> 6;   // chunk-th chunk of sub-list x
+        const int k = 64 * (16 * (chunk >> 1) + ((chunk & 1) ? 15 - x : x)) + (tk & 63);
         if (k >= total) break;
         int lo = 0, hi = n_live - 1;   // the scheduled item holding position k
         while (lo < hi) {
@@ -557,8 +565,14 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3
         const int b = it / a.n_split, sp = it - b * a.n_split;
         const int hk = nrg > 0 ? j / nrg : 0, rg = nrg > 0 ? j - hk * nrg : 0;
         attn_unit<TPW>(a, b, hk, sp, rg, k, Ks, Vs);
-        lds_barrier();   // every wave is done with the LDS block before the next unit stores into it
+        lds_barrier();   // every wave is done with the LDS block (and the ticket) before the next unit
     }
+}
+
+// Zero the scheduling counters before a scheduled launch (a kernel rather than
+// a memset, so that the pair can be captured in a graph).
+__global__ void attn_reset_kernel(float *ws) {
+    if (threadIdx.x < 8) reinterpret_cast<int *>(ws)[threadIdx.x] = 0;
 }
 
 
@@ -592,7 +606,7 @@ __global__ __launch_bounds__(AT) void attn_merge_kernel(AttnArgs a) {
     float *op = a.out + orow * D + 32 * part;
     const int nparts = Lc > 0 ? (Lc + a.split - 1) / a.split : 1;
     const size_t stride = (size_t)a.n_rg * PART;   // between consecutive parts
-    const float *rec = a.ws + (((size_t)b * a.Hkv + hk) * a.n_split * a.n_rg + rg) * PART;
+    const float *rec = a.ws + ATTN_WS_HEADER_BYTES / 4 + (((size_t)b * a.Hkv + hk) * a.n_split * a.n_rg + rg) * PART;
     float M = -INFINITY;
     for (int s = 0; s < nparts; ++s) M = fmaxf(M, rec[s * stride + ROWS * D + rl]);
     float L = 0.f;
@@ -651,6 +665,7 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
     const bool sched = resident >= 8 && (long long)a.B * a.n_split <= SCHED_ITEMS && a.n_rg < 256 &&
                        a.Hkv * a.n_rg < 4096;
     if (sched) {
+        attn_reset_kernel<<<dim3(1), dim3(64), 0, stream>>>(a.ws);
         const int grid = min(resident, xcd_grid(units));
         if (a.rows_wg == 128)
             attn_sched_kernel<2><<<dim3(grid), dim3(AT), 0, stream>>>(a);

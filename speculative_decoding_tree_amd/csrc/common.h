@@ -10,6 +10,9 @@ namespace gdn {
 
 constexpr int D = GDN_TREE_HEAD_DIM;   // d_k = d_v = 128
 constexpr int MAXN = GDN_TREE_MAX_NODES;
+// Attention workspace: scheduling counters first, then the partial records of
+// a split context.
+constexpr int ATTN_WS_HEADER_BYTES = 256;
 
 // Plain-old-data argument block shared by every launcher.
 struct Args {

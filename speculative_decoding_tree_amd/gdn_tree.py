@@ -419,8 +419,9 @@ def attention_workspace_bytes(dims: AttnDims) -> int:
 def attention(q, k_ctx, v_ctx, ctx_offset, k_node, v_node, node_offset, anc_mask, scale: float,
               max_nodes: int, max_ctx: int, split: Optional[int] = None, out=None, lse=None, workspace=None,
               status=None, stream=None):
-    """gdn_tree_attention.  Returns (out, lse, status).  A workspace is allocated
-    when the context is split (split < max_ctx) and none is given."""
+    """gdn_tree_attention.  Returns (out, lse, status).  A workspace of
+    attention_workspace_bytes(dims) is allocated when none is given (work
+    distribution counters, plus partial results when split < max_ctx)."""
     B = int(node_offset.numel()) - 1
     T, Hq = int(q.shape[0]), int(q.shape[1])
     C, Hkv = int(k_ctx.shape[0]), int(k_ctx.shape[1])

@@ -151,8 +151,14 @@ def test_attention_host_validation_pointers_scale_workspace():
     assert L.gdn_tree_attention(ctypes.byref(d), *bad_align, ctypes.c_float(0.1), *tail) == -7
     split = G.make_attn_dims(4, 32, 8, 20, 100, 8, 50, split=16)      # 4 context parts -> workspace needed
     need = G.attention_workspace_bytes(split)
-    assert need == 4 * 8 * 4 * 1 * 64 * 130 * 4      # B, Hkv, 4 parts, 1 row group (8 nodes x 4 heads), rows, D+2 floats
+    # 256 bytes of scheduling counters, then B, Hkv, 4 parts, 1 row group (8 nodes x 4 heads), rows, D+2 floats
+    assert need == 256 + 4 * 8 * 4 * 1 * 64 * 130 * 4
     assert L.gdn_tree_attention(ctypes.byref(split), *good, ctypes.c_float(0.1), *tail) == -8
+    assert L.gdn_tree_attention(ctypes.byref(d), *good, ctypes.c_float(0.1), *tail) == -8   # one pass needs the counters too
+    short = [ok, ok, ok, ctypes.c_size_t(255), None, None]
+    assert L.gdn_tree_attention(ctypes.byref(d), *good, ctypes.c_float(0.1), *short) == -8
+    unaligned = [ok, ok, odd, ctypes.c_size_t(1 << 20), None, None]
+    assert L.gdn_tree_attention(ctypes.byref(d), *good, ctypes.c_float(0.1), *unaligned) == -8
     small = [ok, ok, ok, ctypes.c_size_t(need - 4), None, None]
     assert L.gdn_tree_attention(ctypes.byref(split), *good, ctypes.c_float(0.1), *small) == -8
     assert L.gdn_tree_ancestry(None, None, None, None, None, None) == -1
@@ -162,4 +168,5 @@ def test_attention_empty_batch_is_a_no_op():
     L = G.lib()
     d = G.make_attn_dims(0, 32, 8, 0, 0, 8, 0)
     assert L.gdn_tree_attention(ctypes.byref(d), *ATTN_NULLS) == 0
-    assert G.attention_workspace_bytes(G.make_attn_dims(4, 32, 8, 20, 100, 8, 50)) == 0   # one pass
+    assert G.attention_workspace_bytes(d) == 0                                            # nothing to do
+    assert G.attention_workspace_bytes(G.make_attn_dims(4, 32, 8, 20, 100, 8, 50)) == 256   # one pass: counters
