@@ -50,9 +50,12 @@ bool any_misaligned(Ps... ps) {
 // Query rows per attention workgroup: 128 (two 16-row tiles per wave, so each
 // K/V fragment read from LDS serves 32 rows) once a request can have more
 // than 64 rows, else 64.
-int attn_rows_wg(const gdn_tree_attn_dims *d) {
-    return (long long)d->max_nodes * (d->Hq / d->Hkv) > 64 ? 128 : 64;
-}
+// Query rows per attention workgroup.  64 (one 16-row tile per wave): with
+// the row groups of a request scheduled side by side on one XCD their shared
+// context reads meet in L2, and three such workgroups fit on a CU against two
+// of 128 rows (two tiles per wave); measured 811 -> 694 us on the batch-256
+// trees with 1k-4k contexts.
+int attn_rows_wg(const gdn_tree_attn_dims *) { return 64; }
 
 // Attention dims; also derives the launch shape.  Returns a GDN_TREE_* code.
 int check_attn_dims(const gdn_tree_attn_dims *d, int &n_split, int &n_rg) {

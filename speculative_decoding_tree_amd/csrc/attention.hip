@@ -658,21 +658,21 @@ int cu_count() {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
+    if (a.rows_wg != 64) return hipErrorInvalidValue;   // the host sizes units for one tile per wave
     const int units = a.B * a.Hkv * a.n_split * a.n_rg;
-    // resident workgroups: two per CU for 128-row units (registers), three for 64-row ones
-    const int resident = (((a.rows_wg == 128 ? 2 : 3) * cu_count()) / 8) * 8;
+    // resident workgroups: the runtime's occupancy (registers and LDS) times the CUs
+    static int occupancy = 0;
+    if (occupancy == 0 &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occupancy, attn_sched_kernel<1>, AT, 0) != hipSuccess)
+        occupancy = 0;
+    const int resident = ((occupancy * cu_count()) / 8) * 8;
     // the list packs row groups in 8 bits and an item's unit count in 12
     const bool sched = resident >= 8 && (long long)a.B * a.n_split <= SCHED_ITEMS && a.n_rg < 256 &&
                        a.Hkv * a.n_rg < 4096;
     if (sched) {
         attn_reset_kernel<<<dim3(1), dim3(64), 0, stream>>>(a.ws);
         const int grid = min(resident, xcd_grid(units));
-        if (a.rows_wg == 128)
-            attn_sched_kernel<2><<<dim3(grid), dim3(AT), 0, stream>>>(a);
-        else
-            attn_sched_kernel<1><<<dim3(grid), dim3(AT), 0, stream>>>(a);
-    } else if (a.rows_wg == 128) {
-        attn_kernel<2><<<dim3(xcd_grid(units)), dim3(AT), 0, stream>>>(a);
+        attn_sched_kernel<1><<<dim3(grid), dim3(AT), 0, stream>>>(a);
     } else {
         attn_kernel<1><<<dim3(xcd_grid(units)), dim3(AT), 0, stream>>>(a);
     }
