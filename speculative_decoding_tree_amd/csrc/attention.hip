@@ -150,6 +150,16 @@ __device__ __forceinline__ int nan_end(const AttnArgs &a, int rg, int R) {
     return rg == a.n_rg - 1 ? R : min(R, a.rows_wg * (rg + 1));
 }
 
+// The block loop of one unit.  KG waves share each 16-row tile, wave
+// (tile, group) taking keys [KB g / KG, KB (g + 1) / KG) of every block; the
+// groups' running (max, sum, O) are merged at the end through LDS.  KG = 1 is
+// the plain layout (one tile per wave, every key); units of one or two tiles
+// use KG = 4 or 2 so that no wave idles.
+template <int TPW, int KG>
+__device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int sp, int rg, int rot, uint16_t *Ks,
+                                          uint16_t *Vs, int lo, int N, int c0, int R, int row0, int k0, int k1,
+                                          int nctx, int nblk);
+
 // One unit: query rows [ROWS rg, ROWS (rg + 1)) of (request b, kv-head hk)
 // against context part sp (and, for part 0, the draft nodes).  Ks / Vs are
 // the workgroup's LDS block; rot only varies which wave takes which rows.
@@ -157,7 +167,7 @@ template <int TPW>
 __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int sp, int rg, int rot, uint16_t *Ks,
                                           uint16_t *Vs) {
     constexpr int ROWS = 64 * TPW;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, grp = lane >> 4;
+    const int tid = threadIdx.x;
 
     int lo, N, c0, Lc;
     int st = attn_request(a, b, lo, N, c0, Lc);
@@ -177,11 +187,33 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int 
     const int k1 = min(Lc, k0 + a.split);
     const int nctx = k1 > k0 ? (k1 - k0 + KB - 1) / KB : 0;
     const int nblk = nctx + (sp == 0 ? 1 : 0);   // the draft nodes' own block goes with the first part
+    const int tiles = (min(R - row0, ROWS) + 15) >> 4;
+    if (TPW == 1 && tiles == 1)
+        attn_body<TPW, 4>(a, b, hk, sp, rg, rot, Ks, Vs, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+    else if (TPW == 1 && tiles == 2)
+        attn_body<TPW, 2>(a, b, hk, sp, rg, rot, Ks, Vs, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+    else
+        attn_body<TPW, 1>(a, b, hk, sp, rg, rot, Ks, Vs, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+}
 
+template <int TPW, int KG>
+__device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int sp, int rg, int rot, uint16_t *Ks,
+                                          uint16_t *Vs, int lo, int N, int c0, int R, int row0, int k0, int k1,
+                                          int nctx, int nblk) {
+    constexpr int ROWS = 64 * TPW;
+    static_assert(KG == 1 || TPW == 1, "key groups split one tile per wave");
+    constexpr int NKT = 4 / KG;            // this wave's 16-key tiles per block
+    constexpr int NKS = NKT >= 2 ? NKT / 2 : 1;   // its 32-key value steps
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));   // lane values are recomputed per unit, not held across a resident loop
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), n = lane & 15, grp = lane >> 4;
+    const int G = a.G;
     // ---- this lane's query rows (MFMA B column n), one per tile ----
-    // Row slot wr of the group goes to wave (wr + rot) % 4, so that groups
-    // with a single slot do not all compute on the same wave slot.
-    const int wr = (w - rot) & 3;
+    // With KG = 1, row slot wr of the group goes to wave (wr + rot) % 4, so that
+    // groups with a single slot do not all compute on the same wave slot.
+    const int wr = KG > 1 ? w / KG : (w - rot) & 3;
+    const int kg = KG > 1 ? w % KG : 0;   // key group
+    const int kt_lo = kg * NKT;            // first 16-key tile of the block this wave takes
     int t[TPW], g[TPW];
     bool rvalid[TPW], tact[TPW];   // tact: the tile has a valid row (wave-uniform)
     uint64_t anc_row[TPW];
@@ -265,48 +297,49 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int 
         // scores S^T for keys 16 kt + 4 grp + i of row n (raw q.k); each K
         // fragment serves every tile of the wave; fragments of step
         // j = 4 kt + s are read KPF steps ahead
-        f32x4 sc[TPW][4];
+        f32x4 sc[TPW][NKT];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) sc[tt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < NKT; ++kt) sc[tt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         constexpr int KPF = 4;
         u32x4 kf[KPF];
-        auto kload = [&](int j) {   // row 16 kt + n, chunk 4 s + grp
-            kf[j % KPF] = *reinterpret_cast<const u32x4 *>(&Ks[k_at(16 * (j >> 2) + n, 4 * (j & 3) + grp)]);
+        auto kload = [&](int j) {   // row 16 (kt_lo + kt) + n, chunk 4 s + grp
+            kf[j % KPF] = *reinterpret_cast<const u32x4 *>(&Ks[k_at(16 * (kt_lo + (j >> 2)) + n, 4 * (j & 3) + grp)]);
         };
 #pragma unroll
         for (int j = 0; j < KPF; ++j) kload(j);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 4 * NKT; ++j) {
             const u32x4 k = kf[j % KPF];
-            if (j + KPF < 16) kload(j + KPF);
+            if (j + KPF < 4 * NKT) kload(j + KPF);
 #pragma unroll
             for (int tt = 0; tt < TPW; ++tt)
                 if (tt == 0 || tact[tt]) sc[tt][j >> 2] = mfma(k, qf[tt][j & 3], sc[tt][j >> 2]);
         }
 
         // softmax per tile; P in bf16 hi + lo as the B operand of the value product
-        u32x4 phi[TPW][2], plo[TPW][2];
+        u32x4 phi[TPW][NKS], plo[TPW][NKS];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
-            float x[4][4];
+            float x[NKT][4];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) x[kt][i] = sc[tt][kt][i];
             if (nodeb || rem < KB) {   // the last context block and the nodes' block: hide keys row n may not see
                 const uint64_t vis = nodeb ? anc_row[tt] : ((1ull << rem) - 1ull);
-                const uint64_t vl = vis >> (4 * grp);   // bit 16 kt + i: key 16 kt + 4 grp + i
+                // bit 16 kt + i: key 16 (kt_lo + kt) + 4 grp + i
+                const uint64_t vl = vis >> (4 * grp + 16 * kt_lo);
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
+                for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (!((vl >> (16 * kt + i)) & 1ull)) x[kt][i] = -INFINITY;
             }
             float mloc = -INFINITY;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, x[kt][i]);
             mloc *= a.scale_log2;   // the scale is positive: max commutes with it
@@ -324,21 +357,32 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int 
             }
             const float mneg = m[tt] == -INFINITY ? 0.f : -m[tt];   // nothing visible yet: p = 0
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     x[kt][i] = __builtin_amdgcn_exp2f(fmaf(x[kt][i], a.scale_log2, mneg));
                     l[tt] += x[kt][i];
                 }
+            if constexpr (NKT == 1) {
+                // one 16-key tile: the lower (even tile) or upper (odd tile)
+                // half of its 32-key value step; the other half of P is 0
+                uint32_t h0, l0, h1, l1;
+                split_bf16x2(x[0][0], x[0][1], h0, l0);
+                split_bf16x2(x[0][2], x[0][3], h1, l1);
+                const bool upper = kt_lo & 1;
+                phi[tt][0] = upper ? u32x4{0u, 0u, h0, h1} : u32x4{h0, h1, 0u, 0u};
+                plo[tt][0] = upper ? u32x4{0u, 0u, l0, l1} : u32x4{l0, l1, 0u, 0u};
+            } else {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-                split_bf16x2(x[2 * ks][0], x[2 * ks][1], h0, l0);
-                split_bf16x2(x[2 * ks][2], x[2 * ks][3], h1, l1);
-                split_bf16x2(x[2 * ks + 1][0], x[2 * ks + 1][1], h2, l2);
-                split_bf16x2(x[2 * ks + 1][2], x[2 * ks + 1][3], h3, l3);
-                phi[tt][ks] = u32x4{h0, h1, h2, h3};
-                plo[tt][ks] = u32x4{l0, l1, l2, l3};
+                for (int ks = 0; ks < NKS; ++ks) {
+                    uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+                    split_bf16x2(x[2 * ks][0], x[2 * ks][1], h0, l0);
+                    split_bf16x2(x[2 * ks][2], x[2 * ks][3], h1, l1);
+                    split_bf16x2(x[2 * ks + 1][0], x[2 * ks + 1][1], h2, l2);
+                    split_bf16x2(x[2 * ks + 1][2], x[2 * ks + 1][3], h3, l3);
+                    phi[tt][ks] = u32x4{h0, h1, h2, h3};
+                    plo[tt][ks] = u32x4{l0, l1, l2, l3};
+                }
             }
         }
 
@@ -352,7 +396,7 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int 
         // keys 32 ks + 16 h + 4 grp + e, e = 0..3 (k-slots 4h .. 4h+3)
         const int vsub = 4 * (n & 1);   // element offset inside the 16-byte chunk
         auto vload = [&](int j) {
-            const int ks = j >> 3, mt = j & 7;
+            const int ks = (kt_lo >> 1) + (j >> 3), mt = j & 7;
             const int c = 2 * mt + ((n & 3) >> 1);
             const int r0 = 32 * ks + 4 * grp + (n >> 2);
             const u32x2 va = lds_read_tr16(&Vs[v_at(r0, c) + vsub]);
@@ -362,9 +406,9 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int 
 #pragma unroll
         for (int j = 0; j < PF; ++j) vload(j);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 8 * NKS; ++j) {
             const u32x4 v = vf[j % PF];
-            if (j + PF < 16) vload(j + PF);
+            if (j + PF < 8 * NKS) vload(j + PF);
 #pragma unroll
             for (int tt = 0; tt < TPW; ++tt)
                 if (tt == 0 || tact[tt]) {
@@ -377,6 +421,51 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int 
     for (int tt = 0; tt < TPW; ++tt) {
         l[tt] += __shfl_xor(l[tt], 16);
         l[tt] += __shfl_xor(l[tt], 32);
+    }
+    if constexpr (KG > 1) {
+        // key groups 1 .. KG-1 of each tile leave (O, max, sum) in the LDS block
+        // (slot p = tile (KG - 1) + group - 1: 2048 floats of O laid out
+        // [mt][lane][4], then 128 floats of (max, sum) per slot after the
+        // third slot); group 0 merges them and writes the tile
+        lds_barrier();   // every wave is done with the last block
+        float *ob = reinterpret_cast<float *>(Ks);   // slots 0, 1
+        float *vb = reinterpret_cast<float *>(Vs);   // slot 2, then the (max, sum) pairs
+        auto slot_o = [&](int p) { return p < 2 ? ob + 2048 * p : vb; };
+        float2 *ml = reinterpret_cast<float2 *>(vb + 2048);
+        if (kg > 0) {
+            const int p = wr * (KG - 1) + kg - 1;
+            float *o = slot_o(p);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+                *reinterpret_cast<f32x4 *>(o + (mt * 64 + lane) * 4) = ot[0][mt];
+            ml[p * 64 + lane] = make_float2(m[0], l[0]);
+        }
+        lds_barrier();
+        if (kg == 0) {
+            float mm = m[0];
+#pragma unroll
+            for (int q = 1; q < KG; ++q) mm = fmaxf(mm, ml[(wr * (KG - 1) + q - 1) * 64 + lane].x);
+            const float fs = m[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[0] - mm);
+            l[0] *= fs;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) ot[0][mt] *= fs;
+#pragma unroll
+            for (int q = 1; q < KG; ++q) {
+                const int p = wr * (KG - 1) + q - 1;
+                const float2 pml = ml[p * 64 + lane];
+                const float f = pml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pml.x - mm);
+                l[0] += f * pml.y;
+                const float *o = slot_o(p);
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) {
+                    const f32x4 po = *reinterpret_cast<const f32x4 *>(o + (mt * 64 + lane) * 4);
+                    ot[0][mt] += f * po;
+                }
+            }
+            m[0] = mm;
+        } else {
+            rvalid[0] = false;   // group 0 writes the tile
+        }
     }
 
     // lane (n, grp) holds columns 16 mt + 4 grp .. +3 of its rows
