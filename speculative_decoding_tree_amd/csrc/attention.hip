@@ -665,7 +665,10 @@ __global__ void attn_reset_kernel(float *ws) {
 }
 
 
-// Merge the context parts of each row: thread (row, part) owns 32 columns.
+// Merge the context parts of each row: thread (row, quarter) owns 32 columns.
+// MAXP > 0: at most MAXP parts, every part's loads issued together; MAXP = 0:
+// any number of parts, one after another.
+template <int MAXP>
 __global__ __launch_bounds__(AT) void attn_merge_kernel(AttnArgs a) {
     const int unit = blockIdx.x;
     const int rg = unit % a.n_rg;
@@ -675,52 +678,67 @@ __global__ __launch_bounds__(AT) void attn_merge_kernel(AttnArgs a) {
     const int tid = threadIdx.x;
     int lo, N, c0, Lc;
     int st = attn_request(a, b, lo, N, c0, Lc);
-    st = check_masks(a, st, lo, N);
     if (st == GDN_TREE_S_BAD_OFFSETS) return;
     const int G = a.G;
     const int R = N * G;
     const int ROWS = a.rows_wg;
-    if (ROWS * rg >= R) return;
+    if (ROWS * rg >= R) return;   // a row group past the request's rows (decided before the mask vote)
+    st = check_masks(a, st, lo, N);
     if (st != GDN_TREE_S_OK) {
         nan_rows(a, lo, hk, ROWS * rg, nan_end(a, rg, R));
         return;
     }
-    const int part = tid & 3;
+    const int quarter = tid & 3;
     const size_t PART = part_floats(ROWS);
+    const int nparts = Lc > 0 ? (Lc + a.split - 1) / a.split : 1;
+    const size_t stride = (size_t)a.n_rg * PART;   // between consecutive parts
+    const float *rec = a.ws + ATTN_WS_HEADER_BYTES / 4 + (((size_t)b * a.Hkv + hk) * a.n_split * a.n_rg + rg) * PART;
   for (int rl = tid >> 2; rl < ROWS; rl += AT / 4) {
     const int r = ROWS * rg + rl;
     if (r >= R) break;
     const int t = r / G, g = r - t * G;
     const size_t orow = (size_t)(lo + t) * a.Hq + hk * G + g;
-    float *op = a.out + orow * D + 32 * part;
-    const int nparts = Lc > 0 ? (Lc + a.split - 1) / a.split : 1;
-    const size_t stride = (size_t)a.n_rg * PART;   // between consecutive parts
-    const float *rec = a.ws + ATTN_WS_HEADER_BYTES / 4 + (((size_t)b * a.Hkv + hk) * a.n_split * a.n_rg + rg) * PART;
-    float M = -INFINITY;
-    for (int s = 0; s < nparts; ++s) M = fmaxf(M, rec[s * stride + ROWS * D + rl]);
-    float L = 0.f;
-    float4 acc[8];
+    float *op = a.out + orow * D + 32 * quarter;
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < nparts; ++s) {
-        const float *rs = rec + s * stride;
-        const float wgt = __builtin_amdgcn_exp2f(rs[ROWS * D + rl] - M);
-        L += wgt * rs[ROWS * D + ROWS + rl];
-        const float4 *src = reinterpret_cast<const float4 *>(rs + rl * D + 32 * part);
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (MAXP > 0) {
+        float mp[MAXP], lp[MAXP];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4 v = src[i];
-            acc[i].x += wgt * v.x;
-            acc[i].y += wgt * v.y;
-            acc[i].z += wgt * v.z;
-            acc[i].w += wgt * v.w;
+        for (int s = 0; s < MAXP; ++s) {   // reads stay inside the request's parts (index clamped)
+            const size_t sp = (size_t)min(s, nparts - 1) * stride;
+            const float mv = rec[sp + ROWS * D + rl], lv = rec[sp + ROWS * D + ROWS + rl];
+            mp[s] = s < nparts ? mv : -INFINITY;
+            lp[s] = s < nparts ? lv : 0.f;
+            M = fmaxf(M, mp[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < MAXP; ++s) {
+            if (s < nparts) {
+                const float wgt = __builtin_amdgcn_exp2f(mp[s] - M);
+                L += wgt * lp[s];
+                const f32x4 *src = reinterpret_cast<const f32x4 *>(rec + (size_t)min(s, nparts - 1) * stride +
+                                                                   rl * D + 32 * quarter);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += wgt * src[i];
+            }
+        }
+    } else {
+        for (int s = 0; s < nparts; ++s) M = fmaxf(M, rec[s * stride + ROWS * D + rl]);
+        for (int s = 0; s < nparts; ++s) {
+            const float *rs = rec + s * stride;
+            const float wgt = __builtin_amdgcn_exp2f(rs[ROWS * D + rl] - M);
+            L += wgt * rs[ROWS * D + ROWS + rl];
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(rs + rl * D + 32 * quarter);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += wgt * src[i];
         }
     }
     const float inv = 1.f / L;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<float4 *>(op + 4 * i) = make_float4(acc[i].x * inv, acc[i].y * inv, acc[i].z * inv, acc[i].w * inv);
-    if (part == 0 && a.lse) a.lse[orow] = (M + log2f(L)) * LN2;
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4 *>(op + 4 * i) = acc[i] * inv;
+    if (quarter == 0 && a.lse) a.lse[orow] = (M + log2f(L)) * LN2;
   }
 }
 
@@ -767,7 +785,10 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;
-    attn_merge_kernel<<<dim3(a.B * a.Hkv * a.n_rg), dim3(AT), 0, stream>>>(a);
+    if (a.n_split <= 4)
+        attn_merge_kernel<4><<<dim3(a.B * a.Hkv * a.n_rg), dim3(AT), 0, stream>>>(a);
+    else
+        attn_merge_kernel<0><<<dim3(a.B * a.Hkv * a.n_rg), dim3(AT), 0, stream>>>(a);
     return hipGetLastError();
 }
 
