@@ -311,7 +311,21 @@ def batch_one_row(args, stream):
         G.commit(S0, U, k, g, off, par, path, plen, max_nodes=mn, S_out=S1, status=st, stream=stream)
 
     t = _time_launches(step, max(20, args.steps), stream)
-    return {"workload": "1 request, 6-node root-branch tree, Hv=32, Hk=16, d=128", "step_us": t}
+    # the same step captured once in a HIP graph and replayed (no per-launch host cost)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step(0)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        G.verify(S0, q, k, v, g, beta, off, par, max_nodes=mn, out=out, U=U, anc_mask=anc, status=st)
+        G.accepted_path(off, par, acc, max_nodes=mn, path=path, path_len=plen, status=st)
+        G.commit(S0, U, k, g, off, par, path, plen, max_nodes=mn, S_out=S1, status=st)
+    t_graph = _time_launches(lambda i: graph.replay(), max(20, args.steps), stream)
+    return {"workload": "1 request, 6-node root-branch tree, Hv=32, Hk=16, d=128", "step_us": t,
+            "graph_step_us": t_graph}
 
 
 def main():
