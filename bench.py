@@ -4,8 +4,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c4]
 
 One step = the whole hot path over one batch: gdn_tree_verify (outputs and
-pseudo-values of every draft node), gdn_tree_accepted_path and gdn_tree_commit
-(the accepted path's state, out of place so every step is identical).  Inputs
+pseudo-values of every draft node) and gdn_tree_commit_node (the accepted
+node's root-first path, written out, and the accepted path's state in one
+launch; out of place so every step is identical).  The same step with the
+path and the commit as two launches (gdn_tree_accepted_path, gdn_tree_commit)
+is timed under next_rows.  Inputs
 are seeded synthetic tensors already resident in HBM; three independent copies
 of every buffer are rotated so that no step finds the previous step's data in
 the 256 MB Infinity Cache.  Prints ONE JSON line on stdout.
@@ -193,11 +196,24 @@ def next_rows(args, wl, pools, mn, stream):
         G.accept_commit(p["S0"], p["U"], p["k"], p["g"], p["off"], p["par"], dt, tg, rt, max_nodes=mn,
                         S_out=p["S_out"], accept_node=acc, path=path, path_len=plen, status=st, stream=stream)
 
+    def path_only(i):
+        p = pools[i % len(pools)]
+        G.accepted_path(p["off"], p["par"], p["acc"], max_nodes=mn, path=path, path_len=plen, status=st,
+                        stream=stream)
+
+    def commit_only(i):
+        p = pools[i % len(pools)]
+        G.commit(p["S0"], p["U"], p["k"], p["g"], p["off"], p["par"], p["path"], p["plen"], max_nodes=mn,
+                 S_out=p["S_out"], status=st, stream=stream)
+
     def replay(i):
         p = pools[i % len(pools)]
         G.commit_replay(p["S0"], p["k"], p["v"], p["g"], p["beta"], p["off"], p["par"], p["path"], p["plen"],
                         max_nodes=mn, S_out=p["S_out"], status=st, stream=stream)
 
+    t_path = _time_launches(path_only, n, stream)
+    t_commit = _time_launches(commit_only, n, stream)
+    cb_step = commit_bytes(wl, pools[0]["plen"].cpu().numpy())
     t_greedy = _time_launches(greedy, n, stream)
     t_fused = _time_launches(fused, n, stream)
     L = plen.cpu().numpy()
@@ -218,7 +234,10 @@ def next_rows(args, wl, pools, mn, stream):
                         kept=kept, status=st, stream=stream)
 
     t_budget = _time_launches(budget, n, stream)
-    return {"budget_select": {"avg_us": t_budget, "budget": wl.T // 2, "nodes": wl.T},
+    return {"accepted_path_then_commit": {"accepted_path_avg_us": t_path, "commit_avg_us": t_commit,
+                                          "commit_alg_GBps": cb_step / (t_commit * 1e-6) / 1e9,
+                                          "commit_hbm_frac": cb_step / (t_commit * 1e-6) / 1e9 / HBM_PEAK_GBS},
+            "budget_select": {"avg_us": t_budget, "budget": wl.T // 2, "nodes": wl.T},
             "commit_replay": {"avg_us": t_replay, "alg_bytes": rb, "alg_GBps": rb / (t_replay * 1e-6) / 1e9,
                               "hbm_frac": rb / (t_replay * 1e-6) / 1e9 / HBM_PEAK_GBS,
                               "mean_accepted_len": float(Lr.mean())},
@@ -282,7 +301,7 @@ def attention_row(args, stream):
 
 
 def batch_one_row(args, stream):
-    """Latency of one verify + accepted-path + commit step at batch one: the
+    """Latency of one verify + commit_node step at batch one: the
     6-node root-branch tree of one request, 32 value / 16 key heads (the
     shape of the batch-one decode gate the pages report)."""
     import numpy as np
@@ -307,8 +326,8 @@ def batch_one_row(args, stream):
 
     def step(i):
         G.verify(S0, q, k, v, g, beta, off, par, max_nodes=mn, out=out, U=U, anc_mask=anc, status=st, stream=stream)
-        G.accepted_path(off, par, acc, max_nodes=mn, path=path, path_len=plen, status=st, stream=stream)
-        G.commit(S0, U, k, g, off, par, path, plen, max_nodes=mn, S_out=S1, status=st, stream=stream)
+        G.commit_node(S0, U, k, g, off, par, acc, max_nodes=mn, S_out=S1, path=path, path_len=plen, status=st,
+                      stream=stream)
 
     t = _time_launches(step, max(20, args.steps), stream)
     # the same step captured once in a HIP graph and replayed (no per-launch host cost)
@@ -321,8 +340,7 @@ def batch_one_row(args, stream):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         G.verify(S0, q, k, v, g, beta, off, par, max_nodes=mn, out=out, U=U, anc_mask=anc, status=st)
-        G.accepted_path(off, par, acc, max_nodes=mn, path=path, path_len=plen, status=st)
-        G.commit(S0, U, k, g, off, par, path, plen, max_nodes=mn, S_out=S1, status=st)
+        G.commit_node(S0, U, k, g, off, par, acc, max_nodes=mn, S_out=S1, path=path, path_len=plen, status=st)
     t_graph = _time_launches(lambda i: graph.replay(), max(20, args.steps), stream)
     return {"workload": "1 request, 6-node root-branch tree, Hv=32, Hk=16, d=128", "step_us": t,
             "graph_step_us": t_graph}
@@ -395,14 +413,10 @@ def main():
                  out=p["out"], U=p["U"], anc_mask=p["anc"], status=p["status"], stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        G.accepted_path(p["off"], p["par"], p["acc"], max_nodes=mn, path=p["path"], path_len=p["plen"],
-                        status=p["pst"], stream=stream)
+        G.commit_node(p["S0"], p["U"], p["k"], p["g"], p["off"], p["par"], p["acc"], max_nodes=mn,
+                      S_out=p["S_out"], path=p["path"], path_len=p["plen"], status=p["cst"], stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        G.commit(p["S0"], p["U"], p["k"], p["g"], p["off"], p["par"], p["path"], p["plen"], max_nodes=mn,
-                 S_out=p["S_out"], status=p["cst"], stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
 
     for i in range(args.warmup):
         step(pools[i % len(pools)])
@@ -424,14 +438,13 @@ def main():
     ms_step = ms_total / args.steps
 
     # per-kernel durations: events around each launch (separate pass, same steps)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(pools[i % len(pools)], evs[i])
     torch.cuda.synchronize()
     t_ver = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3     # us
-    t_path = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
-    t_com = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    t_com = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
 
     vb, cb = verify_bytes(wl), commit_bytes(wl, path_len)
     vf = verify_flops(wl)
@@ -446,15 +459,13 @@ def main():
             d["TFLOPs"] = flops / (t.mean() * 1e-6) / 1e12
         return d
 
-    kernels = {"gdn_tree_verify": kstats(t_ver, vb, vf), "gdn_tree_accepted_path": kstats(t_path, 0),
-               "gdn_tree_commit": kstats(t_com, cb)}
-    kernels["gdn_tree_accepted_path"].pop("hbm_frac")
-    dom = max(("gdn_tree_verify", "gdn_tree_commit"), key=lambda k: kernels[k]["avg_us"])
+    kernels = {"gdn_tree_verify": kstats(t_ver, vb, vf), "gdn_tree_commit_node": kstats(t_com, cb)}
+    dom = max(("gdn_tree_verify", "gdn_tree_commit_node"), key=lambda k: kernels[k]["avg_us"])
     ach = kernels[dom]["alg_GBps"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name, dom),
                 "alg_bytes_per_launch": kernels[dom]["alg_bytes"]}
-    for kname in ("gdn_tree_verify", "gdn_tree_commit"):
+    for kname in ("gdn_tree_verify", "gdn_tree_commit_node"):
         kernels[kname]["hbm_traffic_bytes"] = measured_traffic(wl.name, kname)
 
     nodes_per_s = wl.T / (ms_step * 1e-3)

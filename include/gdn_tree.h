@@ -194,6 +194,24 @@ int gdn_tree_accept_greedy(const gdn_tree_dims *dims, const int32_t *node_offset
                            int32_t *path_len, int32_t *status, void *stream);
 
 /*
+ * gdn_tree_commit_node -- gdn_tree_accepted_path fused with gdn_tree_commit,
+ * in one launch: each (request, v-head) workgroup derives the root-first path
+ * of accept_node[b] (int32 [B], request-local, -1 = nothing accepted) in one
+ * wave while its H0 is being read, then composes that path's pseudo-values
+ * into S_out exactly as gdn_tree_commit does (TreeWY, "Method": only the
+ * accepted path is composed into the next state).  path [B][max_nodes] and
+ * path_len [B] are optional outputs (NULL = not written), identical to what
+ * gdn_tree_accepted_path writes.  Device errors: bad offsets (1), bad parent
+ * (3), bad slot (4), accept_node outside [-1, N_b) (5); the request's S_out
+ * is then a copy of S0 (nothing is written where the slot is bad), and its
+ * path is empty.
+ */
+int gdn_tree_commit_node(const gdn_tree_dims *dims, const float *S0, float *S_out,
+                         const int32_t *state_slot, const float *U, const uint16_t *k, const float *g,
+                         const int32_t *node_offset, const int32_t *parent, const int32_t *accept_node,
+                         int32_t *path, int32_t *path_len, int32_t *status, void *stream);
+
+/*
  * gdn_tree_accept_commit -- greedy acceptance fused with the commit, in one
  * launch: each (request, v-head) workgroup repeats the greedy walk of
  * gdn_tree_accept_greedy (one wave, no host round trip) and composes that

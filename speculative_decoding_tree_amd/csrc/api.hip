@@ -277,6 +277,32 @@ int gdn_tree_accept_commit(const gdn_tree_dims *dims, const float *S0, float *S_
     return finish(gdn::launch_accept_commit(a, (hipStream_t)stream));
 }
 
+int gdn_tree_commit_node(const gdn_tree_dims *dims, const float *S0, float *S_out, const int32_t *state_slot,
+                         const float *U, const uint16_t *k, const float *g, const int32_t *node_offset,
+                         const int32_t *parent, const int32_t *accept_node, int32_t *path, int32_t *path_len,
+                         int32_t *status, void *stream) {
+    int rc = check_dims(dims);
+    if (rc != GDN_TREE_OK || dims->B == 0) return rc;
+    if (!S0 || !S_out || !node_offset || !accept_node) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && (!U || !k || !g || !parent)) return GDN_TREE_E_NULL;
+    if (any_misaligned(S0, S_out, U, k)) return GDN_TREE_E_ALIGN;
+    Args a = base_args(dims);
+    a.S0 = S0;
+    a.S_out = S_out;
+    a.state_slot = state_slot;
+    a.U = const_cast<float *>(U);
+    a.k = k;
+    a.g = g;
+    a.node_offset = node_offset;
+    a.parent = parent;
+    a.accept_node = accept_node;
+    a.path_out = path;
+    a.path_len_out = path_len;
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_commit_node(a, (hipStream_t)stream));
+}
+
 int gdn_tree_budget_select(const gdn_tree_dims *dims, const int32_t *node_offset, const int32_t *parent,
                            const float *accept_prob, int32_t budget, float threshold, float *survival,
                            uint8_t *keep, int32_t *kept, int32_t *status, void *stream) {

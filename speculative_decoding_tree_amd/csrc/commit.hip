@@ -53,11 +53,33 @@ __device__ __forceinline__ int path_entry(uint64_t pm, int lane) {
 constexpr int NT = 256;
 constexpr int KCHUNK = 16;   // path rows staged per pass
 
+// Where the accepted path comes from: the caller (a root-first path), the
+// greedy walk over token ids, or the accepted node (its root-first ancestors).
+enum PathSource { PATH_GIVEN = 0, PATH_GREEDY = 1, PATH_FROM_NODE = 2 };
+
+// Inclusive ancestor set of node acc (lane t = node t, parents validated), by
+// pointer doubling over shuffles; 0 for acc = -1.
+__device__ __forceinline__ uint64_t ancestors_of(int lane, int N, int p, int acc) {
+    const bool live = lane < N;
+    int jp = live ? p : -1;
+    uint64_t m = live ? (1ull << lane) : 0ull;
+    while (__ballot(jp >= 0)) {
+        const int src = jp >= 0 ? jp : lane;
+        const uint64_t m_up = __shfl(m, src);
+        const int jp_up = __shfl(jp, src);
+        if (jp >= 0) {
+            m |= m_up;
+            jp = jp_up;
+        }
+    }
+    return acc >= 0 ? __shfl(m, acc) : 0ull;
+}
+
 // The unit's 64 KiB of H0 is requested first (it depends only on the slot);
-// wave 0 then validates parents and the path with ballots, and turns the path
-// gates into decay coefficients with a suffix scan over shuffles, while those
-// loads are in flight.
-template <bool GREEDY>
+// wave 0 then validates parents and the path with ballots (or derives the
+// path), and turns the path gates into decay coefficients with a suffix scan
+// over shuffles, while those loads are in flight.
+template <int SRC>
 __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
     __shared__ float s_k[KCHUNK][D];   // D_aj * k_j rows of the current chunk
     __shared__ float s_coef[MAXN];
@@ -97,18 +119,22 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
         if (st == GDN_TREE_S_OK && slot < 0) st = GDN_TREE_S_BAD_SLOT;
         bool have_path = false;
         int pj = 0;
-        if (GREEDY) {
+        if (SRC != PATH_GIVEN) {
             int accept = -1;
             uint64_t pm = 0;
+            if (SRC == PATH_FROM_NODE && st == GDN_TREE_S_OK) {
+                accept = a.accept_node[b];
+                if (accept < -1 || accept >= N) st = GDN_TREE_S_BAD_ACCEPT;
+            }
             if (st == GDN_TREE_S_OK) {
                 const int p = lane < N ? a.parent[lo + lane] : -1;
-                pm = greedy_walk(a, b, lo, N, lane, p, accept);
+                pm = SRC == PATH_GREEDY ? greedy_walk(a, b, lo, N, lane, p, accept) : ancestors_of(lane, N, p, accept);
                 L = __popcll(pm);
                 pj = path_entry(pm, lane);
                 have_path = true;
             }
             if (h == 0) {   // one head publishes the decision
-                if (a.accept_out && lane == 0) a.accept_out[b] = accept;
+                if (SRC == PATH_GREEDY && a.accept_out && lane == 0) a.accept_out[b] = accept;
                 if (a.path_out) {
                     int32_t *row = a.path_out + (size_t)b * a.max_nodes;
                     if (lane < L) row[lane] = pj;
@@ -376,13 +402,18 @@ __global__ __launch_bounds__(NT) void replay_kernel(Args a) {
 
 }  // namespace
 
+hipError_t launch_commit_node(const Args &a, hipStream_t stream) {
+    commit_kernel<PATH_FROM_NODE><<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
 hipError_t launch_commit(const Args &a, hipStream_t stream) {
-    commit_kernel<false><<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
+    commit_kernel<PATH_GIVEN><<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_accept_commit(const Args &a, hipStream_t stream) {
-    commit_kernel<true><<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
+    commit_kernel<PATH_GREEDY><<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ hipError_t launch_commit(const Args &a, hipStream_t stream);
 hipError_t launch_accepted_path(const Args &a, hipStream_t stream);
 hipError_t launch_accept_greedy(const Args &a, hipStream_t stream);
 hipError_t launch_accept_commit(const Args &a, hipStream_t stream);
+hipError_t launch_commit_node(const Args &a, hipStream_t stream);
 hipError_t launch_commit_replay(const Args &a, hipStream_t stream);
 hipError_t launch_budget_select(const Args &a, int budget, float threshold, hipStream_t stream);
 hipError_t launch_ancestry(const Args &a, hipStream_t stream);

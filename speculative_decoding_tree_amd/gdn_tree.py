@@ -67,6 +67,7 @@ _SIGS = {
     "gdn_tree_commit_storeall": [ctypes.POINTER(Dims)] + [_P] * 9,
     "gdn_tree_accept_greedy": [ctypes.POINTER(Dims)] + [_P] * 10,
     "gdn_tree_accept_commit": [ctypes.POINTER(Dims)] + [_P] * 16,
+    "gdn_tree_commit_node": [ctypes.POINTER(Dims)] + [_P] * 13,
     "gdn_tree_commit_replay": [ctypes.POINTER(Dims)] + [_P] * 13,
     "gdn_tree_budget_select": [ctypes.POINTER(Dims), _P, _P, _P, ctypes.c_int32, ctypes.c_float,
                                _P, _P, _P, _P, _P],
@@ -344,6 +345,36 @@ def accept_commit(S0, U, k, g, node_offset, parent, draft_token, target_token, r
         _ptr(path_len, "path_len", _I32, (B,)), _ptr(status, "status", _I32, (B,)), _stream(stream))
     _check("gdn_tree_accept_commit", rc)
     return S_out, accept_node, path, path_len, status
+
+
+def commit_node(S0, U, k, g, node_offset, parent, accept_node, max_nodes: int, S_out=None, state_slot=None,
+                path=None, path_len=None, status=None, stream=None):
+    """gdn_tree_commit_node (the accepted node's path and the commit in one launch).
+    Returns (S_out, path, path_len, status); the outputs are allocated unless given."""
+    n_slots, Hv = int(S0.shape[0]), int(S0.shape[1])
+    B = int(node_offset.numel()) - 1
+    T = int(parent.numel())
+    Hk = int(k.shape[1])
+    dev = S0.device
+    mk = lambda shape: torch.empty(shape, dtype=torch.int32, device=dev)
+    S_out = S_out if S_out is not None else torch.empty_like(S0)
+    path = path if path is not None else mk((B, max_nodes))
+    path_len = path_len if path_len is not None else mk((B,))
+    status = status if status is not None else mk((B,))
+    dims = make_dims(B, Hv, Hk, T, max_nodes, n_slots)
+    rc = lib().gdn_tree_commit_node(
+        ctypes.byref(dims),
+        _ptr(S0, "S0", _F32, (n_slots, Hv, HEAD_DIM, HEAD_DIM)),
+        _ptr(S_out, "S_out", _F32, (n_slots, Hv, HEAD_DIM, HEAD_DIM)),
+        _ptr(state_slot, "state_slot", _I32, (B,)),
+        _ptr(U, "U", _F32, (T, Hv, HEAD_DIM)), _ptr(k, "k", _B16, (T, Hk, HEAD_DIM)),
+        _ptr(g, "g", _F32, (T, Hv)),
+        _ptr(node_offset, "node_offset", _I32, (B + 1,)), _ptr(parent, "parent", _I32, (T,)),
+        _ptr(accept_node, "accept_node", _I32, (B,)),
+        _ptr(path, "path", _I32, (B, max_nodes)), _ptr(path_len, "path_len", _I32, (B,)),
+        _ptr(status, "status", _I32, (B,)), _stream(stream))
+    _check("gdn_tree_commit_node", rc)
+    return S_out, path, path_len, status
 
 
 def commit_replay(S0, k, v, g, beta, node_offset, parent, path, path_len, max_nodes: int, S_out=None,

@@ -14,7 +14,7 @@ def test_library_exports_every_declared_symbol():
     names = G.declared_symbols()
     assert {"gdn_tree_verify", "gdn_tree_commit", "gdn_tree_accepted_path", "gdn_tree_verify_storeall",
             "gdn_tree_commit_storeall", "gdn_tree_state_bytes", "gdn_tree_strerror",
-            "gdn_tree_abi_version", "gdn_tree_accept_greedy", "gdn_tree_accept_commit", "gdn_tree_commit_replay", "gdn_tree_budget_select",
+            "gdn_tree_abi_version", "gdn_tree_accept_greedy", "gdn_tree_accept_commit", "gdn_tree_commit_node", "gdn_tree_commit_replay", "gdn_tree_budget_select",
             "gdn_tree_ancestry", "gdn_tree_attention", "gdn_tree_attention_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -170,3 +170,21 @@ def test_attention_empty_batch_is_a_no_op():
     assert L.gdn_tree_attention(ctypes.byref(d), *ATTN_NULLS) == 0
     assert G.attention_workspace_bytes(d) == 0                                            # nothing to do
     assert G.attention_workspace_bytes(G.make_attn_dims(4, 32, 8, 20, 100, 8, 50)) == 256   # one pass: counters
+
+
+def test_commit_node_host_validation():
+    L = G.lib()
+    d = G.make_dims(2, 4, 2, 6, 8, 2)
+    nulls = [None] * 12
+    assert L.gdn_tree_commit_node(None, *nulls, None) == -1
+    assert L.gdn_tree_commit_node(ctypes.byref(d), *nulls, None) == -1
+    ok, odd = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10004)
+    # S0, S_out, state_slot, U, k, g, node_offset, parent, accept_node, path, path_len, status, stream
+    args = [ok, ok, None, ok, ok, ok, ok, ok, None, None, None, None, None]   # accept_node missing
+    assert L.gdn_tree_commit_node(ctypes.byref(d), *args) == -1
+    args = [ok, ok, None, odd, ok, ok, ok, ok, ok, None, None, None, None]    # U misaligned
+    assert L.gdn_tree_commit_node(ctypes.byref(d), *args) == -7
+    bad = G.make_dims(2, 4, 2, 6, 65, 2)
+    assert L.gdn_tree_commit_node(ctypes.byref(bad), *args) == -4
+    empty = G.make_dims(0, 4, 2, 0, 8, 2)
+    assert L.gdn_tree_commit_node(ctypes.byref(empty), *nulls, None) == 0

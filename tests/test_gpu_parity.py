@@ -344,6 +344,44 @@ def test_fused_accept_commit_full_batch():
             assert matwise_rel_err(S1h[b, h][None], want[None]) <= TOL
 
 
+@pytest.mark.parametrize("name", ["c3_b16", "mixed_small", "deep_chain64", "forest_empty_single"])
+def test_commit_node_equals_accepted_path_then_commit(name):
+    """The fused launch derives the same path and writes the same state, bit for bit."""
+    wl = SMALL[name]()
+    mn = _mn(wl)
+    d = upload(wl)
+    _, U, _, _ = G.verify(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"], d["parent"],
+                          max_nodes=mn)
+    path, plen, pst = G.accepted_path(d["node_offset"], d["parent"], d["accept_node"], max_nodes=mn)
+    S_ref, cst = G.commit(d["S0"], U, d["k"], d["g"], d["node_offset"], d["parent"], path, plen, max_nodes=mn)
+    S1, path1, plen1, st1 = G.commit_node(d["S0"], U, d["k"], d["g"], d["node_offset"], d["parent"],
+                                          d["accept_node"], max_nodes=mn)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(S1), host(S_ref))
+    assert np.array_equal(host(path1), host(path)) and np.array_equal(host(plen1), host(plen))
+    assert np.array_equal(host(st1), host(cst))
+    po, plo, _ = O.accepted_path_batch(wl.node_offset, wl.parent, wl.accept_node, max_nodes=mn)
+    assert np.array_equal(host(path1), po) and np.array_equal(host(plen1), plo)
+
+
+def test_commit_node_bad_accept_node_keeps_S0():
+    wl = W.make_c3(4)
+    mn = wl.max_nodes
+    d = upload(wl)
+    _, U, _, _ = G.verify(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"], d["parent"],
+                          max_nodes=mn)
+    acc = torch.tensor([2, 6, -2, -1], dtype=torch.int32, device=d["S0"].device)   # 6 and -2 are out of range
+    S1, path, plen, st = G.commit_node(d["S0"], U, d["k"], d["g"], d["node_offset"], d["parent"], acc,
+                                       max_nodes=mn)
+    torch.cuda.synchronize()
+    st, S1h, S0h = host(st), host(S1), wl.S0
+    assert list(st) == [O.STATUS_OK, O.STATUS_BAD_ACCEPT, O.STATUS_BAD_ACCEPT, O.STATUS_OK]
+    for b in (1, 2, 3):                                   # bad node, bad node, nothing accepted: S' = S0
+        assert np.array_equal(S1h[b], S0h[b])
+    assert list(host(plen)) == [3, 0, 0, 0]
+    assert (host(path)[1:] == 0).all()
+
+
 # ----------------------------------------------------------------------------
 # replay commit (no pseudo-values)
 # ----------------------------------------------------------------------------
