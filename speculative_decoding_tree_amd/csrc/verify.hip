@@ -8,14 +8,13 @@
 // with anc*(t) the inclusive ancestors, G_t = sum of g over anc*(t),
 // gamma_t = exp(G_t), D_tj = exp(G_t - G_j) and H0 = S0^T ([d_k][d_v]):
 //
-//   [W; Z] = [K; Q] H0,   [KK; QK] = [K; Q] K^T                (one MFMA pass)
+//   [W; Z] = [K; Q] H0,   [KK; QK] = [K; Q] K^T                (MFMA)
 //   R_t = beta_t (v_t - gamma_t W_t)
 //   u_t = R_t - sum_{j in anc(t)} beta_t D_tj KK_tj u_j           (level by level)
 //   o_t = gamma_t Z_t + sum_{j in anc*(t)} D_tj QK_tj u_j
 //
 // The tree pre-pass (ancestry bitsets, G, depth levels) runs in wave 0 on
-// registers with pointer doubling and ballots while the other waves start
-// their MFMAs.
+// registers with pointer doubling and ballots while the state is in flight.
 //
 // gfx950 layout.  One workgroup (4 wave64) owns one (request, v-head) unit.
 // Wave w keeps its 128 x 32 column slab of H0 in registers as the B operand
@@ -23,16 +22,24 @@
 // exact bf16, so two MFMAs with fp32 accumulation carry ~16 mantissa bits of
 // H0).  Lane (n, grp) of the wave loads float2 columns 32w + 2n, 2n+1 of rows
 // 32s + 8grp .. +7; the even columns form n-tile 0 and the odd ones n-tile 1,
-// so every load instruction reads whole 128-byte row segments.  A operands
-// (16-node tiles of K or Q rows) come from L2, fetched one tile ahead, the
-// first ones together with H0.  One MFMA pass over
-// the tiles gives W = K H0 (turned into R in LDS at once), Z = Q H0 (kept in
-// registers until the outputs) and, in wave w, the grams against K^T for node
-// columns 16w .. 16w+15, whose ancestor entries are scaled on the spot into a
-// coefficient table.  That pass ends with the only workgroup barrier after
-// the tree pre-pass: the solve and the outputs are independent per column,
-// so each wave finishes its own 32 columns alone (LDS operations of one wave
-// complete in order, so one level's writes are seen by the next level).
+// so every load instruction reads whole 128-byte row segments.
+//
+// Loads.  Under full load a global round trip costs microseconds, so a unit
+// makes one: after the node offsets, every wave requests its share of the
+// unit's Q and K rows (staged in LDS) and its v elements, then its H0 slab;
+// wave 0 requests the per-node scalars first.  Loads retire in order, so the
+// tree pre-pass waits for the scalars and the staged rows but not for H0.
+// The staged rows (bf16, XOR-swizzled 16-byte chunks) occupy the R/U area,
+// which holds nothing until R is written: Q rows at its start, K rows at its
+// end.  Then, from LDS: the grams against K^T for node columns 16w .. 16w+15
+// (ancestor entries scaled on the spot into a coefficient table), the Q pass
+// (Z = Q H0 kept in registers, P entries), a barrier (the Q rows are dead),
+// and the K pass (W = K H0, turned into R in place; an R tile that covers
+// staged K rows is written after a barrier, and it only ever covers rows of
+// tiles already read).  After the K pass the solve and the outputs are
+// independent per column, so each wave finishes its own 32 columns alone (LDS
+// operations of one wave complete in order, so one level's writes are seen
+// by the next level).
 #include "common.h"
 #include "launch.h"
 #include "mfma.h"
@@ -51,11 +58,11 @@ constexpr int NT = 256;
 //                             output product (P masked) U)
 template <int NM>
 struct VerifySmem {
-    float ru[NM][D + 4];                       // R, then U after the solve
+    float ru[NM][D + 4];                       // staged Q and K rows, then R, then U after the solve
     float T[NM][NM + 4];
     __attribute__((aligned(16))) uint64_t anc[NM];
     __attribute__((aligned(16))) float gam[NM];
-    __attribute__((aligned(16))) float beta[NM];
+    __attribute__((aligned(16))) float beta[64];   // one per wave-0 lane (clamped copies past N)
     __attribute__((aligned(16))) float G2[NM];   // log2(e) * path-cumulative log-decay
     __attribute__((aligned(16))) int dep[NM];
     int lvl_nodes[NM], lvl_start[NM + 2];
@@ -66,30 +73,32 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// A fragment of a 16-node tile: lane (n, grp) gets row `row`, elements
-// 32 s + 8 grp .. +7 for s = 0..3 (16 bytes each); zero past the last node.
-// `base` is the same for the whole workgroup and the per-lane part is a
-// 32-bit byte offset, so the address needs no 64-bit vector registers.
-__device__ __forceinline__ void load_rows(const uint16_t *base, uint32_t row_stride, int row, int nrows,
-                                          int grp, u32x4 (&f)[4]) {
-    if (row < nrows) {
-        const uint32_t off = ((uint32_t)row * row_stride + 8u * grp) * 2u;
-        const char *p = reinterpret_cast<const char *>(base) + off;
+// Byte offset of 16-byte chunk `chunk` (0..15) of row `row` in a staging
+// area of bf16 rows (256 bytes each): chunks are XOR-swizzled by the row so
+// that a fragment read (16 rows, one chunk each) hits distinct banks.
+__device__ __forceinline__ uint32_t stage_off(int row, int chunk) {
+    return (uint32_t)row * (2 * D) + ((uint32_t)(chunk ^ (row & 15)) << 4);
+}
+
+// A fragment of a 16-node tile from a staging area: lane (n, grp) gets row
+// `row`, elements 32 s + 8 grp .. +7 for s = 0..3 (chunk 4 s + grp).
+__device__ __forceinline__ void lds_rows(const char *st, int row, int grp, u32x4 (&f)[4]) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) f[s] = *reinterpret_cast<const u32x4 *>(p + 64 * s);
-    } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) f[s] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int s = 0; s < 4; ++s) f[s] = *reinterpret_cast<const u32x4 *>(st + stage_off(row, 4 * s + grp));
 }
 
 template <int NM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(Args a) {
     constexpr int KT = NM / 16;   // max 16-node tiles
-    // Q tiles are fetched one tile ahead where the registers allow it (the
-    // 32-node variant would spill; it loads each Q tile after the previous one).
-    constexpr bool QPF = NM != 32;
+    // The unit's Q and K rows are staged in the R/U area, which holds nothing
+    // before the K pass writes R: Q rows from its start (dead after the Q
+    // pass), K rows at its end.  An R tile covers staged K rows of tiles up to
+    // its own only, and is written after a barrier when it covers any.
+    constexpr int RU_BYTES = NM * (D + 4) * 4;
+    constexpr int KOFF = RU_BYTES - NM * 2 * D;
     __shared__ VerifySmem<NM> sm;
+    char *const stq = reinterpret_cast<char *>(&sm.ru[0][0]);
+    char *const stk = stq + KOFF;
 
     const int n_units = a.B * a.Hv;
     const int unit = xcd_unit(blockIdx.x, n_units);
@@ -98,22 +107,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
     const int h = unit - b * a.Hv;
     const int hk = h / (a.Hv / a.Hk);
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, grp = lane >> 4;
     const int c = 32 * w + 2 * n;   // this lane's column pair
 
-    // H0 depends only on (slot, head): its loads go out before the node
-    // offsets come back, so the state is in flight during that round trip.
     const int slot = resolve_slot(a, b);
     float2 hraw[4][8];
-    if (slot >= 0) {
-        const float *H = a.S0 + ((size_t)slot * a.Hv + h) * D * D + 8 * grp * D + c;
+    const float *H = a.S0 + ((size_t)max(slot, 0) * a.Hv + h) * D * D + 8 * grp * D + c;
+    auto issue_h0 = [&]() {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 hraw[s][e] = ld_stream2(H + (32 * s + e) * D);
-    }
+    };
     int lo, N;
     int st = check_offsets(a, b, lo, N);
     if (st == GDN_TREE_S_BAD_OFFSETS) {
@@ -125,32 +132,51 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
     const uint16_t *qbase = a.q + ((size_t)lo * a.Hk + hk) * D;
     const uint16_t *vbase = a.v + ((size_t)lo * a.Hv + h) * D;   // + 32-bit per-lane offsets
     const uint32_t vrow = (uint32_t)a.Hv * D;
+    const int nkt = (N + 15) >> 4;
 
-    // ---- issue the unit's remaining global reads: per-node scalars, v, K, Q ----
+    // ---- the unit's remaining global reads: per-node scalars, staged Q/K rows, v ----
     int p_mine = -1;
     float g_mine = 0.f, b_mine = 0.f;
-    uint32_t vv[4];   // v of the current K tile's rows (the next tile's come with its A fragments)
-    // A fragments of the first K and Q tiles and the K rows of this wave's gram
-    // columns are issued with H0; later tiles are fetched one tile ahead.
+    uint32_t vv[KT][4];   // v rows 16 tau + 4 grp + i, columns c, c + 1 (clamped to the last node)
+    u32x4 sq[KT], sk[KT];   // chunk tid & 15 of Q and K row 16 tau + (tid >> 4) (clamped)
+    const int srow = tid >> 4, sch = tid & 15;
+    auto issue_rest = [&]() {
+#pragma unroll
+        for (int tau = 0; tau < KT; ++tau)
+            if (tau < nkt) {
+                const uint32_t off = ((uint32_t)min(16 * tau + srow, N - 1) * krow) * 2u + 16u * sch;
+                sq[tau] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(qbase) + off);
+                sk[tau] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(kbase) + off);
+            }
+#pragma unroll
+        for (int tau = 0; tau < KT; ++tau)
+            if (tau < nkt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    vv[tau][i] = *reinterpret_cast<const uint32_t *>(
+                        vbase + ((uint32_t)min(16 * tau + 4 * grp + i, N - 1) * vrow + c));
+    };
     const bool gram = 16 * w < N;
     const int jcol = 16 * w + n;   // gram column (node) of this lane
-    u32x4 ka[4], qa[4], bg[4];
     if (st == GDN_TREE_S_OK && N > 0) {
-        const int tc = min(tid, N - 1);
-        const size_t gi = (size_t)(lo + tc) * a.Hv + h;
-        p_mine = a.parent[lo + tc];
-        g_mine = a.g[gi];
-        b_mine = a.beta[gi];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)   // rows past N read the last row; their R rows are never used
-            vv[i] = *reinterpret_cast<const uint32_t *>(vbase + ((uint32_t)min(4 * grp + i, N - 1) * vrow + c));
-        load_rows(kbase, krow, jcol, N, grp, bg);
-        load_rows(kbase, krow, n, N, grp, ka);
-        if (tid < N) sm.beta[tid] = b_mine;
         if (w == 0) {
-            const bool bad = (tid < N) && (p_mine < -1 || p_mine >= tid);
+            // wave 0 needs its per-node scalars first (tree pre-pass): they and
+            // the staged rows go out before its H0 slab, so waiting for them
+            // does not wait for the slab
+            const int tc = min(lane, N - 1);
+            const size_t gi = (size_t)(lo + tc) * a.Hv + h;
+            p_mine = a.parent[lo + tc];
+            g_mine = a.g[gi];
+            b_mine = a.beta[gi];
+            issue_rest();
+            issue_h0();
+            sm.beta[lane] = b_mine;
+            const bool bad = (lane < N) && (p_mine < -1 || p_mine >= lane);
             const unsigned long long any = __ballot(bad);
             if (lane == 0) sm.bad = any != 0ull;
+        } else {
+            issue_rest();
+            issue_h0();
         }
         lds_barrier();
         if (sm.bad) st = GDN_TREE_S_BAD_PARENT;
@@ -222,7 +248,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
         }
     }
 
-    // ---- B operands: H0 slab (hi, lo) and K^T for node columns 16w .. 16w+15 ----
+    // ---- B operand: H0 slab (hi, lo); staged rows to LDS (zeros past N) ----
     u32x4 bhi[4][2], blo[4][2];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -237,75 +263,54 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
             blo[s][1][pr] = l1;
         }
     }
-    lds_barrier();   // ancestry, G, gamma, depths, levels visible
+#pragma unroll
+    for (int tau = 0; tau < KT; ++tau)
+        if (tau < nkt) {
+            const int row = 16 * tau + srow;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4 *>(stq + stage_off(row, sch)) = row < N ? sq[tau] : z;
+            *reinterpret_cast<u32x4 *>(stk + stage_off(row, sch)) = row < N ? sk[tau] : z;
+        }
+    lds_barrier();   // ancestry, G, gamma, depths, levels and the staged rows visible
 
-    // ---- one MFMA pass: K tiles -> R, Q tiles -> Z (registers), grams -> T ----
-    const int nkt = (N + 15) >> 4;
+    // ---- grams against K^T for node columns 16w .. 16w+15 (ancestor entries only) ----
     const float G2_j = gram && jcol < N ? sm.G2[jcol] : 0.f;
     const int qj = gram && jcol < N ? sm.dep[jcol] - 1 : 0;   // position of node jcol in its descendants' lists
+    u32x4 bg[4];
+    if (gram) {
+        lds_rows(stk, jcol, grp, bg);   // jcol < 16 nkt: staged (zeros past N)
+#pragma unroll
+        for (int tau = 0; tau < KT; ++tau) {   // A = beta_r D_rj (k_r.k_j) for strict ancestors j
+            if (tau < nkt) {
+                u32x4 ak[4];
+                lds_rows(stk, 16 * tau + n, grp, ak);
+                f32x4 gk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) gk = mfma(ak[s], bg[s], gk);
+                const int r0 = 16 * tau + 4 * grp;
+                const float4 bt4 = *reinterpret_cast<const float4 *>(&sm.beta[r0]);
+                const float4 g24 = *reinterpret_cast<const float4 *>(&sm.G2[r0]);
+                const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+                const float g2[4] = {g24.x, g24.y, g24.z, g24.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = r0 + i;
+                    if (jcol < r && ((sm.anc[r] >> jcol) & 1ull))
+                        sm.T[r][qj] = bt[i] * exp2_fast(g2[i] - G2_j) * gk[i];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // ---- Q pass: Z = Q H0 kept in registers, P entries ----
     f32x4 zt[KT][2];
 #pragma unroll
-    for (int tau = 0; tau < KT; ++tau) {   // K tiles: R rows and A entries
-        if (tau < nkt) {
-            u32x4 ak[4], nx[4];
-            uint32_t vc[4], vn[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                ak[s] = ka[s];
-                vc[s] = vv[s];
-            }
-            if (tau + 1 == nkt) load_rows(qbase, krow, n, N, grp, qa);
-            if (tau + 1 < KT) {
-                load_rows(kbase, krow, 16 * (tau + 1) + n, N, grp, nx);   // zeros past N
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    vn[i] = *reinterpret_cast<const uint32_t *>(vbase + ((uint32_t)min(16 * (tau + 1) + 4 * grp + i, N - 1) * vrow + c));
-            }
-            f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0, gk = w0;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                w0 = mfma(ak[s], bhi[s][0], w0);
-                w1 = mfma(ak[s], bhi[s][1], w1);
-                w0 = mfma(ak[s], blo[s][0], w0);
-                w1 = mfma(ak[s], blo[s][1], w1);
-                if (gram) gk = mfma(ak[s], bg[s], gk);
-            }
-            // rows r0 .. r0+3 of this lane (rows past N are scratch rows of ru)
-            const int r0 = 16 * tau + 4 * grp;
-            const float4 bt4 = *reinterpret_cast<const float4 *>(&sm.beta[r0]);
-            const float4 gm4 = *reinterpret_cast<const float4 *>(&sm.gam[r0]);
-            const float4 g24 = *reinterpret_cast<const float4 *>(&sm.G2[r0]);
-            const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
-            const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
-            const float g2[4] = {g24.x, g24.y, g24.z, g24.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = r0 + i;
-                float2 rr;
-                rr.x = bt[i] * (bf16_lo(vc[i]) - gm[i] * w0[i]);
-                rr.y = bt[i] * (bf16_hi(vc[i]) - gm[i] * w1[i]);
-                *reinterpret_cast<float2 *>(&sm.ru[r][c]) = rr;
-                // strict ancestor jcol of r: A = beta_r D_rj (k_r.k_j) at position dep(j)-1
-                if (gram && jcol < r && ((sm.anc[r] >> jcol) & 1ull))
-                    sm.T[r][qj] = bt[i] * exp2_fast(g2[i] - G2_j) * gk[i];
-            }
-            if (tau + 1 < KT)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    ka[s] = nx[s];
-                    vv[s] = vn[s];
-                }
-        }
-        __builtin_amdgcn_sched_barrier(0);   // one tile's operands live at a time
-    }
-#pragma unroll
-    for (int tau = 0; tau < KT; ++tau) {   // Q tiles: Z kept in registers, P entries
+    for (int tau = 0; tau < KT; ++tau) {
         zt[tau][0] = zt[tau][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (tau < nkt) {
-            u32x4 aq[4], nx[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) aq[s] = qa[s];
-            if (QPF && tau + 1 < KT) load_rows(qbase, krow, 16 * (tau + 1) + n, N, grp, nx);
+            u32x4 aq[4];
+            lds_rows(stq, 16 * tau + n, grp, aq);
             f32x4 gq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -327,13 +332,40 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
                         sm.T[jcol][r] = ((sm.anc[r] >> jcol) & 1ull) ? exp2_fast(g2[i] - G2_j) * gq[i] : 0.f;
                 }
             }
-            if (tau + 1 < KT) {
-                if (QPF) {
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_barrier();   // every wave is done with the staged Q rows: R rows may take their place
+
+    // ---- K pass: W = K H0, turned into R in LDS ----
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) qa[s] = nx[s];
-                } else {
-                    load_rows(qbase, krow, 16 * (tau + 1) + n, N, grp, qa);
-                }
+    for (int tau = 0; tau < KT; ++tau) {
+        if (tau < nkt) {
+            u32x4 ak[4];
+            lds_rows(stk, 16 * tau + n, grp, ak);
+            f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                w0 = mfma(ak[s], bhi[s][0], w0);
+                w1 = mfma(ak[s], bhi[s][1], w1);
+                w0 = mfma(ak[s], blo[s][0], w0);
+                w1 = mfma(ak[s], blo[s][1], w1);
+            }
+            // this tile's R rows cover staged K rows of tiles <= tau: all waves read them first
+            if ((tau + 1) * 16 * (D + 4) * 4 > KOFF) lds_barrier();
+            // rows r0 .. r0+3 of this lane (rows past N are scratch rows of ru)
+            const int r0 = 16 * tau + 4 * grp;
+            const float4 bt4 = *reinterpret_cast<const float4 *>(&sm.beta[r0]);
+            const float4 gm4 = *reinterpret_cast<const float4 *>(&sm.gam[r0]);
+            const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+            const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = r0 + i;
+                float2 rr;
+                rr.x = bt[i] * (bf16_lo(vv[tau][i]) - gm[i] * w0[i]);
+                rr.y = bt[i] * (bf16_hi(vv[tau][i]) - gm[i] * w1[i]);
+                *reinterpret_cast<float2 *>(&sm.ru[r][c]) = rr;
             }
         }
         __builtin_amdgcn_sched_barrier(0);
