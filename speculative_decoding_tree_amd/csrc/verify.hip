@@ -31,8 +31,9 @@
 // tree pre-pass waits for the scalars and the staged rows but not for H0.
 // The staged rows (bf16, XOR-swizzled 16-byte chunks) occupy the R/U area,
 // which holds nothing until R is written: Q rows at its start, K rows at its
-// end.  Then, from LDS: the grams against K^T for node columns 16w .. 16w+15
-// (ancestor entries scaled on the spot into a coefficient table), the Q pass
+// end.  Then, from LDS: the grams against K^T for 16 node columns per wave
+// (ancestor entries scaled on the spot into a coefficient table; in units of
+// up to 32 nodes the K and the Q products go to different waves), the Q pass
 // (Z = Q H0 kept in registers, P entries), a barrier (the Q rows are dead),
 // and the K pass (W = K H0, turned into R in place; an R tile that covers
 // staged K rows is written after a barrier, and it only ever covers rows of
@@ -132,7 +133,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
     const uint16_t *qbase = a.q + ((size_t)lo * a.Hk + hk) * D;
     const uint16_t *vbase = a.v + ((size_t)lo * a.Hv + h) * D;   // + 32-bit per-lane offsets
     const uint32_t vrow = (uint32_t)a.Hv * D;
+    // Grams: wave w takes node columns 16 ct .. 16 ct + 15 against the K rows
+    // (A entries) and/or the Q rows (P entries).  Units of more than 32 nodes:
+    // each wave both, for ct = w.  Smaller ones would leave waves idle, so the
+    // two products go to different waves.
     const int nkt = (N + 15) >> 4;
+    int ct = w;
+    bool kgram = 16 * w < N, qgram = kgram;
+    if (nkt == 1) {
+        ct = 0;
+        kgram = w == 0;
+        qgram = w == 1;
+    } else if (nkt == 2) {
+        ct = w & 1;
+        kgram = w < 2;
+        qgram = w >= 2;
+    }
+    const bool gram = kgram || qgram;
+    const int jcol = 16 * ct + n;   // gram column (node) of this lane
 
     // ---- the unit's remaining global reads: per-node scalars, staged Q/K rows, v ----
     int p_mine = -1;
@@ -156,8 +174,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
                     vv[tau][i] = *reinterpret_cast<const uint32_t *>(
                         vbase + ((uint32_t)min(16 * tau + 4 * grp + i, N - 1) * vrow + c));
     };
-    const bool gram = 16 * w < N;
-    const int jcol = 16 * w + n;   // gram column (node) of this lane
     if (st == GDN_TREE_S_OK && N > 0) {
         if (w == 0) {
             // wave 0 needs its per-node scalars first (tree pre-pass): they and
@@ -273,12 +289,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
         }
     lds_barrier();   // ancestry, G, gamma, depths, levels and the staged rows visible
 
-    // ---- grams against K^T for node columns 16w .. 16w+15 (ancestor entries only) ----
+    // ---- grams against K^T for node columns 16 ct .. 16 ct + 15 (ancestor entries only) ----
     const float G2_j = gram && jcol < N ? sm.G2[jcol] : 0.f;
     const int qj = gram && jcol < N ? sm.dep[jcol] - 1 : 0;   // position of node jcol in its descendants' lists
     u32x4 bg[4];
     if (gram) {
         lds_rows(stk, jcol, grp, bg);   // jcol < 16 nkt: staged (zeros past N)
+    }
+    if (kgram) {
 #pragma unroll
         for (int tau = 0; tau < KT; ++tau) {   // A = beta_r D_rj (k_r.k_j) for strict ancestors j
             if (tau < nkt) {
@@ -318,9 +336,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
                 zt[tau][1] = mfma(aq[s], bhi[s][1], zt[tau][1]);
                 zt[tau][0] = mfma(aq[s], blo[s][0], zt[tau][0]);
                 zt[tau][1] = mfma(aq[s], blo[s][1], zt[tau][1]);
-                if (gram) gq = mfma(aq[s], bg[s], gq);
+                if (qgram) gq = mfma(aq[s], bg[s], gq);
             }
-            if (gram) {
+            if (qgram) {
                 const int r0 = 16 * tau + 4 * grp;
                 const float4 g24 = *reinterpret_cast<const float4 *>(&sm.G2[r0]);
                 const float g2[4] = {g24.x, g24.y, g24.z, g24.w};
@@ -447,7 +465,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
                 }
 #pragma unroll
                 for (int tau = 0; tau < KT; ++tau) {
-                    if (tau < nkt) {
+                    if (tau < nkt && 32 * ks <= 16 * tau + 15) {   // blocks with every j > t are zero
                         const int t = 16 * tau + n;
                         u32x4 pah, pal;
 #pragma unroll
