@@ -76,6 +76,15 @@ SMALL = {
         [np.zeros(0, np.int32), np.array([-1], np.int32), np.full(8, -1, np.int32),
          np.zeros(0, np.int32), W.random_tree(np.random.default_rng(3), 40)],
         [-1, 0, 5, -1, 7], Hv=4, Hk=4),
+    # 32-node build: units of one and two 16-node tiles (the K and Q grams on
+    # different waves; the second tile's R rows written after a barrier)
+    "nm32_mix": lambda: W.make_custom(
+        [W.random_tree(np.random.default_rng(10 + s), n) for s, n in enumerate([32, 17, 1, 16, 31, 24])],
+        [5, 0, 0, -1, 30, 11], Hv=6, Hk=2),
+    # 16-node build with a full tile
+    "nm16_full": lambda: W.make_custom(
+        [W.random_tree(np.random.default_rng(20 + s), n) for s, n in enumerate([16, 1, 15, 9])],
+        [15, -1, 3, 8], Hv=4, Hk=2),
     "ragged_tail_max": lambda: W.make_custom(
         [W.random_tree(np.random.default_rng(s), n) for s, n in enumerate([64, 17, 33, 5, 63, 1])],
         [3, 0, -1, 4, 10, 0], Hv=6, Hk=3),
