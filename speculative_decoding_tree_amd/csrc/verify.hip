@@ -34,7 +34,7 @@
 // end.  Then, from LDS: the grams against K^T for 16 node columns per wave
 // (ancestor entries scaled on the spot into a coefficient table; in units of
 // up to 32 nodes the K and the Q products go to different waves), the Q pass
-// (Z = Q H0 kept in registers, P entries), a barrier (the Q rows are dead),
+// (Z = Q H0 kept in registers), a barrier (the Q rows are dead),
 // and the K pass (W = K H0, turned into R in place; an R tile that covers
 // staged K rows is written after a barrier, and it only ever covers rows of
 // tiles already read).  After the K pass the solve and the outputs are
@@ -88,8 +88,11 @@ __device__ __forceinline__ void lds_rows(const char *st, int row, int grp, u32x4
     for (int s = 0; s < 4; ++s) f[s] = *reinterpret_cast<const u32x4 *>(st + stage_off(row, 4 * s + grp));
 }
 
+// Occupancy: units of up to 32 nodes fit 128 registers and 23 KiB of LDS, so
+// four workgroups share a CU; the 64-node build needs 148 registers and 52 KiB
+// and runs three.
 template <int NM>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(Args a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4 : 3))) void verify_kernel(Args a) {
     constexpr int KT = NM / 16;   // max 16-node tiles
     // The unit's Q and K rows are staged in the R/U area, which holds nothing
     // before the K pass writes R: Q rows from its start (dead after the Q
@@ -292,36 +295,49 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
     // ---- grams against K^T for node columns 16 ct .. 16 ct + 15 (ancestor entries only) ----
     const float G2_j = gram && jcol < N ? sm.G2[jcol] : 0.f;
     const int qj = gram && jcol < N ? sm.dep[jcol] - 1 : 0;   // position of node jcol in its descendants' lists
-    u32x4 bg[4];
     if (gram) {
+        u32x4 bg[4];
         lds_rows(stk, jcol, grp, bg);   // jcol < 16 nkt: staged (zeros past N)
-    }
-    if (kgram) {
 #pragma unroll
-        for (int tau = 0; tau < KT; ++tau) {   // A = beta_r D_rj (k_r.k_j) for strict ancestors j
+        for (int tau = 0; tau < KT; ++tau) {
             if (tau < nkt) {
-                u32x4 ak[4];
-                lds_rows(stk, 16 * tau + n, grp, ak);
-                f32x4 gk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) gk = mfma(ak[s], bg[s], gk);
                 const int r0 = 16 * tau + 4 * grp;
-                const float4 bt4 = *reinterpret_cast<const float4 *>(&sm.beta[r0]);
                 const float4 g24 = *reinterpret_cast<const float4 *>(&sm.G2[r0]);
-                const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
                 const float g2[4] = {g24.x, g24.y, g24.z, g24.w};
+                if (kgram) {   // A = beta_r D_rj (k_r.k_j) for strict ancestors j
+                    u32x4 ak[4];
+                    lds_rows(stk, 16 * tau + n, grp, ak);
+                    f32x4 gk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = r0 + i;
-                    if (jcol < r && ((sm.anc[r] >> jcol) & 1ull))
-                        sm.T[r][qj] = bt[i] * exp2_fast(g2[i] - G2_j) * gk[i];
+                    for (int s = 0; s < 4; ++s) gk = mfma(ak[s], bg[s], gk);
+                    const float4 bt4 = *reinterpret_cast<const float4 *>(&sm.beta[r0]);
+                    const float bt[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = r0 + i;
+                        if (jcol < r && ((sm.anc[r] >> jcol) & 1ull))
+                            sm.T[r][qj] = bt[i] * exp2_fast(g2[i] - G2_j) * gk[i];
+                    }
+                }
+                if (qgram) {   // P_rj = D_rj (q_r.k_j) for an inclusive ancestor jcol of r, 0 for other j <= r
+                    u32x4 aq[4];
+                    lds_rows(stq, 16 * tau + n, grp, aq);
+                    f32x4 gq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) gq = mfma(aq[s], bg[s], gq);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = r0 + i;
+                        if (jcol < N && jcol <= r)
+                            sm.T[jcol][r] = ((sm.anc[r] >> jcol) & 1ull) ? exp2_fast(g2[i] - G2_j) * gq[i] : 0.f;
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // ---- Q pass: Z = Q H0 kept in registers, P entries ----
+    // ---- Q pass: Z = Q H0 kept in registers ----
     f32x4 zt[KT][2];
 #pragma unroll
     for (int tau = 0; tau < KT; ++tau) {
@@ -329,26 +345,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void ve
         if (tau < nkt) {
             u32x4 aq[4];
             lds_rows(stq, 16 * tau + n, grp, aq);
-            f32x4 gq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 zt[tau][0] = mfma(aq[s], bhi[s][0], zt[tau][0]);
                 zt[tau][1] = mfma(aq[s], bhi[s][1], zt[tau][1]);
                 zt[tau][0] = mfma(aq[s], blo[s][0], zt[tau][0]);
                 zt[tau][1] = mfma(aq[s], blo[s][1], zt[tau][1]);
-                if (qgram) gq = mfma(aq[s], bg[s], gq);
-            }
-            if (qgram) {
-                const int r0 = 16 * tau + 4 * grp;
-                const float4 g24 = *reinterpret_cast<const float4 *>(&sm.G2[r0]);
-                const float g2[4] = {g24.x, g24.y, g24.z, g24.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // P_rj = D_rj (q_r.k_j) for an inclusive ancestor jcol of r, 0 for other j <= r
-                    const int r = r0 + i;
-                    if (jcol < N && jcol <= r)
-                        sm.T[jcol][r] = ((sm.anc[r] >> jcol) & 1ull) ? exp2_fast(g2[i] - G2_j) * gq[i] : 0.f;
-                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
