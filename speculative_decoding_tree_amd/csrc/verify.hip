@@ -59,8 +59,10 @@ constexpr int NT = 256;
 //                             output product (P masked) U)
 template <int NM>
 struct VerifySmem {
-    float ru[NM][D + 4];                       // staged Q and K rows, then R, then U after the solve
-    float T[NM][NM + 4];
+    // Rows padded by two floats: rows eight apart (the four lane groups of an
+    // output fragment read) fall on different banks.
+    float ru[NM][D + 2];                       // staged Q and K rows, then R, then U after the solve
+    float T[NM][NM + 2];
     __attribute__((aligned(16))) uint64_t anc[NM];
     __attribute__((aligned(16))) float gam[NM];
     __attribute__((aligned(16))) float beta[64];   // one per wave-0 lane (clamped copies past N)
@@ -98,8 +100,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
     // before the K pass writes R: Q rows from its start (dead after the Q
     // pass), K rows at its end.  An R tile covers staged K rows of tiles up to
     // its own only, and is written after a barrier when it covers any.
-    constexpr int RU_BYTES = NM * (D + 4) * 4;
+    constexpr int RU_BYTES = NM * (D + 2) * 4;
     constexpr int KOFF = RU_BYTES - NM * 2 * D;
+    static_assert(KOFF % 16 == 0, "staged rows are read 16 bytes at a time");
     __shared__ VerifySmem<NM> sm;
     char *const stq = reinterpret_cast<char *>(&sm.ru[0][0]);
     char *const stk = stq + KOFF;
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
                 w1 = mfma(ak[s], blo[s][1], w1);
             }
             // this tile's R rows cover staged K rows of tiles <= tau: all waves read them first
-            if ((tau + 1) * 16 * (D + 4) * 4 > KOFF) lds_barrier();
+            if ((tau + 1) * 16 * (D + 2) * 4 > KOFF) lds_barrier();
             // rows r0 .. r0+3 of this lane (rows past N are scratch rows of ru)
             const int r0 = 16 * tau + 4 * grp;
             const float4 bt4 = *reinterpret_cast<const float4 *>(&sm.beta[r0]);
