@@ -688,58 +688,79 @@ __global__ __launch_bounds__(AT) void attn_merge_kernel(AttnArgs a) {
         nan_rows(a, lo, hk, ROWS * rg, nan_end(a, rg, R));
         return;
     }
-    const int quarter = tid & 3;
     const size_t PART = part_floats(ROWS);
     const int nparts = Lc > 0 ? (Lc + a.split - 1) / a.split : 1;
     const size_t stride = (size_t)a.n_rg * PART;   // between consecutive parts
     const float *rec = a.ws + ATTN_WS_HEADER_BYTES / 4 + (((size_t)b * a.Hkv + hk) * a.n_split * a.n_rg + rg) * PART;
-  for (int rl = tid >> 2; rl < ROWS; rl += AT / 4) {
-    const int r = ROWS * rg + rl;
-    if (r >= R) break;
-    const int t = r / G, g = r - t * G;
-    const size_t orow = (size_t)(lo + t) * a.Hq + hk * G + g;
-    float *op = a.out + orow * D + 32 * quarter;
-    float M = -INFINITY, L = 0.f;
-    f32x4 acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (MAXP > 0) {
-        float mp[MAXP], lp[MAXP];
+        // thread (row, slice): 8 threads per row, 16 columns each; every part's
+        // max, sum and slice are requested before any of them is used
+        const int sl = tid & 7;
+        for (int rl = tid >> 3; rl < ROWS; rl += AT / 8) {
+            const int r = ROWS * rg + rl;
+            if (r >= R) break;
+            const int t = r / G, g = r - t * G;
+            const size_t orow = (size_t)(lo + t) * a.Hq + hk * G + g;
+            float mp[MAXP], lp[MAXP];
+            f32x4 ov[MAXP][4];
 #pragma unroll
-        for (int s = 0; s < MAXP; ++s) {   // reads stay inside the request's parts (index clamped)
-            const size_t sp = (size_t)min(s, nparts - 1) * stride;
-            const float mv = rec[sp + ROWS * D + rl], lv = rec[sp + ROWS * D + ROWS + rl];
-            mp[s] = s < nparts ? mv : -INFINITY;
-            lp[s] = s < nparts ? lv : 0.f;
-            M = fmaxf(M, mp[s]);
+            for (int s = 0; s < MAXP; ++s) {   // reads stay inside the request's parts (index clamped)
+                const size_t sp = (size_t)min(s, nparts - 1) * stride;
+                mp[s] = rec[sp + ROWS * D + rl];
+                lp[s] = rec[sp + ROWS * D + ROWS + rl];
+                const f32x4 *src = reinterpret_cast<const f32x4 *>(rec + sp + rl * D + 16 * sl);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ov[s][i] = src[i];
+            }
+            float M = -INFINITY, L = 0.f;
+#pragma unroll
+            for (int s = 0; s < MAXP; ++s)
+                if (s < nparts) M = fmaxf(M, mp[s]);
+            f32x4 acc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < MAXP; ++s) {
+                if (s < nparts) {
+                    const float wgt = __builtin_amdgcn_exp2f(mp[s] - M);
+                    L += wgt * lp[s];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] += wgt * ov[s][i];
+                }
+            }
+            const float inv = 1.f / L;
+            float *op = a.out + orow * D + 16 * sl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4 *>(op + 4 * i) = acc[i] * inv;
+            if (sl == 0 && a.lse) a.lse[orow] = (M + log2f(L)) * LN2;
         }
+    } else {
+        const int quarter = tid & 3;
+        for (int rl = tid >> 2; rl < ROWS; rl += AT / 4) {
+            const int r = ROWS * rg + rl;
+            if (r >= R) break;
+            const int t = r / G, g = r - t * G;
+            const size_t orow = (size_t)(lo + t) * a.Hq + hk * G + g;
+            float *op = a.out + orow * D + 32 * quarter;
+            float M = -INFINITY, L = 0.f;
+            f32x4 acc[8];
 #pragma unroll
-        for (int s = 0; s < MAXP; ++s) {
-            if (s < nparts) {
-                const float wgt = __builtin_amdgcn_exp2f(mp[s] - M);
-                L += wgt * lp[s];
-                const f32x4 *src = reinterpret_cast<const f32x4 *>(rec + (size_t)min(s, nparts - 1) * stride +
-                                                                   rl * D + 32 * quarter);
+            for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < nparts; ++s) M = fmaxf(M, rec[s * stride + ROWS * D + rl]);
+            for (int s = 0; s < nparts; ++s) {
+                const float *rs = rec + s * stride;
+                const float wgt = __builtin_amdgcn_exp2f(rs[ROWS * D + rl] - M);
+                L += wgt * rs[ROWS * D + ROWS + rl];
+                const f32x4 *src = reinterpret_cast<const f32x4 *>(rs + rl * D + 32 * quarter);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] += wgt * src[i];
             }
-        }
-    } else {
-        for (int s = 0; s < nparts; ++s) M = fmaxf(M, rec[s * stride + ROWS * D + rl]);
-        for (int s = 0; s < nparts; ++s) {
-            const float *rs = rec + s * stride;
-            const float wgt = __builtin_amdgcn_exp2f(rs[ROWS * D + rl] - M);
-            L += wgt * rs[ROWS * D + ROWS + rl];
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(rs + rl * D + 32 * quarter);
+            const float inv = 1.f / L;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += wgt * src[i];
+            for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4 *>(op + 4 * i) = acc[i] * inv;
+            if (quarter == 0 && a.lse) a.lse[orow] = (M + log2f(L)) * LN2;
         }
     }
-    const float inv = 1.f / L;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4 *>(op + 4 * i) = acc[i] * inv;
-    if (quarter == 0 && a.lse) a.lse[orow] = (M + log2f(L)) * LN2;
-  }
 }
 
 }  // namespace
