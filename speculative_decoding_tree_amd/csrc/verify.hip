@@ -76,6 +76,20 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Staging rule of the R/U area (bytes, rows of 2D bf16 per staged row): the
+// Q rows sit at its start and are dead before any R tile is written; the K
+// rows sit at its end, and R tile tau (written after the K pass has read K
+// tile tau in every wave) may cover staged K rows of tiles 0 .. tau only.
+constexpr bool staging_rule_holds(int nm, int row_bytes) {
+    const int ru_bytes = nm * row_bytes, koff = ru_bytes - nm * 2 * D;
+    if (koff < nm * 2 * D) return false;   // Q and K rows must not overlap
+    for (int tau = 0; tau < nm / 16; ++tau) {
+        const int end = (tau + 1) * 16 * row_bytes;   // R tile tau ends here
+        if (end > koff && (end - koff + 2 * D - 1) / (2 * D) > 16 * (tau + 1)) return false;
+    }
+    return true;
+}
+
 // Byte offset of 16-byte chunk `chunk` (0..15) of row `row` in a staging
 // area of bf16 rows (256 bytes each): chunks are XOR-swizzled by the row so
 // that a fragment read (16 rows, one chunk each) hits distinct banks.
@@ -103,6 +117,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
     constexpr int RU_BYTES = NM * (D + 2) * 4;
     constexpr int KOFF = RU_BYTES - NM * 2 * D;
     static_assert(KOFF % 16 == 0, "staged rows are read 16 bytes at a time");
+    static_assert(staging_rule_holds(NM, (D + 2) * 4), "an R tile would overwrite K rows still to be read");
     __shared__ VerifySmem<NM> sm;
     char *const stq = reinterpret_cast<char *>(&sm.ru[0][0]);
     char *const stk = stq + KOFF;
