@@ -86,6 +86,7 @@ extern "C" {
 #define GDN_TREE_E_SIZE (-6)      /* a buffer would exceed 2^62 bytes */
 #define GDN_TREE_E_ALIGN (-7)     /* a state / q / k / v / out / U / node_state pointer is not 16-byte aligned */
 #define GDN_TREE_E_WORKSPACE (-8) /* attention workspace missing, misaligned or smaller than required */
+#define GDN_TREE_E_OVERLAP (-9)   /* gdn_tree_commit_verify: out or U overlaps U_prev */
 
 /* device-side per-request status codes (status[b]) */
 #define GDN_TREE_S_OK 0
@@ -210,6 +211,43 @@ int gdn_tree_commit_node(const gdn_tree_dims *dims, const float *S0, float *S_ou
                          const int32_t *state_slot, const float *U, const uint16_t *k, const float *g,
                          const int32_t *node_offset, const int32_t *parent, const int32_t *accept_node,
                          int32_t *path, int32_t *path_len, int32_t *status, void *stream);
+
+/*
+ * gdn_tree_commit_verify -- the commit of the previous tree's accepted node
+ * and the verify of the next tree, in one launch.
+ *
+ * In a decoding loop the state committed for one draft tree is the state the
+ * next tree is verified from (TreeWY, "Method": only the accepted path is
+ * composed into the next committed state, and verification starts from the
+ * committed state).  Each (request, v-head) workgroup reads S0 once, composes
+ * the previous tree's accepted path into it as gdn_tree_commit_node does,
+ * writes the result to S_out, and verifies the next tree from the registers
+ * that hold it, so the committed state is not read back.  Results equal
+ * gdn_tree_commit_node(prev_dims, S0 -> S_out, U_prev, k_prev, g_prev,
+ * node_offset_prev, parent_prev, accept_node) followed by
+ * gdn_tree_verify(dims, S_out, ...) bit for bit.
+ *
+ * prev_dims describes the previous tree (its T and max_nodes); B, Hv, Hk and
+ * n_slots must equal those of dims (GDN_TREE_E_DIMS otherwise).  U_prev,
+ * k_prev, g_prev, node_offset_prev and parent_prev are that tree's
+ * pseudo-values (from its verify), keys, gates, offsets and parents, in the
+ * layouts above; accept_node int32 [B] is its accepted node (-1 = none).
+ * The other arguments are those of gdn_tree_verify for the next tree.
+ * S_out may alias S0 (in place: nothing is written for a request with an
+ * empty path); out and U must not overlap U_prev (GDN_TREE_E_OVERLAP).
+ * commit_status [B] (optional) receives the commit's device status as
+ * gdn_tree_commit_node reports it, status [B] the verify's.  A request whose
+ * commit fails (bad offsets, parent or accept_node) is verified from S0,
+ * which is also what S_out then holds; a bad slot writes nothing and gives
+ * NaN outputs, as the two calls would.
+ */
+int gdn_tree_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *dims, const float *S0,
+                           float *S_out, const int32_t *state_slot, const float *U_prev,
+                           const uint16_t *k_prev, const float *g_prev, const int32_t *node_offset_prev,
+                           const int32_t *parent_prev, const int32_t *accept_node, int32_t *commit_status,
+                           const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                           const float *beta, const int32_t *node_offset, const int32_t *parent, float *out,
+                           float *U, uint64_t *anc_mask, int32_t *status, void *stream);
 
 /*
  * gdn_tree_accept_commit -- greedy acceptance fused with the commit, in one

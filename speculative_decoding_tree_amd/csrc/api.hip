@@ -111,6 +111,7 @@ const char *gdn_tree_strerror(int code) {
         case GDN_TREE_E_SIZE: return "buffer or grid size out of range";
         case GDN_TREE_E_ALIGN: return "state, q, k, v, out, U and node_state pointers must be 16-byte aligned";
         case GDN_TREE_E_WORKSPACE: return "attention workspace missing, misaligned or too small";
+        case GDN_TREE_E_OVERLAP: return "out or U overlaps U_prev";
         case GDN_TREE_S_BAD_OFFSETS: return "status: node_offset out of order or beyond T";
         case GDN_TREE_S_TOO_MANY: return "status: request has more than max_nodes nodes";
         case GDN_TREE_S_BAD_PARENT: return "status: parent[t] must satisfy -1 <= parent[t] < t";
@@ -301,6 +302,60 @@ int gdn_tree_commit_node(const gdn_tree_dims *dims, const float *S0, float *S_ou
     a.status = status;
     clear_pending();
     return finish(gdn::launch_commit_node(a, (hipStream_t)stream));
+}
+
+int gdn_tree_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *dims, const float *S0, float *S_out,
+                           const int32_t *state_slot, const float *U_prev, const uint16_t *k_prev,
+                           const float *g_prev, const int32_t *node_offset_prev, const int32_t *parent_prev,
+                           const int32_t *accept_node, int32_t *commit_status, const uint16_t *q,
+                           const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
+                           const int32_t *node_offset, const int32_t *parent, float *out, float *U,
+                           uint64_t *anc_mask, int32_t *status, void *stream) {
+    int rc = check_dims(prev_dims);
+    if (rc != GDN_TREE_OK) return rc;
+    rc = check_dims(dims);
+    if (rc != GDN_TREE_OK) return rc;
+    if (prev_dims->B != dims->B) return GDN_TREE_E_DIMS;
+    if (dims->B == 0) return GDN_TREE_OK;
+    if (prev_dims->Hv != dims->Hv || prev_dims->Hk != dims->Hk || prev_dims->n_slots != dims->n_slots)
+        return GDN_TREE_E_DIMS;
+    if (!S0 || !S_out || !node_offset || !node_offset_prev || !accept_node) return GDN_TREE_E_NULL;
+    if (prev_dims->T > 0 && (!U_prev || !k_prev || !g_prev || !parent_prev)) return GDN_TREE_E_NULL;
+    if (dims->T > 0 && (!q || !k || !v || !g || !beta || !parent || !out || !U)) return GDN_TREE_E_NULL;
+    if (any_misaligned(S0, S_out, U_prev, k_prev, q, k, v, out, U)) return GDN_TREE_E_ALIGN;
+    // out and U are written while other workgroups read U_prev
+    const size_t rows_prev = (size_t)prev_dims->T * dims->Hv * GDN_TREE_HEAD_DIM;
+    const size_t rows = (size_t)dims->T * dims->Hv * GDN_TREE_HEAD_DIM;
+    auto overlaps = [&](const float *x) {
+        return x && U_prev && rows && rows_prev && x < U_prev + rows_prev && U_prev < x + rows;
+    };
+    if (overlaps(U) || overlaps(out)) return GDN_TREE_E_OVERLAP;
+    Args a = base_args(dims);
+    a.S0 = S0;
+    a.S_out = S_out;
+    a.state_slot = state_slot;
+    a.T_prev = prev_dims->T;
+    a.max_nodes_prev = prev_dims->max_nodes;
+    a.U_prev = U_prev;
+    a.k_prev = k_prev;
+    a.g_prev = g_prev;
+    a.node_offset_prev = node_offset_prev;
+    a.parent_prev = parent_prev;
+    a.accept_node = accept_node;
+    a.commit_status = commit_status;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.node_offset = node_offset;
+    a.parent = parent;
+    a.out = out;
+    a.U = U;
+    a.anc_mask = anc_mask;
+    a.status = status;
+    clear_pending();
+    return finish(gdn::launch_commit_verify(a, (hipStream_t)stream));
 }
 
 int gdn_tree_budget_select(const gdn_tree_dims *dims, const int32_t *node_offset, const int32_t *parent,

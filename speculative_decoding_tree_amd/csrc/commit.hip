@@ -42,12 +42,6 @@ __device__ __forceinline__ uint64_t greedy_walk(const Args &a, int b, int lo, in
     return pm;
 }
 
-// Node at position `lane` (root first) of the path set pm, or 0 past its end.
-__device__ __forceinline__ int path_entry(uint64_t pm, int lane) {
-    uint64_t m = pm;
-    for (int k = 0; k < lane && m; ++k) m &= m - 1;
-    return m ? __builtin_ctzll(m) : 0;
-}
 
 
 constexpr int NT = 256;
@@ -56,24 +50,6 @@ constexpr int KCHUNK = 16;   // path rows staged per pass
 // Where the accepted path comes from: the caller (a root-first path), the
 // greedy walk over token ids, or the accepted node (its root-first ancestors).
 enum PathSource { PATH_GIVEN = 0, PATH_GREEDY = 1, PATH_FROM_NODE = 2 };
-
-// Inclusive ancestor set of node acc (lane t = node t, parents validated), by
-// pointer doubling over shuffles; 0 for acc = -1.
-__device__ __forceinline__ uint64_t ancestors_of(int lane, int N, int p, int acc) {
-    const bool live = lane < N;
-    int jp = live ? p : -1;
-    uint64_t m = live ? (1ull << lane) : 0ull;
-    while (__ballot(jp >= 0)) {
-        const int src = jp >= 0 ? jp : lane;
-        const uint64_t m_up = __shfl(m, src);
-        const int jp_up = __shfl(jp, src);
-        if (jp >= 0) {
-            m |= m_up;
-            jp = jp_up;
-        }
-    }
-    return acc >= 0 ? __shfl(m, acc) : 0ull;
-}
 
 // The unit's 64 KiB of H0 is requested first (it depends only on the slot);
 // wave 0 then validates parents and the path with ballots (or derives the
@@ -158,21 +134,14 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
             }
         }
         if (have_path) {
-            // suffix sums: sfx_j = sum of g over path entries j .. L-1
             const bool on = lane < L;
-            float sfx = on ? a.g[(size_t)(lo + pj) * a.Hv + h] : 0.f;
-            const float gj = sfx;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float up = __shfl_down(sfx, off);
-                if (lane + off < 64) sfx += up;
-            }
+            float coef, gam;
+            path_decay(lane, L, on ? a.g[(size_t)(lo + pj) * a.Hv + h] : 0.f, coef, gam);
             if (on) {
                 s_path[lane] = pj;
-                s_coef[lane] = expf(sfx - gj);   // D_aj: gates of the entries after j
+                s_coef[lane] = coef;   // D_aj: gates of the entries after j
             }
-            const float total = __shfl(sfx, 0);
-            if (lane == 0) s_gam = expf(total);
+            if (lane == 0) s_gam = gam;
         }
         if (lane == 0) {
             s_st = st;

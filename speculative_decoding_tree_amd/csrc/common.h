@@ -36,6 +36,13 @@ struct Args {
     float *survival;        // [T]
     uint8_t *keep;          // [T]
     int32_t *kept;          // [B]
+    // gdn_tree_commit_verify: the previous tree, whose accepted path is
+    // committed before the current tree is verified
+    int T_prev, max_nodes_prev;
+    const float *U_prev, *g_prev;
+    const uint16_t *k_prev;
+    const int32_t *node_offset_prev, *parent_prev;
+    int32_t *commit_status;
 };
 
 // Argument block of the tree-bias attention kernels.
@@ -78,14 +85,64 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b16) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Offsets check for request b: returns a GDN_TREE_S_* code and the row range.
-__device__ __forceinline__ int check_offsets(const Args &a, int b, int &lo, int &n) {
-    lo = a.node_offset[b];
-    const int hi = a.node_offset[b + 1];
+// Offsets check for request b of a tree with T rows: returns a GDN_TREE_S_*
+// code and the row range.
+__device__ __forceinline__ int check_offsets_at(const int32_t *node_offset, int T, int max_nodes, int b, int &lo,
+                                                int &n) {
+    lo = node_offset[b];
+    const int hi = node_offset[b + 1];
     n = hi - lo;
-    if (lo < 0 || hi < lo || hi > a.T) return GDN_TREE_S_BAD_OFFSETS;
-    if (n > a.max_nodes) return GDN_TREE_S_TOO_MANY;
+    if (lo < 0 || hi < lo || hi > T) return GDN_TREE_S_BAD_OFFSETS;
+    if (n > max_nodes) return GDN_TREE_S_TOO_MANY;
     return GDN_TREE_S_OK;
+}
+
+__device__ __forceinline__ int check_offsets(const Args &a, int b, int &lo, int &n) {
+    return check_offsets_at(a.node_offset, a.T, a.max_nodes, b, lo, n);
+}
+
+// Inclusive ancestor set of node acc (one wave, lane t = node t, p = parent of
+// node t or -1 past the tree, parents validated), by pointer doubling over
+// shuffles; 0 for acc = -1.
+__device__ __forceinline__ uint64_t ancestors_of(int lane, int N, int p, int acc) {
+    const bool live = lane < N;
+    int jp = live ? p : -1;
+    uint64_t m = live ? (1ull << lane) : 0ull;
+    while (__ballot(jp >= 0)) {
+        const int src = jp >= 0 ? jp : lane;
+        const uint64_t m_up = __shfl(m, src);
+        const int jp_up = __shfl(jp, src);
+        if (jp >= 0) {
+            m |= m_up;
+            jp = jp_up;
+        }
+    }
+    return acc >= 0 ? __shfl(m, acc) : 0ull;
+}
+
+// Node at position `lane` (root first) of the path set pm, or 0 past its end.
+__device__ __forceinline__ int path_entry(uint64_t pm, int lane) {
+    uint64_t m = pm;
+    for (int k = 0; k < lane && m; ++k) m &= m - 1;
+    return m ? __builtin_ctzll(m) : 0;
+}
+
+// Decay of a root-first path of L entries, entry j in lane j with its gate
+// gj: coef = exp(sum of g over the entries after j) (D_aj for the last entry
+// a) and gam = exp(sum of g over the whole path) (gamma_a), from a suffix
+// scan over shuffles.  Every commit kernel forms them this way, so their
+// results agree bit for bit.
+__device__ __forceinline__ void path_decay(int lane, int L, float gj, float &coef, float &gam) {
+    const bool on = lane < L;
+    float sfx = on ? gj : 0.f;
+    const float g0 = sfx;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float up = __shfl_down(sfx, off);
+        if (lane + off < 64) sfx += up;
+    }
+    coef = expf(sfx - g0);
+    gam = expf(__shfl(sfx, 0));
 }
 
 __device__ __forceinline__ int resolve_slot(const Args &a, int b) {

@@ -49,6 +49,7 @@ namespace gdn {
 namespace {
 
 constexpr int NT = 256;
+constexpr int PCHUNK = 16;   // accepted-path rows staged per pass (commit_verify)
 
 // Coefficient table T:
 //   T[t][q], q < dep(t) - 1 : A = beta_t D_tj (k_t.k_j) for the ancestor j of t at
@@ -57,12 +58,21 @@ constexpr int NT = 256;
 //   T[j][t], j <= t         : P_tj = D_tj (q_t.k_j) for ancestors j, 0 otherwise
 //                             (upper triangle, node-indexed: the A operand of the
 //                             output product (P masked) U)
-template <int NM>
+template <int NM, bool FUSED>
 struct VerifySmem {
     // Rows padded by two floats: rows eight apart (the four lane groups of an
     // output fragment read) fall on different banks.
     float ru[NM][D + 2];                       // staged Q and K rows, then R, then U after the solve
-    float T[NM][NM + 2];
+    union {
+        float T[NM][NM + 2];
+        // commit_verify, before the grams: D_aj k_j rows, then u_j rows, of a
+        // chunk of the previous tree's accepted path
+        float prow[FUSED ? 2 * PCHUNK : 1][D];
+    };
+    int cpath[FUSED ? 64 : 1];                 // commit_verify: the path, root first
+    float ccoef[FUSED ? 64 : 1];               // and its decay coefficients D_aj
+    float cgam;
+    int cL;
     __attribute__((aligned(16))) uint64_t anc[NM];
     __attribute__((aligned(16))) float gam[NM];
     __attribute__((aligned(16))) float beta[64];   // one per wave-0 lane (clamped copies past N)
@@ -107,7 +117,15 @@ __device__ __forceinline__ void lds_rows(const char *st, int row, int grp, u32x4
 // Occupancy: units of up to 32 nodes fit 128 registers and 23 KiB of LDS, so
 // four workgroups share a CU; the 64-node build needs 148 registers and 52 KiB
 // and runs three.
-template <int NM>
+//
+// FUSED (gdn_tree_commit_verify): before the verify, the previous tree's
+// accepted path is composed into the state while it sits in registers
+// (H' = gamma_a H0 + sum_j D_aj k_j u_j^T, in the order and precision of the
+// commit kernel), H' is written to S_out, and the verify runs on H'.  Wave 1
+// derives the path from the accepted node while the state is in flight; the
+// path's k and u rows are staged in LDS (in the coefficient table's space,
+// which holds nothing before the grams).
+template <int NM, bool FUSED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4 : 3))) void verify_kernel(Args a) {
     constexpr int KT = NM / 16;   // max 16-node tiles
     // The unit's Q and K rows are staged in the R/U area, which holds nothing
@@ -118,7 +136,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
     constexpr int KOFF = RU_BYTES - NM * 2 * D;
     static_assert(KOFF % 16 == 0, "staged rows are read 16 bytes at a time");
     static_assert(staging_rule_holds(NM, (D + 2) * 4), "an R tile would overwrite K rows still to be read");
-    __shared__ VerifySmem<NM> sm;
+    __shared__ VerifySmem<NM, FUSED> sm;
     char *const stq = reinterpret_cast<char *>(&sm.ru[0][0]);
     char *const stk = stq + KOFF;
 
@@ -135,7 +153,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
 
     const int slot = resolve_slot(a, b);
     float2 hraw[4][8];
-    const float *H = a.S0 + ((size_t)max(slot, 0) * a.Hv + h) * D * D + 8 * grp * D + c;
+    const size_t hoff = ((size_t)max(slot, 0) * a.Hv + h) * D * D + 8 * grp * D + c;
+    const float *H = a.S0 + hoff;
     auto issue_h0 = [&]() {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -145,9 +164,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
     };
     int lo, N;
     int st = check_offsets(a, b, lo, N);
-    if (st == GDN_TREE_S_BAD_OFFSETS) {
-        if (h == 0 && tid == 0 && a.status) a.status[b] = st;
-        return;
+    if constexpr (!FUSED) {
+        if (st == GDN_TREE_S_BAD_OFFSETS) {
+            if (h == 0 && tid == 0 && a.status) a.status[b] = st;
+            return;
+        }
+    } else if (st == GDN_TREE_S_BAD_OFFSETS) {
+        lo = N = 0;   // the tree's rows are unknown: none is read or written
     }
     const uint32_t krow = (uint32_t)a.Hk * D;   // q/k row stride (elements)
     const uint16_t *kbase = a.k + ((size_t)lo * a.Hk + hk) * D;
@@ -195,27 +218,156 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
                     vv[tau][i] = *reinterpret_cast<const uint32_t *>(
                         vbase + ((uint32_t)min(16 * tau + 4 * grp + i, N - 1) * vrow + c));
     };
-    if (st == GDN_TREE_S_OK && N > 0) {
-        if (w == 0) {
-            // wave 0 needs its per-node scalars first (tree pre-pass): they and
-            // the staged rows go out before its H0 slab, so waiting for them
-            // does not wait for the slab
-            const int tc = min(lane, N - 1);
-            const size_t gi = (size_t)(lo + tc) * a.Hv + h;
-            p_mine = a.parent[lo + tc];
-            g_mine = a.g[gi];
-            b_mine = a.beta[gi];
+    // commit_verify: the previous tree's offsets, and in wave 1 its parents and
+    // gates (lane t = node t, clamped), requested before anything else
+    int cst = GDN_TREE_S_OK, plo = 0, PN = 0, pp = -1, acc_node = -1;
+    float pg = 0.f;
+    if constexpr (FUSED) {
+        cst = check_offsets_at(a.node_offset_prev, a.T_prev, a.max_nodes_prev, b, plo, PN);
+        acc_node = a.accept_node[b];
+        if (w == 1 && cst == GDN_TREE_S_OK && PN > 0) {
+            const int tc = min(lane, PN - 1);
+            pp = a.parent_prev[plo + tc];
+            pg = a.g_prev[(size_t)(plo + tc) * a.Hv + h];
+        }
+    }
+    const bool tree_ok = st == GDN_TREE_S_OK && N > 0;
+    // wave 0 needs its per-node scalars first (tree pre-pass): they and the
+    // staged rows go out before its H0 slab, so waiting for them does not
+    // wait for the slab
+    auto issue_scalars = [&]() {
+        const int tc = min(lane, N - 1);
+        const size_t gi = (size_t)(lo + tc) * a.Hv + h;
+        p_mine = a.parent[lo + tc];
+        g_mine = a.g[gi];
+        b_mine = a.beta[gi];
+    };
+    auto check_parents = [&]() {
+        sm.beta[lane] = b_mine;
+        const bool bad = (lane < N) && (p_mine < -1 || p_mine >= lane);
+        const unsigned long long any = __ballot(bad);
+        if (lane == 0) sm.bad = any != 0ull;
+    };
+    if constexpr (!FUSED) {
+        if (tree_ok) {
+            if (w == 0) {
+                issue_scalars();
+                issue_rest();
+                issue_h0();
+                check_parents();
+            } else {
+                issue_rest();
+                issue_h0();
+            }
+        }
+    } else {
+        // the state is read whatever the tree holds (the commit needs it);
+        // one unconditional issue keeps the loads' waits exact
+        if (tree_ok) {
+            if (w == 0) issue_scalars();
             issue_rest();
-            issue_h0();
-            sm.beta[lane] = b_mine;
-            const bool bad = (lane < N) && (p_mine < -1 || p_mine >= lane);
-            const unsigned long long any = __ballot(bad);
-            if (lane == 0) sm.bad = any != 0ull;
-        } else {
-            issue_rest();
-            issue_h0();
+        }
+        issue_h0();
+        if (tree_ok && w == 0) check_parents();
+    }
+    if constexpr (FUSED) {
+        // ---- the previous tree's accepted path (wave 1), as the commit kernel derives it ----
+        if (w == 1) {
+            int L = 0, pj = 0;
+            if (cst == GDN_TREE_S_OK && __ballot(lane < PN && (pp < -1 || pp >= lane))) cst = GDN_TREE_S_BAD_PARENT;
+            if (cst == GDN_TREE_S_OK && slot < 0) cst = GDN_TREE_S_BAD_SLOT;
+            if (cst == GDN_TREE_S_OK && (acc_node < -1 || acc_node >= PN)) cst = GDN_TREE_S_BAD_ACCEPT;
+            if (cst == GDN_TREE_S_OK) {
+                const uint64_t pm = ancestors_of(lane, PN, lane < PN ? pp : -1, acc_node);
+                L = __popcll(pm);
+                pj = path_entry(pm, lane);
+            }
+            float coef, gam;
+            path_decay(lane, L, __shfl(pg, pj), coef, gam);
+            if (lane < L) {
+                sm.cpath[lane] = pj;
+                sm.ccoef[lane] = coef;
+            }
+            if (lane == 0) {
+                sm.cL = L;
+                sm.cgam = gam;
+                if (h == 0 && a.commit_status) a.commit_status[b] = cst;
+            }
         }
         lds_barrier();
+        // staged rows to LDS now, which frees their registers for the commit
+        if (tree_ok) {
+#pragma unroll
+            for (int tau = 0; tau < KT; ++tau)
+                if (tau < nkt) {
+                    const int row = 16 * tau + srow;
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4 *>(stq + stage_off(row, sch)) = row < N ? sq[tau] : z;
+                    *reinterpret_cast<u32x4 *>(stk + stage_off(row, sch)) = row < N ? sk[tau] : z;
+                }
+        }
+        // ---- commit: H' = gamma_a H0 + sum_j D_aj k_j u_j^T on this lane's 64 elements ----
+        const int L = sm.cL;
+        if (L > 0) {   // a valid path (L = 0 on every error)
+            const float gam = sm.cgam;
+            const int jr = tid >> 4, e0 = 8 * (tid & 15);   // staging: path row jr, elements e0 .. e0 + 7
+            for (int j0 = 0; j0 < L; j0 += PCHUNK) {
+                const int nj = min(PCHUNK, L - j0);
+                if (j0 > 0) lds_barrier();   // every wave has read the previous chunk
+                const int q = j0 + min(jr, nj - 1);
+                const int t = sm.cpath[q];
+                const u32x4 kr = *reinterpret_cast<const u32x4 *>(a.k_prev + ((size_t)(plo + t) * a.Hk + hk) * D + e0);
+                const float *up = a.U_prev + ((size_t)(plo + t) * a.Hv + h) * D + e0;
+                const float4 u0 = *reinterpret_cast<const float4 *>(up);
+                const float4 u1 = *reinterpret_cast<const float4 *>(up + 4);
+                const float cf = sm.ccoef[q];
+                if (j0 == 0) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) hraw[s][e] = make_float2(gam * hraw[s][e].x, gam * hraw[s][e].y);
+                }
+                float4 k0, k1;
+                k0.x = cf * bf16_lo(kr[0]);
+                k0.y = cf * bf16_hi(kr[0]);
+                k0.z = cf * bf16_lo(kr[1]);
+                k0.w = cf * bf16_hi(kr[1]);
+                k1.x = cf * bf16_lo(kr[2]);
+                k1.y = cf * bf16_hi(kr[2]);
+                k1.z = cf * bf16_lo(kr[3]);
+                k1.w = cf * bf16_hi(kr[3]);
+                *reinterpret_cast<float4 *>(&sm.prow[jr][e0]) = k0;
+                *reinterpret_cast<float4 *>(&sm.prow[jr][e0 + 4]) = k1;
+                *reinterpret_cast<float4 *>(&sm.prow[PCHUNK + jr][e0]) = u0;
+                *reinterpret_cast<float4 *>(&sm.prow[PCHUNK + jr][e0 + 4]) = u1;
+                lds_barrier();
+                for (int jj = 0; jj < nj; ++jj) {
+                    const float2 u = *reinterpret_cast<const float2 *>(&sm.prow[PCHUNK + jj][c]);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const float4 ka = *reinterpret_cast<const float4 *>(&sm.prow[jj][32 * s + 8 * grp]);
+                        const float4 kb = *reinterpret_cast<const float4 *>(&sm.prow[jj][32 * s + 8 * grp + 4]);
+                        const float kc[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            hraw[s][e].x = fmaf(kc[e], u.x, hraw[s][e].x);
+                            hraw[s][e].y = fmaf(kc[e], u.y, hraw[s][e].y);
+                        }
+                    }
+                }
+            }
+        }
+        if (slot >= 0 && (L > 0 || a.S_out != a.S0)) {
+            float *Ho = a.S_out + hoff;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) st_stream2(Ho + (32 * s + e) * D, hraw[s][e]);
+        }
+    } else if (tree_ok) {
+        lds_barrier();
+    }
+    if (tree_ok) {
         if (sm.bad) st = GDN_TREE_S_BAD_PARENT;
         else if (slot < 0) st = GDN_TREE_S_BAD_SLOT;
     }
@@ -300,14 +452,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
             blo[s][1][pr] = l1;
         }
     }
+    if constexpr (!FUSED) {
 #pragma unroll
-    for (int tau = 0; tau < KT; ++tau)
-        if (tau < nkt) {
-            const int row = 16 * tau + srow;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4 *>(stq + stage_off(row, sch)) = row < N ? sq[tau] : z;
-            *reinterpret_cast<u32x4 *>(stk + stage_off(row, sch)) = row < N ? sk[tau] : z;
-        }
+        for (int tau = 0; tau < KT; ++tau)
+            if (tau < nkt) {
+                const int row = 16 * tau + srow;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4 *>(stq + stage_off(row, sch)) = row < N ? sq[tau] : z;
+                *reinterpret_cast<u32x4 *>(stk + stage_off(row, sch)) = row < N ? sk[tau] : z;
+            }
+    }
     lds_barrier();   // ancestry, G, gamma, depths, levels and the staged rows visible
 
     // ---- grams against K^T for node columns 16 ct .. 16 ct + 15 (ancestor entries only) ----
@@ -523,17 +677,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
     }
 }
 
-}  // namespace
-
-hipError_t launch_verify(const Args &a, hipStream_t stream) {
+template <bool FUSED>
+hipError_t launch_verify_impl(const Args &a, hipStream_t stream) {
     const dim3 grid(xcd_grid(a.B * a.Hv)), block(NT);
     if (a.max_nodes <= 16)
-        verify_kernel<16><<<grid, block, 0, stream>>>(a);
+        verify_kernel<16, FUSED><<<grid, block, 0, stream>>>(a);
     else if (a.max_nodes <= 32)
-        verify_kernel<32><<<grid, block, 0, stream>>>(a);
+        verify_kernel<32, FUSED><<<grid, block, 0, stream>>>(a);
     else
-        verify_kernel<64><<<grid, block, 0, stream>>>(a);
+        verify_kernel<64, FUSED><<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
 }
+
+}  // namespace
+
+hipError_t launch_verify(const Args &a, hipStream_t stream) { return launch_verify_impl<false>(a, stream); }
+
+hipError_t launch_commit_verify(const Args &a, hipStream_t stream) { return launch_verify_impl<true>(a, stream); }
 
 }  // namespace gdn

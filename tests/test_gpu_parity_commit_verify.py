@@ -1,0 +1,186 @@
+"""GPU parity of gdn_tree_commit_verify: the commit of one tree's accepted node
+and the verify of the next tree, in one launch.
+
+It must equal gdn_tree_commit_node followed by gdn_tree_verify on the state
+that commit wrote, bit for bit (states, outputs, pseudo-values, masks and both
+statuses), and the oracle's commit-then-verify within the parity bar.  The
+build used follows the next tree's node cap (16, 32 or 64 nodes); accepted
+paths longer than 16 nodes take several staging passes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from helpers import TOL, anc_u64, host, matwise_rel_err, rowwise_rel_err, upload
+
+import speculative_decoding_tree_amd.gdn_tree as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _trees(seed, sizes):
+    rng = np.random.default_rng(seed)
+    return [W.random_tree(rng, n) if n > 0 else np.zeros(0, np.int32) for n in sizes]
+
+
+PAIRS = {
+    # previous tree, next tree (same B, Hv, Hk)
+    "mixed_to_mixed_nm64": lambda: (W.make_c5(per_kind=3, Hv=6, Hk=2), W.make_c5(seed=1, per_kind=3, Hv=6, Hk=2)),
+    "long_paths_to_nm64": lambda: (
+        W.make_custom([W.chain(64), W.chain(40), W.chain(17), np.zeros(0, np.int32), W.chain(16)],
+                      [63, 39, 16, -1, 15], Hv=4, Hk=2, seed=5),
+        W.make_custom(_trees(6, [64, 3, 0, 33, 1]), [0, 0, -1, 0, 0], Hv=4, Hk=2, seed=6)),
+    "c3_to_c3_nm16": lambda: (W.make_c3(B=16), W.make_c3(B=16, seed=1)),
+    "nm32_to_nm32": lambda: (
+        W.make_custom(_trees(10, [32, 17, 1, 16, 31, 24]), [5, 0, 0, -1, 30, 11], Hv=6, Hk=2, seed=7),
+        W.make_custom(_trees(11, [20, 32, 9, 0, 17, 30]), [0, 0, 0, -1, 0, 0], Hv=6, Hk=2, seed=8)),
+    "nm64_to_nm16": lambda: (
+        W.make_custom(_trees(12, [64, 50, 7, 33]), [20, 49, 6, 1], Hv=4, Hk=4, seed=9),
+        W.make_custom(_trees(13, [16, 1, 15, 9]), [0, 0, 0, 0], Hv=4, Hk=4, seed=10)),
+}
+
+
+def _zeros_like_outputs(C, dev):
+    return (torch.zeros((C.T, C.Hv, 128), dtype=torch.float32, device=dev),
+            torch.zeros((C.T, C.Hv, 128), dtype=torch.float32, device=dev),
+            torch.zeros((C.T,), dtype=torch.int64, device=dev))
+
+
+def run_pair(P, C, accept=None, state_slot=None, inplace=False, edit=None):
+    """Separate (commit_node, then verify on its state) and fused launches on the same inputs."""
+    dP, dC = upload(P), upload(C)
+    if edit is not None:
+        edit(dP, dC)
+    dev = dP["S0"].device
+    mnP, mnC = max(1, P.max_nodes), max(1, C.max_nodes)
+    acc = dP["accept_node"] if accept is None else torch.tensor(accept, dtype=torch.int32, device=dev)
+    ss = None if state_slot is None else torch.tensor(state_slot, dtype=torch.int32, device=dev)
+    _, U_P, _, _ = G.verify(dP["S0"], dP["q"], dP["k"], dP["v"], dP["g"], dP["beta"], dP["node_offset"],
+                            dP["parent"], max_nodes=mnP)
+    S_mid = dP["S0"].clone()
+    G.commit_node(dP["S0"], U_P, dP["k"], dP["g"], dP["node_offset"], dP["parent"], acc, max_nodes=mnP,
+                  S_out=S_mid, state_slot=ss)
+    cst_r = torch.empty((P.B,), dtype=torch.int32, device=dev)
+    G.commit_node(dP["S0"], U_P, dP["k"], dP["g"], dP["node_offset"], dP["parent"], acc, max_nodes=mnP,
+                  S_out=dP["S0"].clone(), state_slot=ss, status=cst_r)
+    out_r, U_r, anc_r = _zeros_like_outputs(C, dev)
+    _, _, _, st_r = G.verify(S_mid, dC["q"], dC["k"], dC["v"], dC["g"], dC["beta"], dC["node_offset"],
+                             dC["parent"], max_nodes=mnC, state_slot=ss, out=out_r, U=U_r, anc_mask=anc_r)
+    S_in = dP["S0"].clone()
+    out_f, U_f, anc_f = _zeros_like_outputs(C, dev)
+    prev = dict(U=U_P, k=dP["k"], g=dP["g"], node_offset=dP["node_offset"], parent=dP["parent"], max_nodes=mnP)
+    S_f, _, _, _, st_f, cst_f = G.commit_verify(
+        S_in, prev, acc, dC["q"], dC["k"], dC["v"], dC["g"], dC["beta"], dC["node_offset"], dC["parent"],
+        max_nodes=mnC, S_out=S_in if inplace else dP["S0"].clone(), state_slot=ss, out=out_f, U=U_f,
+        anc_mask=anc_f)
+    torch.cuda.synchronize()
+    return dict(S_r=host(S_mid), out_r=host(out_r), U_r=host(U_r), anc_r=anc_u64(anc_r), st_r=host(st_r),
+                cst_r=host(cst_r), S_f=host(S_f), out_f=host(out_f), U_f=host(U_f), anc_f=anc_u64(anc_f),
+                st_f=host(st_f), cst_f=host(cst_f), acc=host(acc), dP=dP, dC=dC)
+
+
+def assert_same_bits(res):
+    for a, b in (("S_r", "S_f"), ("out_r", "out_f"), ("U_r", "U_f")):
+        x, y = res[a], res[b]
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), (a, int((x.view(np.uint32) != y.view(np.uint32)).sum()))
+    assert np.array_equal(res["anc_r"], res["anc_f"])
+    assert np.array_equal(res["st_r"], res["st_f"])
+    assert np.array_equal(res["cst_r"], res["cst_f"])
+
+
+def oracle_check(P, C, res):
+    """The oracle: commit the previous tree's accepted path, then verify the next tree from that state."""
+    mnP, mnC = max(1, P.max_nodes), max(1, C.max_nodes)
+    po, plo, pso = O.accepted_path_batch(P.node_offset, P.parent, res["acc"], max_nodes=mnP)
+    S_mid, cso = O.commit_batch(P.S0, P.q64(), P.k64(), P.v64(), P.g, P.beta, P.node_offset, P.parent, po, plo,
+                                P.Hv, P.Hk, max_nodes=mnP)
+    assert np.array_equal(res["cst_f"], np.where(pso != 0, pso, cso))
+    Oo, Uo, anco, sto = O.verify_batch(S_mid, C.q64(), C.k64(), C.v64(), C.g, C.beta, C.node_offset, C.parent,
+                                       C.Hv, C.Hk, max_nodes=mnC)
+    assert np.array_equal(res["st_f"], sto)
+    assert np.array_equal(res["anc_f"], anco)
+    assert matwise_rel_err(res["S_f"], S_mid) <= TOL
+    ok = np.concatenate([np.arange(C.node_offset[b], C.node_offset[b + 1])
+                         for b in range(C.B) if sto[b] == 0] + [np.zeros(0, int)]).astype(int)
+    eo, eu = rowwise_rel_err(res["out_f"][ok], Oo[ok]), rowwise_rel_err(res["U_f"][ok], Uo[ok])
+    assert eo <= TOL and eu <= TOL, (eo, eu)
+
+
+@pytest.mark.parametrize("name", sorted(PAIRS))
+def test_commit_verify_equals_commit_node_then_verify(name):
+    P, C = PAIRS[name]()
+    res = run_pair(P, C)
+    assert_same_bits(res)
+    oracle_check(P, C, res)
+
+
+def test_commit_verify_inplace_keeps_unaccepted_states():
+    P, C = PAIRS["long_paths_to_nm64"]()
+    res = run_pair(P, C, inplace=True)
+    assert_same_bits(res)
+    # request 3 accepted nothing: its state is S0, bit for bit
+    assert np.array_equal(res["S_f"][3], P.S0[3])
+    oracle_check(P, C, res)
+
+
+def test_commit_verify_device_errors():
+    """Commit errors keep S0 and the next tree is verified from it; next-tree errors give NaN
+    outputs while the commit still lands; a bad slot writes no state."""
+    P, C = PAIRS["mixed_to_mixed_nm64"]()
+    accept = P.accept_node.copy()
+    accept[2] = P.nodes(2)        # outside [-1, N)
+    accept[3] = -1                # nothing accepted
+
+    def edit(dP, dC):
+        lo = int(P.node_offset[1])
+        if P.nodes(1) > 2:
+            dP["parent"][lo + 1] = 1  # parent[1] = 1 is not < 1
+        lo = int(C.node_offset[4])
+        if C.nodes(4) > 2:
+            dC["parent"][lo + 2] = 5
+    slots = list(range(P.B))
+    slots[5] = P.B + 3            # outside [0, n_slots)
+    res = run_pair(P, C, accept=accept, state_slot=slots, edit=edit)
+    assert_same_bits(res)
+    cst, st = res["cst_f"], res["st_f"]
+    if P.nodes(1) > 2:
+        assert cst[1] == O.STATUS_BAD_PARENT
+        assert np.array_equal(res["S_f"][1], P.S0[1])
+    assert cst[2] == O.STATUS_BAD_ACCEPT and np.array_equal(res["S_f"][2], P.S0[2])
+    assert cst[3] == O.STATUS_OK and np.array_equal(res["S_f"][3], P.S0[3])
+    assert cst[5] == O.STATUS_BAD_SLOT and st[5] == O.STATUS_BAD_SLOT
+    lo, hi = C.node_offset[5], C.node_offset[6]
+    assert np.isnan(res["out_f"][lo:hi]).all()
+    if C.nodes(4) > 2:
+        assert st[4] == O.STATUS_BAD_PARENT
+        lo, hi = C.node_offset[4], C.node_offset[5]
+        assert np.isnan(res["out_f"][lo:hi]).all() and np.isnan(res["U_f"][lo:hi]).all()
+        # the commit of request 4 still happened
+        assert cst[4] == O.STATUS_OK
+
+
+def test_commit_verify_rejects_overlap_and_mismatched_dims():
+    P, C = PAIRS["c3_to_c3_nm16"]()
+    dP, dC = upload(P), upload(C)
+    mn = max(1, P.max_nodes)
+    _, U_P, _, _ = G.verify(dP["S0"], dP["q"], dP["k"], dP["v"], dP["g"], dP["beta"], dP["node_offset"],
+                            dP["parent"], max_nodes=mn)
+    prev = dict(U=U_P, k=dP["k"], g=dP["g"], node_offset=dP["node_offset"], parent=dP["parent"], max_nodes=mn)
+    args = (dC["q"], dC["k"], dC["v"], dC["g"], dC["beta"], dC["node_offset"], dC["parent"])
+    with pytest.raises(G.GdnTreeError) as e:
+        G.commit_verify(dP["S0"], prev, dP["accept_node"], *args, max_nodes=mn, U=U_P)
+    assert e.value.code == -9
+    with pytest.raises(G.GdnTreeError) as e:
+        G.commit_verify(dP["S0"], prev, dP["accept_node"], *args, max_nodes=mn, out=U_P)
+    assert e.value.code == -9
+    torch.cuda.synchronize()
+
+
+def test_commit_verify_full_mixed_batch():
+    """The launch the benchmark times (256 mixed trees, 48 v-heads): fused equals the two calls bit for bit."""
+    P, C = W.make_c5(), W.make_c5(seed=1)
+    res = run_pair(P, C)
+    assert_same_bits(res)
+    assert (res["st_f"] == 0).all() and (res["cst_f"] == 0).all()
