@@ -360,8 +360,18 @@ def batch_one_row(args, stream):
                         anc_mask=anc, status=st, commit_status=plen, stream=stream)
 
     t_fused = _time_launches(fstep, max(20, args.steps), stream)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fstep(0)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    fgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(fgraph):
+        G.commit_verify(S0, prev, acc, q, k, v, g, beta, off, par, max_nodes=mn, S_out=S1, out=out2, U=U2,
+                        anc_mask=anc, status=st, commit_status=plen)
+    t_fgraph = _time_launches(lambda i: fgraph.replay(), max(20, args.steps), stream)
     return {"workload": "1 request, 6-node root-branch tree, Hv=32, Hk=16, d=128", "step_us": t,
-            "graph_step_us": t_graph, "commit_verify_step_us": t_fused}
+            "graph_step_us": t_graph, "commit_verify_step_us": t_fused, "commit_verify_graph_step_us": t_fgraph}
 
 
 def main():

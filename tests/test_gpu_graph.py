@@ -81,6 +81,42 @@ def test_verify_path_commit_step_replays_bit_exact():
     _replays_match(_capture(step), outputs, poison, ref)
 
 
+def test_commit_verify_step_replays_bit_exact():
+    """The one-launch step (previous tree's commit, next tree's verify) captured and replayed."""
+    P, C = W.make_c3(16), W.make_c3(16, seed=1)
+    uP, uC = upload(P), upload(C)
+    mn, d = P.max_nodes, uP["S0"].device
+    _, U_P, _, _ = G.verify(uP["S0"], uP["q"], uP["k"], uP["v"], uP["g"], uP["beta"], uP["node_offset"],
+                            uP["parent"], max_nodes=mn)
+    prev = dict(U=U_P, k=uP["k"], g=uP["g"], node_offset=uP["node_offset"], parent=uP["parent"], max_nodes=mn)
+    out = torch.empty((C.T, C.Hv, 128), dtype=torch.float32, device=d)
+    U = torch.empty_like(out)
+    anc = torch.empty((C.T,), dtype=torch.int64, device=d)
+    st = torch.empty((C.B,), dtype=torch.int32, device=d)
+    cst = torch.empty((C.B,), dtype=torch.int32, device=d)
+    S1 = torch.empty_like(uP["S0"])
+
+    def step():
+        G.commit_verify(uP["S0"], prev, uP["accept_node"], uC["q"], uC["k"], uC["v"], uC["g"], uC["beta"],
+                        uC["node_offset"], uC["parent"], max_nodes=mn, S_out=S1, out=out, U=U, anc_mask=anc,
+                        status=st, commit_status=cst)
+
+    step()
+    torch.cuda.synchronize()
+    outputs = (S1, out, U, anc, st, cst)
+    ref = [host(x).copy() for x in outputs]
+    assert (ref[-1] == 0).all() and (ref[-2] == 0).all()
+
+    def poison():
+        for x in (out, U, S1):
+            x.fill_(float("nan"))
+        for x in (st, cst):
+            x.fill_(-7)
+        anc.fill_(0)
+
+    _replays_match(_capture(step), outputs, poison, ref)
+
+
 @pytest.mark.parametrize("split", [None, 64])
 def test_attention_replays_bit_exact(split):
     # the scheduled launch is a counter-reset kernel plus the attention kernel
