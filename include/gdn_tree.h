@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define GDN_TREE_ABI_VERSION 1
+#define GDN_TREE_ABI_VERSION 2   /* 2: gdn_tree_commit_verify, GDN_TREE_E_OVERLAP */
 #define GDN_TREE_MAX_NODES 64   /* per request: one wave64 lane and one uint64 bit per node */
 #define GDN_TREE_HEAD_DIM 128
 

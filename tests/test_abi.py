@@ -14,11 +14,11 @@ def test_library_exports_every_declared_symbol():
     names = G.declared_symbols()
     assert {"gdn_tree_verify", "gdn_tree_commit", "gdn_tree_accepted_path", "gdn_tree_verify_storeall",
             "gdn_tree_commit_storeall", "gdn_tree_state_bytes", "gdn_tree_strerror",
-            "gdn_tree_abi_version", "gdn_tree_accept_greedy", "gdn_tree_accept_commit", "gdn_tree_commit_node", "gdn_tree_commit_replay", "gdn_tree_budget_select",
+            "gdn_tree_abi_version", "gdn_tree_accept_greedy", "gdn_tree_accept_commit", "gdn_tree_commit_node", "gdn_tree_commit_replay", "gdn_tree_budget_select", "gdn_tree_commit_verify",
             "gdn_tree_ancestry", "gdn_tree_attention", "gdn_tree_attention_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert G.abi_version() == 1
+    assert G.abi_version() == 2
 
 
 def test_header_constants_match_binding():
@@ -42,7 +42,7 @@ def test_attention_status_codes_agree_with_oracle_numbers():
 
 
 def test_strerror_never_null():
-    for c in range(-9, 10):
+    for c in range(-10, 10):
         assert isinstance(G.strerror(c), str) and G.strerror(c)
 
 
@@ -188,3 +188,39 @@ def test_commit_node_host_validation():
     assert L.gdn_tree_commit_node(ctypes.byref(bad), *args) == -4
     empty = G.make_dims(0, 4, 2, 0, 8, 2)
     assert L.gdn_tree_commit_node(ctypes.byref(empty), *nulls, None) == 0
+
+
+def _cv_args(**over):
+    """Pointer arguments of gdn_tree_commit_verify (after the two dims), all aligned fakes."""
+    names = ["S0", "S_out", "state_slot", "U_prev", "k_prev", "g_prev", "node_offset_prev", "parent_prev",
+             "accept_node", "commit_status", "q", "k", "v", "g", "beta", "node_offset", "parent", "out", "U",
+             "anc_mask", "status", "stream"]
+    vals = {n: ctypes.c_void_p(0x100000 * (i + 1)) for i, n in enumerate(names)}
+    for n in ("state_slot", "commit_status", "anc_mask", "status", "stream"):
+        vals[n] = None
+    vals.update(over)
+    return [vals[n] for n in names]
+
+
+def test_commit_verify_host_validation():
+    L = G.lib()
+    pd, d = G.make_dims(4, 32, 16, 20, 8, 4), G.make_dims(4, 32, 16, 24, 8, 4)
+    cv = lambda a, b, **o: L.gdn_tree_commit_verify(ctypes.byref(a), ctypes.byref(b), *_cv_args(**o))
+    # the two trees must share B, Hv, Hk and n_slots
+    for field, val in (("B", 5), ("Hv", 16), ("Hk", 8), ("n_slots", 5)):
+        bad = G.make_dims(4, 32, 16, 20, 8, 4)
+        setattr(bad, field, val)
+        assert cv(bad, d) == -2, field
+    bad = G.make_dims(4, 32, 16, 20, 65, 4)
+    assert cv(bad, d) == -4 and cv(pd, bad) == -4
+    assert L.gdn_tree_commit_verify(None, ctypes.byref(d), *_cv_args()) == -1
+    for name in ("S0", "S_out", "node_offset", "node_offset_prev", "accept_node", "U_prev", "k_prev", "q", "U"):
+        assert cv(pd, d, **{name: None}) == -1, name
+    assert cv(pd, d, k_prev=ctypes.c_void_p(0x100008)) == -7
+    # out or U overlapping the previous tree's U rows (20 x 32 x 128 floats)
+    up = 0x100000 * 4
+    assert cv(pd, d, U=ctypes.c_void_p(up + 20 * 32 * 128 * 4 - 16)) == -9
+    assert cv(pd, d, out=ctypes.c_void_p(up)) == -9
+    assert "overlap" in G.strerror(-9)
+    empty_p, empty = G.make_dims(0, 32, 16, 0, 8, 1), G.make_dims(0, 32, 16, 0, 8, 1)
+    assert L.gdn_tree_commit_verify(ctypes.byref(empty_p), ctypes.byref(empty), *([None] * 22)) == 0
