@@ -184,3 +184,12 @@ def test_commit_verify_full_mixed_batch():
     res = run_pair(P, C)
     assert_same_bits(res)
     assert (res["st_f"] == 0).all() and (res["cst_f"] == 0).all()
+
+
+def test_commit_verify_state_slot_permutation():
+    """Requests read and write their state through state_slot (a permutation here), in place."""
+    P, C = PAIRS["nm32_to_nm32"]()
+    slots = list(reversed(range(P.B)))
+    res = run_pair(P, C, state_slot=slots, inplace=True)
+    assert_same_bits(res)
+    assert (res["st_f"] == 0).all() and (res["cst_f"] == 0).all()
