@@ -312,9 +312,10 @@ def attention_row(args, stream):
 
 
 def batch_one_row(args, stream):
-    """Latency of one verify + commit_node step at batch one: the
-    6-node root-branch tree of one request, 32 value / 16 key heads (the
-    shape of the batch-one decode gate the pages report)."""
+    """Latency of one step at batch one, as verify + commit_node launches
+    (eager and captured in a HIP graph) and as one commit_verify launch (eager
+    and captured): the 6-node root-branch tree of one request, 32 value / 16
+    key heads (the shape of the batch-one decode gate the pages report)."""
     import numpy as np
     import torch
     import workloads as W
