@@ -245,6 +245,19 @@ def next_rows(args, wl, pools, mn, stream):
                         kept=kept, status=st, stream=stream)
 
     t_budget = _time_launches(budget, n, stream)
+    # greedy acceptance, commit and the next tree's verify in one launch
+    cst2 = torch.empty((B,), dtype=torch.int32, device=dev)
+    tok = dict(draft_token=dt, target_token=tg, root_token=rt)
+
+    def greedy_step(i):
+        p = pools[i % len(pools)]
+        prev = dict(U=p["U"], k=p["k"], g=p["g"], node_offset=p["off"], parent=p["par"], max_nodes=mn)
+        G.commit_verify(p["S0"], prev, acc, p["q"], p["k"], p["v"], p["g"], p["beta"], p["off"], p["par"],
+                        max_nodes=mn, S_out=p["S_out"], out=p["out2"], U=p["U2"], anc_mask=p["anc"], status=st,
+                        commit_status=cst2, stream=stream, greedy=tok)
+
+    t_gcv = _time_launches(greedy_step, n, stream)
+    gcv_b = verify_bytes(wl) + cb - wl.B * wl.Hv * D * D * 4
     return {"accepted_path_then_commit": {"accepted_path_avg_us": t_path, "commit_avg_us": t_commit,
                                           "commit_alg_GBps": cb_step / (t_commit * 1e-6) / 1e9,
                                           "commit_hbm_frac": cb_step / (t_commit * 1e-6) / 1e9 / HBM_PEAK_GBS},
@@ -253,6 +266,9 @@ def next_rows(args, wl, pools, mn, stream):
                               "hbm_frac": rb / (t_replay * 1e-6) / 1e9 / HBM_PEAK_GBS,
                               "mean_accepted_len": float(Lr.mean())},
             "accept_greedy": {"avg_us": t_greedy, "mean_accepted_len": float(L.mean())},
+            "accept_commit_verify": {"avg_us": t_gcv, "alg_bytes": gcv_b,
+                                     "alg_GBps": gcv_b / (t_gcv * 1e-6) / 1e9,
+                                     "hbm_frac": gcv_b / (t_gcv * 1e-6) / 1e9 / HBM_PEAK_GBS},
             "accept_commit_fused": {"avg_us": t_fused, "alg_bytes": cb,
                                     "alg_GBps": cb / (t_fused * 1e-6) / 1e9,
                                     "hbm_frac": cb / (t_fused * 1e-6) / 1e9 / HBM_PEAK_GBS}}

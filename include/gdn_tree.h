@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define GDN_TREE_ABI_VERSION 2   /* 2: gdn_tree_commit_verify, GDN_TREE_E_OVERLAP */
+#define GDN_TREE_ABI_VERSION 2   /* 2: gdn_tree_commit_verify, gdn_tree_accept_commit_verify, GDN_TREE_E_OVERLAP */
 #define GDN_TREE_MAX_NODES 64   /* per request: one wave64 lane and one uint64 bit per node */
 #define GDN_TREE_HEAD_DIM 128
 
@@ -248,6 +248,29 @@ int gdn_tree_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *
                            const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                            const float *beta, const int32_t *node_offset, const int32_t *parent, float *out,
                            float *U, uint64_t *anc_mask, int32_t *status, void *stream);
+
+/*
+ * gdn_tree_accept_commit_verify -- gdn_tree_commit_verify with the previous
+ * tree's accepted node chosen on the device by the greedy walk of
+ * gdn_tree_accept_greedy (TreeWY, "Results": greedy drafting and
+ * verification; GDN Tree-Scan, abstract: device-side choice of the committed
+ * draft), in the same launch: the acceptance, the commit and the next tree's
+ * verify take one launch per layer.  draft_token and target_token (int32
+ * [T_prev]) and root_token (int32 [B]) are the previous tree's token ids as
+ * gdn_tree_accept_greedy takes them; accept_node (int32 [B], optional output)
+ * receives the node the walk accepted (-1 when none, or on a commit error).
+ * Results equal gdn_tree_accept_commit followed by gdn_tree_verify bit for
+ * bit; everything else is as in gdn_tree_commit_verify.
+ */
+int gdn_tree_accept_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *dims, const float *S0,
+                                  float *S_out, const int32_t *state_slot, const float *U_prev,
+                                  const uint16_t *k_prev, const float *g_prev, const int32_t *node_offset_prev,
+                                  const int32_t *parent_prev, const int32_t *draft_token,
+                                  const int32_t *target_token, const int32_t *root_token, int32_t *accept_node,
+                                  int32_t *commit_status, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                  const float *g, const float *beta, const int32_t *node_offset,
+                                  const int32_t *parent, float *out, float *U, uint64_t *anc_mask,
+                                  int32_t *status, void *stream);
 
 /*
  * gdn_tree_accept_commit -- greedy acceptance fused with the commit, in one

@@ -304,22 +304,28 @@ int gdn_tree_commit_node(const gdn_tree_dims *dims, const float *S0, float *S_ou
     return finish(gdn::launch_commit_node(a, (hipStream_t)stream));
 }
 
-int gdn_tree_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *dims, const float *S0, float *S_out,
-                           const int32_t *state_slot, const float *U_prev, const uint16_t *k_prev,
-                           const float *g_prev, const int32_t *node_offset_prev, const int32_t *parent_prev,
-                           const int32_t *accept_node, int32_t *commit_status, const uint16_t *q,
-                           const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
-                           const int32_t *node_offset, const int32_t *parent, float *out, float *U,
-                           uint64_t *anc_mask, int32_t *status, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and argument block shared by the one-launch commit + verify entry
+// points; returns a GDN_TREE_* code (GDN_TREE_OK with a.B == 0: nothing to do).
+int commit_verify_args(Args &a, const gdn_tree_dims *prev_dims, const gdn_tree_dims *dims, const float *S0,
+                       float *S_out, const int32_t *state_slot, const float *U_prev, const uint16_t *k_prev,
+                       const float *g_prev, const int32_t *node_offset_prev, const int32_t *parent_prev,
+                       int32_t *commit_status, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       const float *g, const float *beta, const int32_t *node_offset, const int32_t *parent,
+                       float *out, float *U, uint64_t *anc_mask, int32_t *status) {
     int rc = check_dims(prev_dims);
     if (rc != GDN_TREE_OK) return rc;
     rc = check_dims(dims);
     if (rc != GDN_TREE_OK) return rc;
     if (prev_dims->B != dims->B) return GDN_TREE_E_DIMS;
+    a = base_args(dims);
     if (dims->B == 0) return GDN_TREE_OK;
     if (prev_dims->Hv != dims->Hv || prev_dims->Hk != dims->Hk || prev_dims->n_slots != dims->n_slots)
         return GDN_TREE_E_DIMS;
-    if (!S0 || !S_out || !node_offset || !node_offset_prev || !accept_node) return GDN_TREE_E_NULL;
+    if (!S0 || !S_out || !node_offset || !node_offset_prev) return GDN_TREE_E_NULL;
     if (prev_dims->T > 0 && (!U_prev || !k_prev || !g_prev || !parent_prev)) return GDN_TREE_E_NULL;
     if (dims->T > 0 && (!q || !k || !v || !g || !beta || !parent || !out || !U)) return GDN_TREE_E_NULL;
     if (any_misaligned(S0, S_out, U_prev, k_prev, q, k, v, out, U)) return GDN_TREE_E_ALIGN;
@@ -330,7 +336,6 @@ int gdn_tree_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *
         return x && U_prev && rows && rows_prev && x < U_prev + rows_prev && U_prev < x + rows;
     };
     if (overlaps(U) || overlaps(out)) return GDN_TREE_E_OVERLAP;
-    Args a = base_args(dims);
     a.S0 = S0;
     a.S_out = S_out;
     a.state_slot = state_slot;
@@ -341,7 +346,6 @@ int gdn_tree_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *
     a.g_prev = g_prev;
     a.node_offset_prev = node_offset_prev;
     a.parent_prev = parent_prev;
-    a.accept_node = accept_node;
     a.commit_status = commit_status;
     a.q = q;
     a.k = k;
@@ -354,8 +358,52 @@ int gdn_tree_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *
     a.U = U;
     a.anc_mask = anc_mask;
     a.status = status;
+    return GDN_TREE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_tree_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *dims, const float *S0, float *S_out,
+                           const int32_t *state_slot, const float *U_prev, const uint16_t *k_prev,
+                           const float *g_prev, const int32_t *node_offset_prev, const int32_t *parent_prev,
+                           const int32_t *accept_node, int32_t *commit_status, const uint16_t *q,
+                           const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
+                           const int32_t *node_offset, const int32_t *parent, float *out, float *U,
+                           uint64_t *anc_mask, int32_t *status, void *stream) {
+    Args a;
+    int rc = commit_verify_args(a, prev_dims, dims, S0, S_out, state_slot, U_prev, k_prev, g_prev, node_offset_prev,
+                                parent_prev, commit_status, q, k, v, g, beta, node_offset, parent, out, U, anc_mask,
+                                status);
+    if (rc != GDN_TREE_OK || a.B == 0) return rc;
+    if (!accept_node) return GDN_TREE_E_NULL;
+    a.accept_node = accept_node;
     clear_pending();
     return finish(gdn::launch_commit_verify(a, (hipStream_t)stream));
+}
+
+int gdn_tree_accept_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *dims, const float *S0,
+                                  float *S_out, const int32_t *state_slot, const float *U_prev,
+                                  const uint16_t *k_prev, const float *g_prev, const int32_t *node_offset_prev,
+                                  const int32_t *parent_prev, const int32_t *draft_token,
+                                  const int32_t *target_token, const int32_t *root_token, int32_t *accept_node,
+                                  int32_t *commit_status, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                  const float *g, const float *beta, const int32_t *node_offset,
+                                  const int32_t *parent, float *out, float *U, uint64_t *anc_mask,
+                                  int32_t *status, void *stream) {
+    Args a;
+    int rc = commit_verify_args(a, prev_dims, dims, S0, S_out, state_slot, U_prev, k_prev, g_prev, node_offset_prev,
+                                parent_prev, commit_status, q, k, v, g, beta, node_offset, parent, out, U, anc_mask,
+                                status);
+    if (rc != GDN_TREE_OK || a.B == 0) return rc;
+    if (!root_token || (prev_dims->T > 0 && (!draft_token || !target_token))) return GDN_TREE_E_NULL;
+    a.draft_token = draft_token;
+    a.target_token = target_token;
+    a.root_token = root_token;
+    a.accept_out = accept_node;
+    clear_pending();
+    return finish(gdn::launch_accept_commit_verify(a, (hipStream_t)stream));
 }
 
 int gdn_tree_budget_select(const gdn_tree_dims *dims, const int32_t *node_offset, const int32_t *parent,

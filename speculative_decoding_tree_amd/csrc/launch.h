@@ -10,6 +10,7 @@ namespace gdn {
 
 hipError_t launch_verify(const Args &a, hipStream_t stream);
 hipError_t launch_commit_verify(const Args &a, hipStream_t stream);
+hipError_t launch_accept_commit_verify(const Args &a, hipStream_t stream);
 hipError_t launch_commit(const Args &a, hipStream_t stream);
 hipError_t launch_accepted_path(const Args &a, hipStream_t stream);
 hipError_t launch_accept_greedy(const Args &a, hipStream_t stream);

@@ -118,15 +118,18 @@ __device__ __forceinline__ void lds_rows(const char *st, int row, int grp, u32x4
 // four workgroups share a CU; the 64-node build needs 148 registers and 52 KiB
 // and runs three.
 //
-// FUSED (gdn_tree_commit_verify): before the verify, the previous tree's
-// accepted path is composed into the state while it sits in registers
-// (H' = gamma_a H0 + sum_j D_aj k_j u_j^T, in the order and precision of the
-// commit kernel), H' is written to S_out, and the verify runs on H'.  Wave 1
-// derives the path from the accepted node while the state is in flight; the
-// path's k and u rows are staged in LDS (in the coefficient table's space,
-// which holds nothing before the grams).
-template <int NM, bool FUSED>
+// MODE 1 (gdn_tree_commit_verify) and 2 (gdn_tree_accept_commit_verify):
+// before the verify, the previous tree's accepted path is composed into the
+// state while it sits in registers (H' = gamma_a H0 + sum_j D_aj k_j u_j^T,
+// in the order and precision of the commit kernel), H' is written to S_out,
+// and the verify runs on H'.  Wave 1 derives the path while the state is in
+// flight: from the accepted node (MODE 1), or by the greedy walk over the
+// previous tree's draft and target tokens (MODE 2).  The path's k and u rows
+// are staged in LDS (in the coefficient table's space, which holds nothing
+// before the grams).
+template <int NM, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4 : 3))) void verify_kernel(Args a) {
+    constexpr bool FUSED = MODE != 0, GREEDY = MODE == 2;
     constexpr int KT = NM / 16;   // max 16-node tiles
     // The unit's Q and K rows are staged in the R/U area, which holds nothing
     // before the K pass writes R: Q rows from its start (dead after the Q
@@ -220,15 +223,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
     };
     // commit_verify: the previous tree's offsets, and in wave 1 its parents and
     // gates (lane t = node t, clamped), requested before anything else
-    int cst = GDN_TREE_S_OK, plo = 0, PN = 0, pp = -1, acc_node = -1;
+    // (greedy: also its draft and target tokens, and the root's target token)
+    int cst = GDN_TREE_S_OK, plo = 0, PN = 0, pp = -1, acc_node = -1, root_tok = 0, dtok = 0, ttok = 0;
     float pg = 0.f;
     if constexpr (FUSED) {
         cst = check_offsets_at(a.node_offset_prev, a.T_prev, a.max_nodes_prev, b, plo, PN);
-        acc_node = a.accept_node[b];
+        if constexpr (GREEDY) root_tok = a.root_token[b];
+        else acc_node = a.accept_node[b];
         if (w == 1 && cst == GDN_TREE_S_OK && PN > 0) {
             const int tc = min(lane, PN - 1);
             pp = a.parent_prev[plo + tc];
             pg = a.g_prev[(size_t)(plo + tc) * a.Hv + h];
+            if constexpr (GREEDY) {
+                dtok = a.draft_token[plo + tc];
+                ttok = a.target_token[plo + tc];
+            }
         }
     }
     const bool tree_ok = st == GDN_TREE_S_OK && N > 0;
@@ -273,12 +282,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
     if constexpr (FUSED) {
         // ---- the previous tree's accepted path (wave 1), as the commit kernel derives it ----
         if (w == 1) {
-            int L = 0, pj = 0;
+            int L = 0, pj = 0, accept = -1;
             if (cst == GDN_TREE_S_OK && __ballot(lane < PN && (pp < -1 || pp >= lane))) cst = GDN_TREE_S_BAD_PARENT;
             if (cst == GDN_TREE_S_OK && slot < 0) cst = GDN_TREE_S_BAD_SLOT;
-            if (cst == GDN_TREE_S_OK && (acc_node < -1 || acc_node >= PN)) cst = GDN_TREE_S_BAD_ACCEPT;
+            if (!GREEDY && cst == GDN_TREE_S_OK && (acc_node < -1 || acc_node >= PN)) cst = GDN_TREE_S_BAD_ACCEPT;
             if (cst == GDN_TREE_S_OK) {
-                const uint64_t pm = ancestors_of(lane, PN, lane < PN ? pp : -1, acc_node);
+                uint64_t pm = 0;
+                if constexpr (GREEDY) {
+                    // from the committed root, enter the first child in index order
+                    // whose draft token is the target's prediction, until none is
+                    int want = root_tok;
+                    for (int step = 0; step < PN; ++step) {
+                        const uint64_t mk = __ballot(lane < PN && pp == accept && dtok == want);
+                        if (!mk) break;
+                        accept = __builtin_ctzll(mk);
+                        pm |= 1ull << accept;
+                        want = __shfl(ttok, accept);
+                    }
+                } else {
+                    pm = ancestors_of(lane, PN, lane < PN ? pp : -1, acc_node);
+                }
                 L = __popcll(pm);
                 pj = path_entry(pm, lane);
             }
@@ -292,6 +315,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
                 sm.cL = L;
                 sm.cgam = gam;
                 if (h == 0 && a.commit_status) a.commit_status[b] = cst;
+                if (GREEDY && h == 0 && a.accept_out) a.accept_out[b] = accept;
             }
         }
         lds_barrier();
@@ -677,22 +701,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
     }
 }
 
-template <bool FUSED>
+template <int MODE>
 hipError_t launch_verify_impl(const Args &a, hipStream_t stream) {
     const dim3 grid(xcd_grid(a.B * a.Hv)), block(NT);
     if (a.max_nodes <= 16)
-        verify_kernel<16, FUSED><<<grid, block, 0, stream>>>(a);
+        verify_kernel<16, MODE><<<grid, block, 0, stream>>>(a);
     else if (a.max_nodes <= 32)
-        verify_kernel<32, FUSED><<<grid, block, 0, stream>>>(a);
+        verify_kernel<32, MODE><<<grid, block, 0, stream>>>(a);
     else
-        verify_kernel<64, FUSED><<<grid, block, 0, stream>>>(a);
+        verify_kernel<64, MODE><<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_verify(const Args &a, hipStream_t stream) { return launch_verify_impl<false>(a, stream); }
+hipError_t launch_verify(const Args &a, hipStream_t stream) { return launch_verify_impl<0>(a, stream); }
 
-hipError_t launch_commit_verify(const Args &a, hipStream_t stream) { return launch_verify_impl<true>(a, stream); }
+hipError_t launch_commit_verify(const Args &a, hipStream_t stream) { return launch_verify_impl<1>(a, stream); }
+
+hipError_t launch_accept_commit_verify(const Args &a, hipStream_t stream) {
+    return launch_verify_impl<2>(a, stream);
+}
 
 }  // namespace gdn

@@ -69,6 +69,7 @@ _SIGS = {
     "gdn_tree_accept_commit": [ctypes.POINTER(Dims)] + [_P] * 16,
     "gdn_tree_commit_node": [ctypes.POINTER(Dims)] + [_P] * 13,
     "gdn_tree_commit_verify": [ctypes.POINTER(Dims), ctypes.POINTER(Dims)] + [_P] * 22,
+    "gdn_tree_accept_commit_verify": [ctypes.POINTER(Dims), ctypes.POINTER(Dims)] + [_P] * 25,
     "gdn_tree_commit_replay": [ctypes.POINTER(Dims)] + [_P] * 13,
     "gdn_tree_budget_select": [ctypes.POINTER(Dims), _P, _P, _P, ctypes.c_int32, ctypes.c_float,
                                _P, _P, _P, _P, _P],
@@ -380,11 +381,13 @@ def commit_node(S0, U, k, g, node_offset, parent, accept_node, max_nodes: int, S
 
 def commit_verify(S0, prev, accept_node, q, k, v, g, beta, node_offset, parent, max_nodes: int, S_out=None,
                   state_slot=None, out=None, U=None, anc_mask=None, status=None, commit_status=None,
-                  stream=None):
+                  stream=None, greedy=None):
     """gdn_tree_commit_verify: commit the previous tree's accepted node into S_out, then verify the
     next tree from that state, in one launch.  ``prev`` is a dict with the previous tree's
     ``U``, ``k``, ``g``, ``node_offset``, ``parent`` and ``max_nodes``.
-    Returns (S_out, out, U, anc_mask, status, commit_status); outputs not given are allocated."""
+    With ``greedy`` = dict(draft_token, target_token, root_token) the accepted node comes from the
+    device-side greedy walk instead (gdn_tree_accept_commit_verify) and ``accept_node`` is an
+    optional output.  Returns (S_out, out, U, anc_mask, status, commit_status[, accept_node])."""
     B, Hv, Hk, T, n_slots = _geometry(S0, q, v, node_offset, parent, max_nodes)
     U_p, k_p, g_p, off_p, par_p = prev["U"], prev["k"], prev["g"], prev["node_offset"], prev["parent"]
     T_p = int(par_p.numel())
@@ -398,24 +401,34 @@ def commit_verify(S0, prev, accept_node, q, k, v, g, beta, node_offset, parent, 
                      else torch.empty((B,), dtype=torch.int32, device=dev))
     pdims = make_dims(int(off_p.numel()) - 1, Hv, Hk, T_p, prev["max_nodes"], n_slots)
     dims = make_dims(B, Hv, Hk, T, max_nodes, n_slots)
-    rc = lib().gdn_tree_commit_verify(
-        ctypes.byref(pdims), ctypes.byref(dims),
-        _ptr(S0, "S0", _F32, (n_slots, Hv, HEAD_DIM, HEAD_DIM)),
-        _ptr(S_out, "S_out", _F32, (n_slots, Hv, HEAD_DIM, HEAD_DIM)),
-        _ptr(state_slot, "state_slot", _I32, (B,)),
-        _ptr(U_p, "prev U", _F32, (T_p, Hv, HEAD_DIM)), _ptr(k_p, "prev k", _B16, (T_p, Hk, HEAD_DIM)),
-        _ptr(g_p, "prev g", _F32, (T_p, Hv)),
-        _ptr(off_p, "prev node_offset", _I32, (B + 1,)), _ptr(par_p, "prev parent", _I32, (T_p,)),
-        _ptr(accept_node, "accept_node", _I32, (B,)), _ptr(commit_status, "commit_status", _I32, (B,)),
-        _ptr(q, "q", _B16, (T, Hk, HEAD_DIM)), _ptr(k, "k", _B16, (T, Hk, HEAD_DIM)),
-        _ptr(v, "v", _B16, (T, Hv, HEAD_DIM)),
-        _ptr(g, "g", _F32, (T, Hv)), _ptr(beta, "beta", _F32, (T, Hv)),
-        _ptr(node_offset, "node_offset", _I32, (B + 1,)), _ptr(parent, "parent", _I32, (T,)),
-        _ptr(out, "out", _F32, (T, Hv, HEAD_DIM)), _ptr(U, "U", _F32, (T, Hv, HEAD_DIM)),
-        _ptr(anc_mask, "anc_mask", _U64, (T,)), _ptr(status, "status", _I32, (B,)),
-        _stream(stream))
-    _check("gdn_tree_commit_verify", rc)
-    return S_out, out, U, anc_mask, status, commit_status
+    head = [ctypes.byref(pdims), ctypes.byref(dims),
+            _ptr(S0, "S0", _F32, (n_slots, Hv, HEAD_DIM, HEAD_DIM)),
+            _ptr(S_out, "S_out", _F32, (n_slots, Hv, HEAD_DIM, HEAD_DIM)),
+            _ptr(state_slot, "state_slot", _I32, (B,)),
+            _ptr(U_p, "prev U", _F32, (T_p, Hv, HEAD_DIM)), _ptr(k_p, "prev k", _B16, (T_p, Hk, HEAD_DIM)),
+            _ptr(g_p, "prev g", _F32, (T_p, Hv)),
+            _ptr(off_p, "prev node_offset", _I32, (B + 1,)), _ptr(par_p, "prev parent", _I32, (T_p,))]
+    tail = [_ptr(q, "q", _B16, (T, Hk, HEAD_DIM)), _ptr(k, "k", _B16, (T, Hk, HEAD_DIM)),
+            _ptr(v, "v", _B16, (T, Hv, HEAD_DIM)),
+            _ptr(g, "g", _F32, (T, Hv)), _ptr(beta, "beta", _F32, (T, Hv)),
+            _ptr(node_offset, "node_offset", _I32, (B + 1,)), _ptr(parent, "parent", _I32, (T,)),
+            _ptr(out, "out", _F32, (T, Hv, HEAD_DIM)), _ptr(U, "U", _F32, (T, Hv, HEAD_DIM)),
+            _ptr(anc_mask, "anc_mask", _U64, (T,)), _ptr(status, "status", _I32, (B,)),
+            _stream(stream)]
+    if greedy is None:
+        rc = lib().gdn_tree_commit_verify(
+            *head, _ptr(accept_node, "accept_node", _I32, (B,)),
+            _ptr(commit_status, "commit_status", _I32, (B,)), *tail)
+        _check("gdn_tree_commit_verify", rc)
+        return S_out, out, U, anc_mask, status, commit_status
+    accept_node = accept_node if accept_node is not None else torch.empty((B,), dtype=torch.int32, device=dev)
+    rc = lib().gdn_tree_accept_commit_verify(
+        *head, _ptr(greedy["draft_token"], "draft_token", _I32, (T_p,)),
+        _ptr(greedy["target_token"], "target_token", _I32, (T_p,)),
+        _ptr(greedy["root_token"], "root_token", _I32, (B,)), _ptr(accept_node, "accept_node", _I32, (B,)),
+        _ptr(commit_status, "commit_status", _I32, (B,)), *tail)
+    _check("gdn_tree_accept_commit_verify", rc)
+    return S_out, out, U, anc_mask, status, commit_status, accept_node
 
 
 def commit_replay(S0, k, v, g, beta, node_offset, parent, path, path_len, max_nodes: int, S_out=None,

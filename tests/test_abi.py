@@ -14,7 +14,7 @@ def test_library_exports_every_declared_symbol():
     names = G.declared_symbols()
     assert {"gdn_tree_verify", "gdn_tree_commit", "gdn_tree_accepted_path", "gdn_tree_verify_storeall",
             "gdn_tree_commit_storeall", "gdn_tree_state_bytes", "gdn_tree_strerror",
-            "gdn_tree_abi_version", "gdn_tree_accept_greedy", "gdn_tree_accept_commit", "gdn_tree_commit_node", "gdn_tree_commit_replay", "gdn_tree_budget_select", "gdn_tree_commit_verify",
+            "gdn_tree_abi_version", "gdn_tree_accept_greedy", "gdn_tree_accept_commit", "gdn_tree_commit_node", "gdn_tree_commit_replay", "gdn_tree_budget_select", "gdn_tree_commit_verify", "gdn_tree_accept_commit_verify",
             "gdn_tree_ancestry", "gdn_tree_attention", "gdn_tree_attention_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -224,3 +224,22 @@ def test_commit_verify_host_validation():
     assert "overlap" in G.strerror(-9)
     empty_p, empty = G.make_dims(0, 32, 16, 0, 8, 1), G.make_dims(0, 32, 16, 0, 8, 1)
     assert L.gdn_tree_commit_verify(ctypes.byref(empty_p), ctypes.byref(empty), *([None] * 22)) == 0
+
+
+def test_accept_commit_verify_host_validation():
+    L = G.lib()
+    pd, d = G.make_dims(4, 32, 16, 20, 8, 4), G.make_dims(4, 32, 16, 24, 8, 4)
+    fake = lambda i: ctypes.c_void_p(0x4000000 + 0x100000 * i)
+
+    def acv(**over):
+        a = _cv_args()
+        head, tail = a[:8], a[10:]        # drop accept_node and commit_status
+        toks = {"draft_token": fake(1), "target_token": fake(2), "root_token": fake(3), "accept_node": None}
+        toks.update(over)
+        return L.gdn_tree_accept_commit_verify(ctypes.byref(pd), ctypes.byref(d), *head, toks["draft_token"],
+                                               toks["target_token"], toks["root_token"], toks["accept_node"],
+                                               None, *tail)
+    for name in ("draft_token", "target_token", "root_token"):
+        assert acv(**{name: None}) == -1, name
+    bad = G.make_dims(4, 32, 8, 20, 8, 4)
+    assert L.gdn_tree_accept_commit_verify(ctypes.byref(bad), ctypes.byref(d), *([None] * 25)) == -2

@@ -193,3 +193,46 @@ def test_commit_verify_state_slot_permutation():
     res = run_pair(P, C, state_slot=slots, inplace=True)
     assert_same_bits(res)
     assert (res["st_f"] == 0).all() and (res["cst_f"] == 0).all()
+
+
+@pytest.mark.parametrize("name", ["c3_to_c3_nm16", "mixed_to_mixed_nm64", "nm32_to_nm32"])
+def test_accept_commit_verify_equals_accept_commit_then_verify(name):
+    """Greedy acceptance inside the launch: the same accepted node, state and verify results as
+    gdn_tree_accept_commit followed by gdn_tree_verify, bit for bit, and the oracle's."""
+    P, C = PAIRS[name]()
+    draft, tgt, root = W.greedy_tokens(P)
+    dP, dC = upload(P), upload(C)
+    dev = dP["S0"].device
+    i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(dev)
+    dt, tg, rt = i32(draft), i32(tgt), i32(root)
+    if name == "mixed_to_mixed_nm64" and P.nodes(1) > 2:
+        dP["parent"][int(P.node_offset[1]) + 1] = 1   # request 1: invalid previous tree
+    mnP, mnC = max(1, P.max_nodes), max(1, C.max_nodes)
+    _, U_P, _, _ = G.verify(dP["S0"], dP["q"], dP["k"], dP["v"], dP["g"], dP["beta"], dP["node_offset"],
+                            dP["parent"], max_nodes=mnP)
+    S_mid = dP["S0"].clone()
+    acc_r = torch.empty((P.B,), dtype=torch.int32, device=dev)
+    cst_r = torch.empty((P.B,), dtype=torch.int32, device=dev)
+    G.accept_commit(dP["S0"], U_P, dP["k"], dP["g"], dP["node_offset"], dP["parent"], dt, tg, rt, max_nodes=mnP,
+                    S_out=S_mid, accept_node=acc_r, status=cst_r)
+    out_r, U_r, anc_r = _zeros_like_outputs(C, dev)
+    _, _, _, st_r = G.verify(S_mid, dC["q"], dC["k"], dC["v"], dC["g"], dC["beta"], dC["node_offset"],
+                             dC["parent"], max_nodes=mnC, out=out_r, U=U_r, anc_mask=anc_r)
+    out_f, U_f, anc_f = _zeros_like_outputs(C, dev)
+    prev = dict(U=U_P, k=dP["k"], g=dP["g"], node_offset=dP["node_offset"], parent=dP["parent"], max_nodes=mnP)
+    S_f, _, _, _, st_f, cst_f, acc_f = G.commit_verify(
+        dP["S0"], prev, None, dC["q"], dC["k"], dC["v"], dC["g"], dC["beta"], dC["node_offset"], dC["parent"],
+        max_nodes=mnC, S_out=dP["S0"].clone(), out=out_f, U=U_f, anc_mask=anc_f,
+        greedy=dict(draft_token=dt, target_token=tg, root_token=rt))
+    torch.cuda.synchronize()
+    res = dict(S_r=host(S_mid), out_r=host(out_r), U_r=host(U_r), anc_r=anc_u64(anc_r), st_r=host(st_r),
+               cst_r=host(cst_r), S_f=host(S_f), out_f=host(out_f), U_f=host(U_f), anc_f=anc_u64(anc_f),
+               st_f=host(st_f), cst_f=host(cst_f), acc=host(acc_f))
+    assert_same_bits(res)
+    assert np.array_equal(host(acc_f), host(acc_r))
+    if name == "mixed_to_mixed_nm64" and P.nodes(1) > 2:
+        assert res["cst_f"][1] == O.STATUS_BAD_PARENT and res["acc"][1] == -1
+        assert np.array_equal(res["S_f"][1], P.S0[1])
+    else:
+        assert (res["cst_f"] == 0).all() and (res["acc"] >= 0).any()
+        oracle_check(P, C, res)
