@@ -236,7 +236,10 @@ int gdn_tree_commit_node(const gdn_tree_dims *dims, const float *S0, float *S_ou
  * S_out may alias S0 (in place: nothing is written for a request with an
  * empty path); out and U must not overlap U_prev (GDN_TREE_E_OVERLAP).
  * commit_status [B] (optional) receives the commit's device status as
- * gdn_tree_commit_node reports it, status [B] the verify's.  A request whose
+ * gdn_tree_commit_node reports it, status [B] the verify's.  path
+ * [B][prev max_nodes] and path_len [B] (optional, NULL = not written) receive
+ * the previous tree's accepted root-first path as gdn_tree_accepted_path
+ * writes it (for moving the accepted nodes' attention KV rows, for example).  A request whose
  * commit fails (bad offsets, parent or accept_node) is verified from S0,
  * which is also what S_out then holds; a bad slot writes nothing and gives
  * NaN outputs, as the two calls would.
@@ -244,10 +247,11 @@ int gdn_tree_commit_node(const gdn_tree_dims *dims, const float *S0, float *S_ou
 int gdn_tree_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *dims, const float *S0,
                            float *S_out, const int32_t *state_slot, const float *U_prev,
                            const uint16_t *k_prev, const float *g_prev, const int32_t *node_offset_prev,
-                           const int32_t *parent_prev, const int32_t *accept_node, int32_t *commit_status,
-                           const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
-                           const float *beta, const int32_t *node_offset, const int32_t *parent, float *out,
-                           float *U, uint64_t *anc_mask, int32_t *status, void *stream);
+                           const int32_t *parent_prev, const int32_t *accept_node, int32_t *path,
+                           int32_t *path_len, int32_t *commit_status, const uint16_t *q, const uint16_t *k,
+                           const uint16_t *v, const float *g, const float *beta, const int32_t *node_offset,
+                           const int32_t *parent, float *out, float *U, uint64_t *anc_mask, int32_t *status,
+                           void *stream);
 
 /*
  * gdn_tree_accept_commit_verify -- gdn_tree_commit_verify with the previous
@@ -267,10 +271,10 @@ int gdn_tree_accept_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree
                                   const uint16_t *k_prev, const float *g_prev, const int32_t *node_offset_prev,
                                   const int32_t *parent_prev, const int32_t *draft_token,
                                   const int32_t *target_token, const int32_t *root_token, int32_t *accept_node,
-                                  int32_t *commit_status, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                  const float *g, const float *beta, const int32_t *node_offset,
-                                  const int32_t *parent, float *out, float *U, uint64_t *anc_mask,
-                                  int32_t *status, void *stream);
+                                  int32_t *path, int32_t *path_len, int32_t *commit_status, const uint16_t *q,
+                                  const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
+                                  const int32_t *node_offset, const int32_t *parent, float *out, float *U,
+                                  uint64_t *anc_mask, int32_t *status, void *stream);
 
 /*
  * gdn_tree_accept_commit -- greedy acceptance fused with the commit, in one

@@ -368,10 +368,10 @@ extern "C" {
 int gdn_tree_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *dims, const float *S0, float *S_out,
                            const int32_t *state_slot, const float *U_prev, const uint16_t *k_prev,
                            const float *g_prev, const int32_t *node_offset_prev, const int32_t *parent_prev,
-                           const int32_t *accept_node, int32_t *commit_status, const uint16_t *q,
-                           const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
-                           const int32_t *node_offset, const int32_t *parent, float *out, float *U,
-                           uint64_t *anc_mask, int32_t *status, void *stream) {
+                           const int32_t *accept_node, int32_t *path, int32_t *path_len,
+                           int32_t *commit_status, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const float *g, const float *beta, const int32_t *node_offset, const int32_t *parent,
+                           float *out, float *U, uint64_t *anc_mask, int32_t *status, void *stream) {
     Args a;
     int rc = commit_verify_args(a, prev_dims, dims, S0, S_out, state_slot, U_prev, k_prev, g_prev, node_offset_prev,
                                 parent_prev, commit_status, q, k, v, g, beta, node_offset, parent, out, U, anc_mask,
@@ -379,6 +379,8 @@ int gdn_tree_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree_dims *
     if (rc != GDN_TREE_OK || a.B == 0) return rc;
     if (!accept_node) return GDN_TREE_E_NULL;
     a.accept_node = accept_node;
+    a.path_out = path;
+    a.path_len_out = path_len;
     clear_pending();
     return finish(gdn::launch_commit_verify(a, (hipStream_t)stream));
 }
@@ -388,10 +390,10 @@ int gdn_tree_accept_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree
                                   const uint16_t *k_prev, const float *g_prev, const int32_t *node_offset_prev,
                                   const int32_t *parent_prev, const int32_t *draft_token,
                                   const int32_t *target_token, const int32_t *root_token, int32_t *accept_node,
-                                  int32_t *commit_status, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                  const float *g, const float *beta, const int32_t *node_offset,
-                                  const int32_t *parent, float *out, float *U, uint64_t *anc_mask,
-                                  int32_t *status, void *stream) {
+                                  int32_t *path, int32_t *path_len, int32_t *commit_status, const uint16_t *q,
+                                  const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
+                                  const int32_t *node_offset, const int32_t *parent, float *out, float *U,
+                                  uint64_t *anc_mask, int32_t *status, void *stream) {
     Args a;
     int rc = commit_verify_args(a, prev_dims, dims, S0, S_out, state_slot, U_prev, k_prev, g_prev, node_offset_prev,
                                 parent_prev, commit_status, q, k, v, g, beta, node_offset, parent, out, U, anc_mask,
@@ -402,6 +404,8 @@ int gdn_tree_accept_commit_verify(const gdn_tree_dims *prev_dims, const gdn_tree
     a.target_token = target_token;
     a.root_token = root_token;
     a.accept_out = accept_node;
+    a.path_out = path;
+    a.path_len_out = path_len;
     clear_pending();
     return finish(gdn::launch_accept_commit_verify(a, (hipStream_t)stream));
 }

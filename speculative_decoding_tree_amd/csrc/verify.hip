@@ -311,10 +311,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
                 sm.cpath[lane] = pj;
                 sm.ccoef[lane] = coef;
             }
+            if (h == 0 && a.path_out) {   // one head publishes the root-first path (zero-filled row)
+                int32_t *row = a.path_out + (size_t)b * a.max_nodes_prev;
+                if (lane < L) row[lane] = pj;
+                for (int i = L + lane; i < a.max_nodes_prev; i += 64) row[i] = 0;
+            }
             if (lane == 0) {
                 sm.cL = L;
                 sm.cgam = gam;
                 if (h == 0 && a.commit_status) a.commit_status[b] = cst;
+                if (h == 0 && a.path_len_out) a.path_len_out[b] = L;
                 if (GREEDY && h == 0 && a.accept_out) a.accept_out[b] = accept;
             }
         }

@@ -68,8 +68,8 @@ _SIGS = {
     "gdn_tree_accept_greedy": [ctypes.POINTER(Dims)] + [_P] * 10,
     "gdn_tree_accept_commit": [ctypes.POINTER(Dims)] + [_P] * 16,
     "gdn_tree_commit_node": [ctypes.POINTER(Dims)] + [_P] * 13,
-    "gdn_tree_commit_verify": [ctypes.POINTER(Dims), ctypes.POINTER(Dims)] + [_P] * 22,
-    "gdn_tree_accept_commit_verify": [ctypes.POINTER(Dims), ctypes.POINTER(Dims)] + [_P] * 25,
+    "gdn_tree_commit_verify": [ctypes.POINTER(Dims), ctypes.POINTER(Dims)] + [_P] * 24,
+    "gdn_tree_accept_commit_verify": [ctypes.POINTER(Dims), ctypes.POINTER(Dims)] + [_P] * 27,
     "gdn_tree_commit_replay": [ctypes.POINTER(Dims)] + [_P] * 13,
     "gdn_tree_budget_select": [ctypes.POINTER(Dims), _P, _P, _P, ctypes.c_int32, ctypes.c_float,
                                _P, _P, _P, _P, _P],
@@ -381,13 +381,15 @@ def commit_node(S0, U, k, g, node_offset, parent, accept_node, max_nodes: int, S
 
 def commit_verify(S0, prev, accept_node, q, k, v, g, beta, node_offset, parent, max_nodes: int, S_out=None,
                   state_slot=None, out=None, U=None, anc_mask=None, status=None, commit_status=None,
-                  stream=None, greedy=None):
+                  stream=None, greedy=None, path=None, path_len=None):
     """gdn_tree_commit_verify: commit the previous tree's accepted node into S_out, then verify the
     next tree from that state, in one launch.  ``prev`` is a dict with the previous tree's
     ``U``, ``k``, ``g``, ``node_offset``, ``parent`` and ``max_nodes``.
     With ``greedy`` = dict(draft_token, target_token, root_token) the accepted node comes from the
     device-side greedy walk instead (gdn_tree_accept_commit_verify) and ``accept_node`` is an
-    optional output.  Returns (S_out, out, U, anc_mask, status, commit_status[, accept_node])."""
+    optional output.  ``path`` [B][prev max_nodes] and ``path_len`` [B] are optional outputs
+    (the accepted root-first path; not written when None).
+    Returns (S_out, out, U, anc_mask, status, commit_status[, accept_node])."""
     B, Hv, Hk, T, n_slots = _geometry(S0, q, v, node_offset, parent, max_nodes)
     U_p, k_p, g_p, off_p, par_p = prev["U"], prev["k"], prev["g"], prev["node_offset"], prev["parent"]
     T_p = int(par_p.numel())
@@ -415,9 +417,11 @@ def commit_verify(S0, prev, accept_node, q, k, v, g, beta, node_offset, parent, 
             _ptr(out, "out", _F32, (T, Hv, HEAD_DIM)), _ptr(U, "U", _F32, (T, Hv, HEAD_DIM)),
             _ptr(anc_mask, "anc_mask", _U64, (T,)), _ptr(status, "status", _I32, (B,)),
             _stream(stream)]
+    mnp = int(prev["max_nodes"])
+    pth = [_ptr(path, "path", _I32, (B, mnp)), _ptr(path_len, "path_len", _I32, (B,))]
     if greedy is None:
         rc = lib().gdn_tree_commit_verify(
-            *head, _ptr(accept_node, "accept_node", _I32, (B,)),
+            *head, _ptr(accept_node, "accept_node", _I32, (B,)), *pth,
             _ptr(commit_status, "commit_status", _I32, (B,)), *tail)
         _check("gdn_tree_commit_verify", rc)
         return S_out, out, U, anc_mask, status, commit_status
@@ -426,7 +430,7 @@ def commit_verify(S0, prev, accept_node, q, k, v, g, beta, node_offset, parent, 
         *head, _ptr(greedy["draft_token"], "draft_token", _I32, (T_p,)),
         _ptr(greedy["target_token"], "target_token", _I32, (T_p,)),
         _ptr(greedy["root_token"], "root_token", _I32, (B,)), _ptr(accept_node, "accept_node", _I32, (B,)),
-        _ptr(commit_status, "commit_status", _I32, (B,)), *tail)
+        *pth, _ptr(commit_status, "commit_status", _I32, (B,)), *tail)
     _check("gdn_tree_accept_commit_verify", rc)
     return S_out, out, U, anc_mask, status, commit_status, accept_node
 

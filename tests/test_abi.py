@@ -193,10 +193,10 @@ def test_commit_node_host_validation():
 def _cv_args(**over):
     """Pointer arguments of gdn_tree_commit_verify (after the two dims), all aligned fakes."""
     names = ["S0", "S_out", "state_slot", "U_prev", "k_prev", "g_prev", "node_offset_prev", "parent_prev",
-             "accept_node", "commit_status", "q", "k", "v", "g", "beta", "node_offset", "parent", "out", "U",
-             "anc_mask", "status", "stream"]
+             "accept_node", "path", "path_len", "commit_status", "q", "k", "v", "g", "beta", "node_offset", "parent",
+             "out", "U", "anc_mask", "status", "stream"]
     vals = {n: ctypes.c_void_p(0x100000 * (i + 1)) for i, n in enumerate(names)}
-    for n in ("state_slot", "commit_status", "anc_mask", "status", "stream"):
+    for n in ("state_slot", "path", "path_len", "commit_status", "anc_mask", "status", "stream"):
         vals[n] = None
     vals.update(over)
     return [vals[n] for n in names]
@@ -223,7 +223,7 @@ def test_commit_verify_host_validation():
     assert cv(pd, d, out=ctypes.c_void_p(up)) == -9
     assert "overlap" in G.strerror(-9)
     empty_p, empty = G.make_dims(0, 32, 16, 0, 8, 1), G.make_dims(0, 32, 16, 0, 8, 1)
-    assert L.gdn_tree_commit_verify(ctypes.byref(empty_p), ctypes.byref(empty), *([None] * 22)) == 0
+    assert L.gdn_tree_commit_verify(ctypes.byref(empty_p), ctypes.byref(empty), *([None] * 24)) == 0
 
 
 def test_accept_commit_verify_host_validation():
@@ -233,13 +233,13 @@ def test_accept_commit_verify_host_validation():
 
     def acv(**over):
         a = _cv_args()
-        head, tail = a[:8], a[10:]        # drop accept_node and commit_status
+        head, tail = a[:8], a[12:]        # drop accept_node, path, path_len and commit_status
         toks = {"draft_token": fake(1), "target_token": fake(2), "root_token": fake(3), "accept_node": None}
         toks.update(over)
         return L.gdn_tree_accept_commit_verify(ctypes.byref(pd), ctypes.byref(d), *head, toks["draft_token"],
                                                toks["target_token"], toks["root_token"], toks["accept_node"],
-                                               None, *tail)
+                                               None, None, None, *tail)
     for name in ("draft_token", "target_token", "root_token"):
         assert acv(**{name: None}) == -1, name
     bad = G.make_dims(4, 32, 8, 20, 8, 4)
-    assert L.gdn_tree_accept_commit_verify(ctypes.byref(bad), ctypes.byref(d), *([None] * 25)) == -2
+    assert L.gdn_tree_accept_commit_verify(ctypes.byref(bad), ctypes.byref(d), *([None] * 27)) == -2

@@ -60,8 +60,8 @@ def run_pair(P, C, accept=None, state_slot=None, inplace=False, edit=None):
     _, U_P, _, _ = G.verify(dP["S0"], dP["q"], dP["k"], dP["v"], dP["g"], dP["beta"], dP["node_offset"],
                             dP["parent"], max_nodes=mnP)
     S_mid = dP["S0"].clone()
-    G.commit_node(dP["S0"], U_P, dP["k"], dP["g"], dP["node_offset"], dP["parent"], acc, max_nodes=mnP,
-                  S_out=S_mid, state_slot=ss)
+    _, path_r, plen_r, _ = G.commit_node(dP["S0"], U_P, dP["k"], dP["g"], dP["node_offset"], dP["parent"], acc,
+                                         max_nodes=mnP, S_out=S_mid, state_slot=ss)
     cst_r = torch.empty((P.B,), dtype=torch.int32, device=dev)
     G.commit_node(dP["S0"], U_P, dP["k"], dP["g"], dP["node_offset"], dP["parent"], acc, max_nodes=mnP,
                   S_out=dP["S0"].clone(), state_slot=ss, status=cst_r)
@@ -70,15 +70,18 @@ def run_pair(P, C, accept=None, state_slot=None, inplace=False, edit=None):
                              dC["parent"], max_nodes=mnC, state_slot=ss, out=out_r, U=U_r, anc_mask=anc_r)
     S_in = dP["S0"].clone()
     out_f, U_f, anc_f = _zeros_like_outputs(C, dev)
+    path_f = torch.full((P.B, mnP), -5, dtype=torch.int32, device=dev)
+    plen_f = torch.full((P.B,), -5, dtype=torch.int32, device=dev)
     prev = dict(U=U_P, k=dP["k"], g=dP["g"], node_offset=dP["node_offset"], parent=dP["parent"], max_nodes=mnP)
     S_f, _, _, _, st_f, cst_f = G.commit_verify(
         S_in, prev, acc, dC["q"], dC["k"], dC["v"], dC["g"], dC["beta"], dC["node_offset"], dC["parent"],
         max_nodes=mnC, S_out=S_in if inplace else dP["S0"].clone(), state_slot=ss, out=out_f, U=U_f,
-        anc_mask=anc_f)
+        anc_mask=anc_f, path=path_f, path_len=plen_f)
     torch.cuda.synchronize()
     return dict(S_r=host(S_mid), out_r=host(out_r), U_r=host(U_r), anc_r=anc_u64(anc_r), st_r=host(st_r),
                 cst_r=host(cst_r), S_f=host(S_f), out_f=host(out_f), U_f=host(U_f), anc_f=anc_u64(anc_f),
-                st_f=host(st_f), cst_f=host(cst_f), acc=host(acc), dP=dP, dC=dC)
+                st_f=host(st_f), cst_f=host(cst_f), acc=host(acc), dP=dP, dC=dC,
+                path_r=host(path_r), plen_r=host(plen_r), path_f=host(path_f), plen_f=host(plen_f))
 
 
 def assert_same_bits(res):
@@ -88,6 +91,8 @@ def assert_same_bits(res):
     assert np.array_equal(res["anc_r"], res["anc_f"])
     assert np.array_equal(res["st_r"], res["st_f"])
     assert np.array_equal(res["cst_r"], res["cst_f"])
+    if "path_f" in res:   # the published path: as commit_node (and accepted_path) write it
+        assert np.array_equal(res["path_r"], res["path_f"]) and np.array_equal(res["plen_r"], res["plen_f"])
 
 
 def oracle_check(P, C, res):
@@ -213,21 +218,26 @@ def test_accept_commit_verify_equals_accept_commit_then_verify(name):
     S_mid = dP["S0"].clone()
     acc_r = torch.empty((P.B,), dtype=torch.int32, device=dev)
     cst_r = torch.empty((P.B,), dtype=torch.int32, device=dev)
+    path_r = torch.empty((P.B, mnP), dtype=torch.int32, device=dev)
+    plen_r = torch.empty((P.B,), dtype=torch.int32, device=dev)
     G.accept_commit(dP["S0"], U_P, dP["k"], dP["g"], dP["node_offset"], dP["parent"], dt, tg, rt, max_nodes=mnP,
-                    S_out=S_mid, accept_node=acc_r, status=cst_r)
+                    S_out=S_mid, accept_node=acc_r, path=path_r, path_len=plen_r, status=cst_r)
     out_r, U_r, anc_r = _zeros_like_outputs(C, dev)
     _, _, _, st_r = G.verify(S_mid, dC["q"], dC["k"], dC["v"], dC["g"], dC["beta"], dC["node_offset"],
                              dC["parent"], max_nodes=mnC, out=out_r, U=U_r, anc_mask=anc_r)
     out_f, U_f, anc_f = _zeros_like_outputs(C, dev)
+    path_f = torch.full((P.B, mnP), -5, dtype=torch.int32, device=dev)
+    plen_f = torch.full((P.B,), -5, dtype=torch.int32, device=dev)
     prev = dict(U=U_P, k=dP["k"], g=dP["g"], node_offset=dP["node_offset"], parent=dP["parent"], max_nodes=mnP)
     S_f, _, _, _, st_f, cst_f, acc_f = G.commit_verify(
         dP["S0"], prev, None, dC["q"], dC["k"], dC["v"], dC["g"], dC["beta"], dC["node_offset"], dC["parent"],
         max_nodes=mnC, S_out=dP["S0"].clone(), out=out_f, U=U_f, anc_mask=anc_f,
-        greedy=dict(draft_token=dt, target_token=tg, root_token=rt))
+        greedy=dict(draft_token=dt, target_token=tg, root_token=rt), path=path_f, path_len=plen_f)
     torch.cuda.synchronize()
     res = dict(S_r=host(S_mid), out_r=host(out_r), U_r=host(U_r), anc_r=anc_u64(anc_r), st_r=host(st_r),
                cst_r=host(cst_r), S_f=host(S_f), out_f=host(out_f), U_f=host(U_f), anc_f=anc_u64(anc_f),
-               st_f=host(st_f), cst_f=host(cst_f), acc=host(acc_f))
+               st_f=host(st_f), cst_f=host(cst_f), acc=host(acc_f),
+               path_r=host(path_r), plen_r=host(plen_r), path_f=host(path_f), plen_f=host(plen_f))
     assert_same_bits(res)
     assert np.array_equal(host(acc_f), host(acc_r))
     if name == "mixed_to_mixed_nm64" and P.nodes(1) > 2:
