@@ -526,7 +526,8 @@ def main():
         prev = dict(U=p["U"], k=p["k"], g=p["g"], node_offset=p["off"], parent=p["par"], max_nodes=mn)
         G.commit_verify(p["S0"], prev, p["acc"], p["q"], p["k"], p["v"], p["g"], p["beta"], p["off"], p["par"],
                         max_nodes=mn, S_out=p["S_out"], out=p["out2"], U=p["U2"], anc_mask=p["anc"],
-                        status=p["status"], commit_status=p["cst"], stream=stream)
+                        status=p["status"], commit_status=p["cst"], path=p["path"], path_len=p["plen"],
+                        stream=stream)
 
     for i in range(args.warmup):
         fstep(pools[i % len(pools)])
