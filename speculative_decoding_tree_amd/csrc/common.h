@@ -161,4 +161,20 @@ __device__ __forceinline__ int xcd_unit(int w, int n_units) {
 
 __host__ __device__ __forceinline__ int xcd_grid(int n_units) { return ((n_units + 7) >> 3) << 3; }
 
+// Head-group-interleaved mapping: the r = Hv/Hk v-heads that share a key head
+// form a head group; head groups (b Hk + g) are dealt round-robin over the 8
+// XCDs (workgroup w runs on XCD w % 8), so every XCD gets the same share of
+// every request's heads (exactly when Hk is a multiple of 8), whatever the
+// mix of tree sizes, and the v-heads of a group run one after another on one
+// XCD, where their q and k rows meet in L2.  Returns the unit b Hv + h, or -1
+// for a slot past the last group.
+__device__ __forceinline__ int xcd_group_unit(int w, int B, int Hk, int r) {
+    const int x = w & 7, s = w >> 3;
+    const int qi = s / r, j = s - qi * r;
+    const int q = x + 8 * qi;
+    return q < B * Hk ? q * r + j : -1;
+}
+
+__host__ __device__ __forceinline__ int xcd_group_grid(int B, int Hk, int r) { return 8 * ((B * Hk + 7) / 8) * r; }
+
 }  // namespace gdn

@@ -16,7 +16,9 @@
 // The tree pre-pass (ancestry bitsets, G, depth levels) runs in wave 0 on
 // registers with pointer doubling and ballots while the state is in flight.
 //
-// gfx950 layout.  One workgroup (4 wave64) owns one (request, v-head) unit.
+// gfx950 layout.  One workgroup (4 wave64) owns one (request, v-head) unit;
+// units are dealt to the XCDs by head group (xcd_group_unit), so that every
+// XCD gets the same share of every request, whatever the mix of tree sizes.
 // Wave w keeps its 128 x 32 column slab of H0 in registers as the B operand
 // of v_mfma_f32_16x16x32_bf16, split into bf16 hi + lo parts (q and k are
 // exact bf16, so two MFMAs with fp32 accumulation carry ~16 mantissa bits of
@@ -143,9 +145,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
     char *const stq = reinterpret_cast<char *>(&sm.ru[0][0]);
     char *const stk = stq + KOFF;
 
-    const int n_units = a.B * a.Hv;
-    const int unit = xcd_unit(blockIdx.x, n_units);
-    if (unit >= n_units) return;
+    const int unit = xcd_group_unit(blockIdx.x, a.B, a.Hk, a.Hv / a.Hk);
+    if (unit < 0) return;
     const int b = unit / a.Hv;
     const int h = unit - b * a.Hv;
     const int hk = h / (a.Hv / a.Hk);
@@ -709,7 +710,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
 
 template <int MODE>
 hipError_t launch_verify_impl(const Args &a, hipStream_t stream) {
-    const dim3 grid(xcd_grid(a.B * a.Hv)), block(NT);
+    const dim3 grid(xcd_group_grid(a.B, a.Hk, a.Hv / a.Hk)), block(NT);
     if (a.max_nodes <= 16)
         verify_kernel<16, MODE><<<grid, block, 0, stream>>>(a);
     else if (a.max_nodes <= 32)
