@@ -20,9 +20,10 @@ int check_dims(const gdn_tree_dims *d) {
     if (d->Hv < 1 || d->Hk < 1 || d->Hv % d->Hk != 0 || d->n_slots < 1) return GDN_TREE_E_DIMS;
     if (d->d_k != GDN_TREE_HEAD_DIM || d->d_v != GDN_TREE_HEAD_DIM) return GDN_TREE_E_HEAD_DIM;
     if (d->max_nodes < 1 || d->max_nodes > GDN_TREE_MAX_NODES) return GDN_TREE_E_MAX_NODES;
-    // one workgroup per (request, v-head); indices are computed in 64-bit
+    // one workgroup per (request, v-head), the grid rounded up to whole
+    // head-group chunks per XCD (int arithmetic); indices are computed in 64-bit
     const long long units = (long long)d->B * d->Hv;
-    if (units > (long long)INT_MAX - 8) return GDN_TREE_E_SIZE;
+    if (units > (long long)INT_MAX / 2) return GDN_TREE_E_SIZE;
     const long long state = (long long)GDN_TREE_HEAD_DIM * GDN_TREE_HEAD_DIM * 4;
     if ((long long)d->n_slots * d->Hv > (1ll << 62) / state) return GDN_TREE_E_SIZE;
     if ((long long)d->T * d->Hv > (1ll << 62) / state) return GDN_TREE_E_SIZE;
@@ -47,9 +48,6 @@ bool any_misaligned(Ps... ps) {
     return (misaligned((const void *)ps) || ...);
 }
 
-// Query rows per attention workgroup: 128 (two 16-row tiles per wave, so each
-// K/V fragment read from LDS serves 32 rows) once a request can have more
-// than 64 rows, else 64.
 // Query rows per attention workgroup.  64 (one 16-row tile per wave): with
 // the row groups of a request scheduled side by side on one XCD their shared
 // context reads meet in L2, and three such workgroups fit on a CU against two

@@ -162,19 +162,26 @@ __device__ __forceinline__ int xcd_unit(int w, int n_units) {
 __host__ __device__ __forceinline__ int xcd_grid(int n_units) { return ((n_units + 7) >> 3) << 3; }
 
 // Head-group-interleaved mapping: the r = Hv/Hk v-heads that share a key head
-// form a head group; head groups (b Hk + g) are dealt round-robin over the 8
-// XCDs (workgroup w runs on XCD w % 8), so every XCD gets the same share of
-// every request's heads (exactly when Hk is a multiple of 8), whatever the
-// mix of tree sizes, and the v-heads of a group run one after another on one
-// XCD, where their q and k rows meet in L2.  Returns the unit b Hv + h, or -1
-// for a slot past the last group.
+// form a head group; chunks of C consecutive head groups (b Hk + g) are dealt
+// round-robin over the 8 XCDs (workgroup w runs on XCD w % 8).  Every XCD
+// gets the same share of every request's heads (exactly when Hk is a
+// multiple of 8 C), whatever the mix of tree sizes; the v-heads of a group
+// run one after another on one XCD, where their q and k rows meet in L2; and
+// a chunk's states are contiguous.  C = 2 when Hk is a multiple of 16, else 1
+// (measured on 16 key heads: C = 2 beats 1 and 4).  Returns the unit b Hv + h,
+// or -1 for a slot past the last group.
 __device__ __forceinline__ int xcd_group_unit(int w, int B, int Hk, int r) {
+    const int cs = (Hk & 15) == 0 ? 1 : 0;   // log2 C
     const int x = w & 7, s = w >> 3;
-    const int qi = s / r, j = s - qi * r;
-    const int q = x + 8 * qi;
+    const int qi = s / r, j = s - qi * r;   // this XCD's qi-th head group, v-head j of it
+    const int ch = qi >> cs, wi = qi - (ch << cs);
+    const int q = ((ch * 8 + x) << cs) + wi;
     return q < B * Hk ? q * r + j : -1;
 }
 
-__host__ __device__ __forceinline__ int xcd_group_grid(int B, int Hk, int r) { return 8 * ((B * Hk + 7) / 8) * r; }
+__host__ __device__ __forceinline__ int xcd_group_grid(int B, int Hk, int r) {
+    const int C = (Hk & 15) == 0 ? 2 : 1;
+    return 8 * ((B * Hk + 8 * C - 1) / (8 * C)) * C * r;
+}
 
 }  // namespace gdn
