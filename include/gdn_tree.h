@@ -38,6 +38,8 @@
  *     S0, S_out   float32 [n_slots][Hv][d_k][d_v]: the state stored transposed
  *                 (H = S^T): row i holds what the state returns for key e_i.
  *     state_slot  int32 [B]: slot of request b in S0/S_out; NULL = slot b.
+ *                 Entry points that write S_out need distinct slots (two
+ *                 requests on one slot would write it concurrently).
  *     q, k        bfloat16 bit patterns (uint16) [T][Hk][d_k]
  *     v           bfloat16 bit patterns [T][Hv][d_v]
  *     g, beta     float32 [T][Hv]: log-decay g <= 0 (alpha = exp(g)) and beta
