@@ -184,11 +184,28 @@ def test_commit_verify_rejects_overlap_and_mismatched_dims():
 
 
 def test_commit_verify_full_mixed_batch():
-    """The launch the benchmark times (256 mixed trees, 48 v-heads): fused equals the two calls bit for bit."""
+    """The launch the benchmark times (256 mixed trees, 48 v-heads): fused equals the two calls bit for
+    bit, and sampled requests (the largest trees included) match the oracle's commit-then-verify."""
     P, C = W.make_c5(), W.make_c5(seed=1)
     res = run_pair(P, C)
     assert_same_bits(res)
     assert (res["st_f"] == 0).all() and (res["cst_f"] == 0).all()
+    rng = np.random.default_rng(3)
+    reqs = set(rng.choice(P.B, size=5, replace=False).tolist())
+    reqs |= {int(np.argmax(np.diff(P.node_offset))), int(np.argmax(np.diff(C.node_offset)))}
+    Pq, Pk, Pv, Cq, Ck, Cv = P.q64(), P.k64(), P.v64(), C.q64(), C.k64(), C.v64()
+    worst = [0.0, 0.0, 0.0]
+    for b in sorted(reqs):
+        _, _, _, _, states = O.verify_request(P.S0, Pq, Pk, Pv, P.g, P.beta, P.node_offset, P.parent, b, P.Hv, P.Hk)
+        path = O.accepted_path(P.parents_of(b), int(P.accept_node[b]))
+        S_mid = np.stack([O.commit_unit(P.S0[b, h], states[h], path) for h in range(P.Hv)])
+        worst[0] = max(worst[0], matwise_rel_err(res["S_f"][b], S_mid))
+        _, Ob, Ub, _, _ = O.verify_request(S_mid[None], Cq, Ck, Cv, C.g, C.beta, C.node_offset, C.parent, b, C.Hv,
+                                           C.Hk, state_slot=np.zeros(C.B, np.int32))
+        lo, hi = C.node_offset[b], C.node_offset[b + 1]
+        worst[1] = max(worst[1], rowwise_rel_err(res["out_f"][lo:hi], Ob))
+        worst[2] = max(worst[2], rowwise_rel_err(res["U_f"][lo:hi], Ub))
+    assert max(worst) <= TOL, worst
 
 
 def test_commit_verify_state_slot_permutation():
