@@ -258,6 +258,23 @@ def next_rows(args, wl, pools, mn, stream):
 
     t_gcv = _time_launches(greedy_step, n, stream)
     gcv_b = verify_bytes(wl) + cb - wl.B * wl.Hv * D * D * 4
+    # the one-launch step in place (S_out = S0, as a serving loop keeps one state per slot):
+    # requests that accepted nothing write no state.  Each pool's state drifts from step to
+    # step (the same path is committed again); only the timing is used.
+    ip = [dict(S=p["S0"].clone()) for p in pools[:2]]
+
+    def inplace_step(i):
+        p, s = pools[i % 2], ip[i % 2]
+        prev = dict(U=p["U"], k=p["k"], g=p["g"], node_offset=p["off"], parent=p["par"], max_nodes=mn)
+        G.commit_verify(s["S"], prev, p["acc"], p["q"], p["k"], p["v"], p["g"], p["beta"], p["off"], p["par"],
+                        max_nodes=mn, S_out=s["S"], out=p["out2"], U=p["U2"], anc_mask=p["anc"], status=st,
+                        commit_status=cst2, stream=stream)
+
+    t_ip = _time_launches(inplace_step, n, stream)
+    L0 = pools[0]["plen"].cpu().numpy()
+    ip_b = int(verify_bytes(wl) + commit_bytes(wl, L0) - wl.B * wl.Hv * D * D * 4
+               - (L0 == 0).sum() * wl.Hv * D * D * 4)   # no state write where nothing was accepted
+    del ip
     return {"accepted_path_then_commit": {"accepted_path_avg_us": t_path, "commit_avg_us": t_commit,
                                           "commit_alg_GBps": cb_step / (t_commit * 1e-6) / 1e9,
                                           "commit_hbm_frac": cb_step / (t_commit * 1e-6) / 1e9 / HBM_PEAK_GBS},
@@ -266,6 +283,10 @@ def next_rows(args, wl, pools, mn, stream):
                               "hbm_frac": rb / (t_replay * 1e-6) / 1e9 / HBM_PEAK_GBS,
                               "mean_accepted_len": float(Lr.mean())},
             "accept_greedy": {"avg_us": t_greedy, "mean_accepted_len": float(L.mean())},
+            "commit_verify_in_place": {"avg_us": t_ip, "alg_bytes": ip_b, "nodes_per_s": wl.T / (t_ip * 1e-6),
+                                       "alg_GBps": ip_b / (t_ip * 1e-6) / 1e9,
+                                       "hbm_frac": ip_b / (t_ip * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                       "requests_without_state_write": int((L0 == 0).sum())},
             "accept_commit_verify": {"avg_us": t_gcv, "alg_bytes": gcv_b,
                                      "alg_GBps": gcv_b / (t_gcv * 1e-6) / 1e9,
                                      "hbm_frac": gcv_b / (t_gcv * 1e-6) / 1e9 / HBM_PEAK_GBS},
