@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of tree-structured GDN speculative verify + commit on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixed_b256|random32_b256]
 
 One step = the whole hot path over one batch, as a decoding loop runs it:
 gdn_tree_commit_verify commits the previous tree's accepted node into the
@@ -312,7 +312,7 @@ def attention_row(args, stream):
     import workloads as W
     from speculative_decoding_tree_amd import gdn_tree as G
     t0 = time.time()
-    wl = W.make_attn_c5(0)
+    wl = W.make_attn_mixed_b256(0)
     dev = torch.device("cuda:0")
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
@@ -343,7 +343,7 @@ def attention_row(args, stream):
         res[key] = {"avg_us": t, "alg_bytes": nbytes, "alg_GBps": nbytes / (t * 1e-6) / 1e9,
                     "hbm_frac": nbytes / (t * 1e-6) / 1e9 / HBM_PEAK_GBS}
         if split is None:
-            res[key]["hbm_traffic_bytes"] = measured_traffic("c5_mixed_b256", "gdn_tree_attention")
+            res[key]["hbm_traffic_bytes"] = measured_traffic("mixed_b256", "gdn_tree_attention")
     assert (st.cpu().numpy() == 0).all()
     return res
 
@@ -357,7 +357,7 @@ def batch_one_row(args, stream):
     import torch
     import workloads as W
     from speculative_decoding_tree_amd import gdn_tree as G
-    wl = W.make_c3(B=1)
+    wl = W.make_root_branch6(B=1)
     dev = torch.device("cuda:0")
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
@@ -419,7 +419,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c5", choices=["c5", "c4"])
+    ap.add_argument("--workload", default="mixed_b256", choices=["mixed_b256", "random32_b256"])
     ap.add_argument("--pools", type=int, default=3, help="rotated copies of every buffer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-storeall", action="store_true")
@@ -449,7 +449,7 @@ def main():
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
 
     t0 = time.time()
-    wl = W.make_c5() if args.workload == "c5" else W.make_c4()
+    wl = W.make_mixed_b256() if args.workload == "mixed_b256" else W.make_random32_b256()
     log(f"[bench] generated {wl.name}: B={wl.B} Hv={wl.Hv} Hk={wl.Hk} T={wl.T} "
         f"max_nodes={wl.max_nodes} in {time.time() - t0:.1f}s")
     mn = wl.max_nodes
@@ -586,7 +586,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "Hv": wl.Hv, "Hk": wl.Hk, "d_k": D, "d_v": D, "T": wl.T,
                    "max_nodes": mn, "trees": ("64 each of chain-3, root-branch-6, random-16, random-64"
-                                              if args.workload == "c5" else "random-32, depth <= 6"),
+                                              if args.workload == "mixed_b256" else "random-32, depth <= 6"),
                    "inputs": "q/k/v bf16, S0/g/beta fp32, seed 0", "parallelism": "single-gpu"},
         "step": "gdn_tree_commit_verify: the previous tree's commit and this tree's verify, one launch",
         "commits_per_s": wl.B / (ms_fused * 1e-3),

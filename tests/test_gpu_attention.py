@@ -87,9 +87,9 @@ def compare(wl, out, lse, ref_out, ref_lse, reqs):
 
 # ---- ancestry ----------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["c3_b16", "c5"])
+@pytest.mark.parametrize("name", ["rootbranch6_b16", "mixed_b256"])
 def test_ancestry_bit_exact(name):
-    wl = W.make_c5() if name == "c5" else W.make_c3(16)
+    wl = W.make_mixed_b256() if name == "mixed_b256" else W.make_root_branch6(16)
     d = _dev()
     no = torch.from_numpy(wl.node_offset).to(d)
     par = torch.from_numpy(wl.parent).to(d)
@@ -170,12 +170,12 @@ def test_attention_gqa_groups_and_wide_group():
 
 @pytest.mark.parametrize("split", [None, 1024])
 def test_attention_full_size_sampled(split):
-    wl = W.make_attn_c5(0)
+    wl = W.make_attn_mixed_b256(0)
     out, lse, st, _ = run_attn(wl, split=split)
     assert (st == 0).all()
     kinds = np.array(wl.kinds)
     lens = np.diff(wl.ctx_offset)
-    reqs = sorted({int(np.flatnonzero(kinds == k)[0]) for k in W.C5_KINDS} |
+    reqs = sorted({int(np.flatnonzero(kinds == k)[0]) for k in W.MIXED_KINDS} |
                   {int(np.argmax(lens)), int(np.argmin(lens)), wl.B - 1})
     ref_out, ref_lse = oracle_attn_sampled(wl, reqs)
     compare(wl, out, lse, ref_out, ref_lse, reqs)

@@ -46,7 +46,7 @@ def _replays_match(graph, outputs, poison, ref, reps=4):
 
 
 def test_verify_path_commit_step_replays_bit_exact():
-    wl = W.make_c3(16)
+    wl = W.make_root_branch6(16)
     u = upload(wl)
     mn, d = wl.max_nodes, u["S0"].device
     out = torch.empty((wl.T, wl.Hv, 128), dtype=torch.float32, device=d)
@@ -83,7 +83,7 @@ def test_verify_path_commit_step_replays_bit_exact():
 
 def test_commit_verify_step_replays_bit_exact():
     """The one-launch step (previous tree's commit, next tree's verify) captured and replayed."""
-    P, C = W.make_c3(16), W.make_c3(16, seed=1)
+    P, C = W.make_root_branch6(16), W.make_root_branch6(16, seed=1)
     uP, uC = upload(P), upload(C)
     mn, d = P.max_nodes, uP["S0"].device
     _, U_P, _, _ = G.verify(uP["S0"], uP["q"], uP["k"], uP["v"], uP["g"], uP["beta"], uP["node_offset"],

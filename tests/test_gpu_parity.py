@@ -64,13 +64,13 @@ def check_full(wl, res, state_slot=None, mn=None):
 
 
 SMALL = {
-    "c1_chain_pad": lambda: W.zero_pad(W.make_c1("chain")),
-    "c1_tree_pad": lambda: W.zero_pad(W.make_c1("tree")),
-    "c2": W.make_c2,
-    "c3_b1": lambda: W.make_c3(B=1),
-    "c3_b16": lambda: W.make_c3(B=16),
-    "c3_b16_bfs": lambda: W.make_c3(B=16, bfs=True),
-    "mixed_small": lambda: W.make_c5(per_kind=3, Hv=6, Hk=2),
+    "tiny_d16_chain_pad": lambda: W.zero_pad(W.make_tiny_d16("chain")),
+    "tiny_d16_tree_pad": lambda: W.zero_pad(W.make_tiny_d16("tree")),
+    "chain3_b64": W.make_chain3_b64,
+    "rootbranch6_b1": lambda: W.make_root_branch6(B=1),
+    "rootbranch6_b16": lambda: W.make_root_branch6(B=16),
+    "rootbranch6_b16_bfs": lambda: W.make_root_branch6(B=16, bfs=True),
+    "mixed_small": lambda: W.make_mixed_b256(per_kind=3, Hv=6, Hk=2),
     "deep_chain64": lambda: W.make_custom([W.chain(64), W.chain(64)], [63, 20], Hv=4, Hk=2),
     "forest_empty_single": lambda: W.make_custom(
         [np.zeros(0, np.int32), np.array([-1], np.int32), np.full(8, -1, np.int32),
@@ -99,21 +99,21 @@ def test_small_configs_full_parity(name):
 
 
 def test_zero_padding_is_exact():
-    wl = W.zero_pad(W.make_c1("tree"))
+    wl = W.zero_pad(W.make_tiny_d16("tree"))
     res = run_gpu(wl)
     assert np.all(res["out"][..., 16:] == 0) and np.all(res["U"][..., 16:] == 0)
     assert np.all(res["S1"][..., 16:, :] == 0) and np.all(res["S1"][..., :, 16:] == 0)
 
 
 def test_state_slot_permutation_and_inplace_commit():
-    wl = W.make_c5(per_kind=2, Hv=4, Hk=2, seed=5)
+    wl = W.make_mixed_b256(per_kind=2, Hv=4, Hk=2, seed=5)
     slots = list(range(wl.B))[::-1]
     res = run_gpu(wl, state_slot=slots, inplace=True)
     check_full(wl, res, state_slot=slots)
 
 
 def test_deterministic_bitwise():
-    wl = W.make_c5(per_kind=2, Hv=6, Hk=2, seed=7)
+    wl = W.make_mixed_b256(per_kind=2, Hv=6, Hk=2, seed=7)
     a, b = run_gpu(wl), run_gpu(wl)
     for key in ("out", "U", "S1", "anc", "path"):
         assert np.array_equal(a[key], b[key]), key
@@ -219,10 +219,10 @@ def test_device_errors_paths_offsets_slots_and_node_cap():
 # storeall comparison variant
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["c2", "c3_b16", "mixed_small", "forest_empty_single"])
+@pytest.mark.parametrize("name", ["chain3_b64", "rootbranch6_b16", "mixed_small", "forest_empty_single"])
 def test_storeall_parity(name):
     wl = SMALL[name]()
-    if name == "c2":
+    if name == "chain3_b64":
         wl = W.subset(wl, range(16))
     mn = _mn(wl)
     d = upload(wl)
@@ -270,16 +270,16 @@ def sampled_check(wl, res, n_sample=24, seed=0):
     return worst
 
 
-def test_c4_full_batch_sampled():
-    wl = W.make_c4()
+def test_random32_b256_full_batch_sampled():
+    wl = W.make_random32_b256()
     res = run_gpu(wl)
-    print("c4 worst rel err out/U/S':", sampled_check(wl, res))
+    print("random32_b256 worst rel err out/U/S':", sampled_check(wl, res))
 
 
-def test_c5_full_batch_sampled():
-    wl = W.make_c5()
+def test_mixed_b256_full_batch_sampled():
+    wl = W.make_mixed_b256()
     res = run_gpu(wl)
-    print("c5 worst rel err out/U/S':", sampled_check(wl, res))
+    print("mixed_b256 worst rel err out/U/S':", sampled_check(wl, res))
 
 
 def test_commit_alone_from_oracle_pseudo_values():
@@ -301,7 +301,7 @@ def test_commit_alone_from_oracle_pseudo_values():
 # device-side greedy acceptance, alone and fused with the commit
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["c2", "c3_b16", "mixed_small", "forest_empty_single", "deep_chain64"])
+@pytest.mark.parametrize("name", ["chain3_b64", "rootbranch6_b16", "mixed_small", "forest_empty_single", "deep_chain64"])
 def test_greedy_accept_and_fused_commit(name):
     wl = SMALL[name]()
     mn = _mn(wl)
@@ -328,7 +328,7 @@ def test_greedy_accept_and_fused_commit(name):
 
 
 def test_fused_accept_commit_full_batch():
-    wl = W.make_c5()
+    wl = W.make_mixed_b256()
     mn = wl.max_nodes
     draft, tgt, root = W.greedy_tokens(wl)
     acc_o, path_o, plen_o, _ = O.greedy_accept_batch(wl.node_offset, wl.parent, draft, tgt, root, max_nodes=mn)
@@ -353,7 +353,7 @@ def test_fused_accept_commit_full_batch():
             assert matwise_rel_err(S1h[b, h][None], want[None]) <= TOL
 
 
-@pytest.mark.parametrize("name", ["c3_b16", "mixed_small", "deep_chain64", "forest_empty_single"])
+@pytest.mark.parametrize("name", ["rootbranch6_b16", "mixed_small", "deep_chain64", "forest_empty_single"])
 def test_commit_node_equals_accepted_path_then_commit(name):
     """The fused launch derives the same path and writes the same state, bit for bit."""
     wl = SMALL[name]()
@@ -374,7 +374,7 @@ def test_commit_node_equals_accepted_path_then_commit(name):
 
 
 def test_commit_node_bad_accept_node_keeps_S0():
-    wl = W.make_c3(4)
+    wl = W.make_root_branch6(4)
     mn = wl.max_nodes
     d = upload(wl)
     _, U, _, _ = G.verify(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"], d["parent"],
@@ -395,7 +395,7 @@ def test_commit_node_bad_accept_node_keeps_S0():
 # replay commit (no pseudo-values)
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["c2", "c3_b16", "mixed_small", "deep_chain64", "forest_empty_single"])
+@pytest.mark.parametrize("name", ["chain3_b64", "rootbranch6_b16", "mixed_small", "deep_chain64", "forest_empty_single"])
 def test_commit_replay_parity(name):
     wl = SMALL[name]()
     mn = _mn(wl)
@@ -438,7 +438,7 @@ def test_commit_replay_inplace_and_bad_path():
 
 @pytest.mark.parametrize("budget_frac,thr", [(0.0, 0.0), (0.1, 0.0), (0.5, 0.05), (0.9, 0.3), (1.2, 0.0)])
 def test_budget_select_bit_exact(budget_frac, thr):
-    wl = W.make_c5(per_kind=8, Hv=2, Hk=1, seed=4)
+    wl = W.make_mixed_b256(per_kind=8, Hv=2, Hk=1, seed=4)
     p = W.acceptance_probs(wl, seed=5)
     p[::11] = 1.0                                    # exact survival ties along paths
     budget = int(budget_frac * wl.T)
@@ -452,7 +452,7 @@ def test_budget_select_bit_exact(budget_frac, thr):
 
 
 def test_budget_select_invalid_request_and_full_batch():
-    wl = W.make_c5()
+    wl = W.make_mixed_b256()
     p = W.acceptance_probs(wl)
     par = wl.parent.copy()
     par[wl.node_offset[7] + 1] = 5                   # request 7 breaks parent order

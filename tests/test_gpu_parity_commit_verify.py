@@ -27,12 +27,12 @@ def _trees(seed, sizes):
 
 PAIRS = {
     # previous tree, next tree (same B, Hv, Hk)
-    "mixed_to_mixed_nm64": lambda: (W.make_c5(per_kind=3, Hv=6, Hk=2), W.make_c5(seed=1, per_kind=3, Hv=6, Hk=2)),
+    "mixed_to_mixed_nm64": lambda: (W.make_mixed_b256(per_kind=3, Hv=6, Hk=2), W.make_mixed_b256(seed=1, per_kind=3, Hv=6, Hk=2)),
     "long_paths_to_nm64": lambda: (
         W.make_custom([W.chain(64), W.chain(40), W.chain(17), np.zeros(0, np.int32), W.chain(16)],
                       [63, 39, 16, -1, 15], Hv=4, Hk=2, seed=5),
         W.make_custom(_trees(6, [64, 3, 0, 33, 1]), [0, 0, -1, 0, 0], Hv=4, Hk=2, seed=6)),
-    "c3_to_c3_nm16": lambda: (W.make_c3(B=16), W.make_c3(B=16, seed=1)),
+    "rootbranch6_to_rootbranch6_nm16": lambda: (W.make_root_branch6(B=16), W.make_root_branch6(B=16, seed=1)),
     "nm32_to_nm32": lambda: (
         W.make_custom(_trees(10, [32, 17, 1, 16, 31, 24]), [5, 0, 0, -1, 30, 11], Hv=6, Hk=2, seed=7),
         W.make_custom(_trees(11, [20, 32, 9, 0, 17, 30]), [0, 0, 0, -1, 0, 0], Hv=6, Hk=2, seed=8)),
@@ -167,7 +167,7 @@ def test_commit_verify_device_errors():
 
 
 def test_commit_verify_rejects_overlap_and_mismatched_dims():
-    P, C = PAIRS["c3_to_c3_nm16"]()
+    P, C = PAIRS["rootbranch6_to_rootbranch6_nm16"]()
     dP, dC = upload(P), upload(C)
     mn = max(1, P.max_nodes)
     _, U_P, _, _ = G.verify(dP["S0"], dP["q"], dP["k"], dP["v"], dP["g"], dP["beta"], dP["node_offset"],
@@ -186,7 +186,7 @@ def test_commit_verify_rejects_overlap_and_mismatched_dims():
 def test_commit_verify_full_mixed_batch():
     """The launch the benchmark times (256 mixed trees, 48 v-heads): fused equals the two calls bit for
     bit, and sampled requests (the largest trees included) match the oracle's commit-then-verify."""
-    P, C = W.make_c5(), W.make_c5(seed=1)
+    P, C = W.make_mixed_b256(), W.make_mixed_b256(seed=1)
     res = run_pair(P, C)
     assert_same_bits(res)
     assert (res["st_f"] == 0).all() and (res["cst_f"] == 0).all()
@@ -217,7 +217,7 @@ def test_commit_verify_state_slot_permutation():
     assert (res["st_f"] == 0).all() and (res["cst_f"] == 0).all()
 
 
-@pytest.mark.parametrize("name", ["c3_to_c3_nm16", "mixed_to_mixed_nm64", "nm32_to_nm32"])
+@pytest.mark.parametrize("name", ["rootbranch6_to_rootbranch6_nm16", "mixed_to_mixed_nm64", "nm32_to_nm32"])
 def test_accept_commit_verify_equals_accept_commit_then_verify(name):
     """Greedy acceptance inside the launch: the same accepted node, state and verify results as
     gdn_tree_accept_commit followed by gdn_tree_verify, bit for bit, and the oracle's."""

@@ -383,7 +383,7 @@ def test_c1_worked_cases():
     """The small fp64 configuration: 4-node chain and the 5-node tree."""
     import workloads as W
     for kind, want_path in (("chain", [0, 1, 2, 3]), ("tree", [0, 1, 3])):
-        wl = W.make_c1(kind)
+        wl = W.make_tiny_d16(kind)
         p = O.accepted_path(wl.parent, int(wl.accept_node[0]))
         assert p == want_path
         st, Ob, Ub, anc, states = O.verify_request(wl.S0, wl.q, wl.k, wl.v, wl.g, wl.beta,
@@ -446,7 +446,7 @@ def test_greedy_accept_chain_prefix():
 
 def test_greedy_tokens_generator_contract():
     import workloads as W
-    wl = W.make_c5(per_kind=4, Hv=2, Hk=1)
+    wl = W.make_mixed_b256(per_kind=4, Hv=2, Hk=1)
     draft, tgt, root = W.greedy_tokens(wl)
     for b in range(wl.B):
         lo = wl.node_offset[b]
@@ -483,7 +483,7 @@ def test_survival_chain_closed_form():
 @pytest.mark.parametrize("seed", range(4))
 def test_budget_select_properties(seed):
     import workloads as W
-    wl = W.make_c5(per_kind=3, Hv=2, Hk=1, seed=seed)
+    wl = W.make_mixed_b256(per_kind=3, Hv=2, Hk=1, seed=seed)
     p = W.acceptance_probs(wl, seed=seed)
     p[::7] = 1.0                                     # exact ties along paths
     for budget, thr in ((0, 0.0), (10, 0.0), (wl.T // 2, 0.05), (wl.T + 5, 0.2), (wl.T, 0.0)):

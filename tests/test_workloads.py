@@ -16,7 +16,7 @@ def test_bf16_round_trip_and_ties():
     assert W.f32_to_bf16_bits(tie)[0] == 0x3F80
 
 
-@pytest.mark.parametrize("name", ["c1_chain", "c1_tree", "c2", "c3_b1", "c3_b16"])
+@pytest.mark.parametrize("name", ["tiny_d16_chain", "tiny_d16_tree", "chain3_b64", "rootbranch6_b1", "rootbranch6_b16"])
 def test_deterministic(name):
     a, b = W.make(name), W.make(name)
     for f in ("node_offset", "parent", "accept_node", "S0", "q", "k", "v", "g", "beta"):
@@ -24,7 +24,7 @@ def test_deterministic(name):
 
 
 def test_c2_shapes_and_distributions():
-    wl = W.make("c2")
+    wl = W.make("chain3_b64")
     assert (wl.B, wl.Hv, wl.Hk, wl.d, wl.T) == (64, 32, 16, 128, 192)
     assert wl.S0.shape == (64, 32, 128, 128) and wl.S0.dtype == np.float32
     assert abs(wl.S0.std() - np.sqrt(0.02)) < 1e-3
@@ -44,10 +44,10 @@ def test_random_tree_depth_cap():
 
 
 def test_c5_composition():
-    wl = W.make_c5(per_kind=8, Hv=6, Hk=2)
+    wl = W.make_mixed_b256(per_kind=8, Hv=6, Hk=2)
     assert wl.B == 32
     from collections import Counter
-    assert Counter(wl.kinds) == {k: 8 for k in W.C5_KINDS}
+    assert Counter(wl.kinds) == {k: 8 for k in W.MIXED_KINDS}
     sizes = {"chain3": 3, "rootbranch6": 6, "random16": 16, "random64": 64}
     for b, kd in enumerate(wl.kinds):
         assert wl.nodes(b) == sizes[kd]
@@ -61,7 +61,7 @@ def test_accept_by_edge_probabilities():
 
 
 def test_zero_pad_and_subset():
-    wl = W.make_c1("tree")
+    wl = W.make_tiny_d16("tree")
     p = W.zero_pad(wl)
     assert p.d == 128 and p.S0.dtype == np.float32
     assert np.all(p.S0[:, :, 16:, :] == 0) and np.all(W.bf16_bits_to_f32(p.q)[:, :, 16:] == 0)

@@ -37,7 +37,7 @@ __all__ = [
     "Workload", "CONFIGS", "make", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "chain", "root_branch", "random_tree", "accept_by_edge", "tree_depths",
     "zero_pad", "subset", "greedy_tokens", "acceptance_probs",
-    "AttnWorkload", "make_attn", "make_attn_small", "make_attn_c5",
+    "AttnWorkload", "make_attn", "make_attn_small", "make_attn_mixed_b256",
 ]
 
 
@@ -217,52 +217,52 @@ def _deepest_first_index(parent: np.ndarray) -> int:
     return int(np.argmax(dep))      # ties go to the lowest index
 
 
-def make_c1(kind: str = "chain", seed: int = 0) -> Workload:
+def make_tiny_d16(kind: str = "chain", seed: int = 0) -> Workload:
     """1 request, 1 head, d=16, fp64 inputs; a 4-node chain or the 5-node tree
     [-1,0,0,1,2]; accepted path = root to the deepest node (lowest index on a tie)."""
     rng = np.random.default_rng(seed)
     parent = chain(4) if kind == "chain" else np.array([-1, 0, 0, 1, 2], dtype=np.int32)
     acc = _deepest_first_index(parent)
-    return _assemble(f"c1_{kind}", rng, [parent], [acc], Hv=1, Hk=1, d=16, s0_var=1.0 / 16, fp64=True)
+    return _assemble(f"tiny_d16_{kind}", rng, [parent], [acc], Hv=1, Hk=1, d=16, s0_var=1.0 / 16, fp64=True)
 
 
-def make_c2(seed: int = 0, B: int = 64) -> Workload:
+def make_chain3_b64(seed: int = 0, B: int = 64) -> Workload:
     """Depth-3 draft chains, 64 requests x 32 v-heads (16 k-heads), accepted
     length uniform in {0..3}."""
     rng = np.random.default_rng(seed)
     parents = [chain(3) for _ in range(B)]
     accepts = [int(rng.integers(0, 4)) - 1 for _ in range(B)]
-    return _assemble("c2_chain3", rng, parents, accepts, Hv=32, Hk=16, d=128, s0_var=0.02)
+    return _assemble("chain3_b64", rng, parents, accepts, Hv=32, Hk=16, d=128, s0_var=0.02)
 
 
-def make_c3(B: int = 16, seed: int = 0, bfs: bool = False) -> Workload:
+def make_root_branch6(B: int = 16, seed: int = 0, bfs: bool = False) -> Workload:
     """6-node root-branch trees, batch 1 or 16, 32 v-heads (16 k-heads), S0 with
     variance 1/16; the accepted node is uniform over {none} and the nodes."""
     rng = np.random.default_rng(seed)
     base = np.array([-1, -1, 0, 1, 2, 3], dtype=np.int32) if bfs else root_branch()
     parents = [base.copy() for _ in range(B)]
     accepts = [int(rng.integers(0, 7)) - 1 for _ in range(B)]
-    return _assemble(f"c3_rootbranch_b{B}" + ("_bfs" if bfs else ""), rng, parents, accepts,
+    return _assemble(f"rootbranch6_b{B}" + ("_bfs" if bfs else ""), rng, parents, accepts,
                      Hv=32, Hk=16, d=128, s0_var=1.0 / 16)
 
 
-def make_c4(seed: int = 0, B: int = 256, n: int = 32, Hv: int = 32, Hk: int = 16) -> Workload:
+def make_random32_b256(seed: int = 0, B: int = 256, n: int = 32, Hv: int = 32, Hk: int = 16) -> Workload:
     """Random 32-node trees (depth <= 6), batch 256, 32 v-heads / 16 k-heads,
     acceptance 0.7 per edge."""
     rng = np.random.default_rng(seed)
     parents = [random_tree(rng, n) for _ in range(B)]
     accepts = [accept_by_edge(rng, p) for p in parents]
-    return _assemble(f"c4_random{n}_b{B}", rng, parents, accepts, Hv=Hv, Hk=Hk, d=128, s0_var=0.02)
+    return _assemble(f"random{n}_b{B}", rng, parents, accepts, Hv=Hv, Hk=Hk, d=128, s0_var=0.02)
 
 
-C5_KINDS = ("chain3", "rootbranch6", "random16", "random64")
+MIXED_KINDS = ("chain3", "rootbranch6", "random16", "random64")
 
 
-def make_c5(seed: int = 0, per_kind: int = 64, Hv: int = 48, Hk: int = 16) -> Workload:
+def make_mixed_b256(seed: int = 0, per_kind: int = 64, Hv: int = 48, Hk: int = 16) -> Workload:
     """Ragged batch: per_kind requests of each of chain-3, root-branch-6,
     random-16 and random-64 trees in a seeded shuffle; 48 v-heads / 16 k-heads."""
     rng = np.random.default_rng(seed)
-    kinds = [k for k in C5_KINDS for _ in range(per_kind)]
+    kinds = [k for k in MIXED_KINDS for _ in range(per_kind)]
     order = rng.permutation(len(kinds))
     kinds = [kinds[i] for i in order]
     parents = []
@@ -276,7 +276,7 @@ def make_c5(seed: int = 0, per_kind: int = 64, Hv: int = 48, Hk: int = 16) -> Wo
         else:
             parents.append(random_tree(rng, 64))
     accepts = [accept_by_edge(rng, p) for p in parents]
-    return _assemble(f"c5_mixed_b{len(kinds)}", rng, parents, accepts, Hv=Hv, Hk=Hk, d=128,
+    return _assemble(f"mixed_b{len(kinds)}", rng, parents, accepts, Hv=Hv, Hk=Hk, d=128,
                      s0_var=0.02, kinds=kinds)
 
 
@@ -289,14 +289,14 @@ def make_custom(parents: List[np.ndarray], accepts: List[int], Hv: int = 4, Hk: 
 
 
 CONFIGS = {
-    "c1_chain": lambda: make_c1("chain"),
-    "c1_tree": lambda: make_c1("tree"),
-    "c2": make_c2,
-    "c3_b1": lambda: make_c3(B=1),
-    "c3_b16": lambda: make_c3(B=16),
-    "c3_b16_bfs": lambda: make_c3(B=16, bfs=True),
-    "c4": make_c4,
-    "c5": make_c5,
+    "tiny_d16_chain": lambda: make_tiny_d16("chain"),
+    "tiny_d16_tree": lambda: make_tiny_d16("tree"),
+    "chain3_b64": make_chain3_b64,
+    "rootbranch6_b1": lambda: make_root_branch6(B=1),
+    "rootbranch6_b16": lambda: make_root_branch6(B=16),
+    "rootbranch6_b16_bfs": lambda: make_root_branch6(B=16, bfs=True),
+    "random32_b256": make_random32_b256,
+    "mixed_b256": make_mixed_b256,
 }
 
 
@@ -510,11 +510,11 @@ def make_attn_small(seed: int = 0) -> AttnWorkload:
     return make_attn(parents, ctx, Hq=8, Hkv=2, seed=seed, name="attn_small")
 
 
-def make_attn_c5(seed: int = 0, ctx_lo: int = 1024, ctx_hi: int = 4096, Hq: int = 32, Hkv: int = 8) -> AttnWorkload:
+def make_attn_mixed_b256(seed: int = 0, ctx_lo: int = 1024, ctx_hi: int = 4096, Hq: int = 32, Hkv: int = 8) -> AttnWorkload:
     """The mixed batch-256 trees (64 each of chain-3, root-branch-6, random-16,
     random-64, shuffled) with committed contexts uniform in [ctx_lo, ctx_hi]."""
-    wl = make_c5(seed)
+    wl = make_mixed_b256(seed)
     parents = [wl.parents_of(b) for b in range(wl.B)]
     rng = np.random.default_rng(seed + 7)
     ctx = [int(x) for x in rng.integers(ctx_lo, ctx_hi + 1, size=wl.B)]
-    return make_attn(parents, ctx, Hq=Hq, Hkv=Hkv, seed=seed + 11, name="attn_c5_b256", kinds=wl.kinds)
+    return make_attn(parents, ctx, Hq=Hq, Hkv=Hkv, seed=seed + 11, name="attn_mixed_b256", kinds=wl.kinds)
