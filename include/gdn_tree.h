@@ -204,10 +204,10 @@ int gdn_tree_accept_greedy(const gdn_tree_dims *dims, const int32_t *node_offset
  * into S_out exactly as gdn_tree_commit does (TreeWY, "Method": only the
  * accepted path is composed into the next state).  path [B][max_nodes] and
  * path_len [B] are optional outputs (NULL = not written), identical to what
- * gdn_tree_accepted_path writes.  Device errors: bad offsets (1), bad parent
- * (3), bad slot (4), accept_node outside [-1, N_b) (5); the request's S_out
- * is then a copy of S0 (nothing is written where the slot is bad), and its
- * path is empty.
+ * gdn_tree_accepted_path writes.  Device errors: bad offsets (1), too many
+ * nodes (2), bad parent (3), bad slot (6), accept_node outside [-1, N_b) (5);
+ * the request's S_out is then a copy of S0 (nothing is written where the slot
+ * is bad), and its path is empty.
  */
 int gdn_tree_commit_node(const gdn_tree_dims *dims, const float *S0, float *S_out,
                          const int32_t *state_slot, const float *U, const uint16_t *k, const float *g,
@@ -406,9 +406,13 @@ int gdn_tree_commit_storeall(const gdn_tree_dims *dims, const float *S0, float *
 
 /*
  * gdn_tree_state_bytes -- speculative recurrent-state bytes one layer holds
- * beyond S0: storeall != 0 gives T*Hv*d_k*d_v*4 (one state per node and head),
- * storeall == 0 gives the pseudo-value matrix U, T*Hv*d_v*4.  Host only; 0 on
- * invalid dims.
+ * beyond S0, for the memory comparison of the two schemes.  storeall != 0
+ * gives T*Hv*d_k*d_v*4: one fp32 state per node and head (TreeWY, "Prior
+ * work": storeall keeps the committed state plus one state per candidate
+ * position, so a depth-3 chain needs four).  storeall == 0 gives the fp32
+ * pseudo-value matrix U, T*Hv*d_v*4 (TreeWY, "Novelty": one small
+ * pseudo-value matrix replaces the per-node states, and one full state is
+ * rebuilt for the accepted path only).  Host only; 0 on invalid dims.
  */
 size_t gdn_tree_state_bytes(const gdn_tree_dims *dims, int storeall);
 

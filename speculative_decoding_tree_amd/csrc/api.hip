@@ -1,7 +1,10 @@
 // Host side of the C ABI declared in include/gdn_tree.h: argument checks
 // (nothing is enqueued when one fails), then one launch per entry point on
-// the caller's stream.  The library holds no state, allocates nothing and
-// never synchronises.
+// the caller's stream.  The library allocates nothing and never
+// synchronises.  Its only host state is a per-device cache of two launch
+// facts of the attention kernel (compute units, resident workgroups per CU),
+// kept in atomics and written with the same value by any thread that fills
+// them.
 #include <limits.h>
 #include <math.h>
 

@@ -34,6 +34,8 @@
 // kernel merges them.
 #include <math.h>
 
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 #include "mfma.h"
@@ -773,29 +775,47 @@ hipError_t launch_ancestry(const Args &a, hipStream_t stream) {
 }
 
 namespace {
-// Compute units of the current device (cached per device; 0 if unknown).
-int cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cached[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cached[dev] = cus;
+constexpr int MAX_DEVICES = 64;
+// Launch facts of the current device, cached per device: its compute units and
+// the scheduled attention kernel's resident workgroups per CU (0 = unknown).
+// Threads that race to fill an entry compute the same value; the atomics keep
+// those stores and loads well defined.
+std::atomic<int> g_cus[MAX_DEVICES];
+std::atomic<int> g_occupancy[MAX_DEVICES];
+
+int cached_fact(std::atomic<int> *table, int dev, int (*query)(int)) {
+    if (dev < 0 || dev >= MAX_DEVICES) return query(dev);
+    int v = table[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        v = query(dev);
+        if (v > 0) table[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
+}
+
+int query_cus(int dev) {
+    int cus = 0;
+    return hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? cus : 0;
+}
+
+int query_occupancy(int) {
+    int occ = 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attn_sched_kernel<1>, AT, 0) == hipSuccess ? occ : 0;
+}
+
+// Resident workgroups of the scheduled launch on the current device: the
+// runtime's occupancy (registers and LDS) times the compute units.
+int resident_workgroups() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    return cached_fact(g_occupancy, dev, query_occupancy) * cached_fact(g_cus, dev, query_cus);
 }
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
     if (a.rows_wg != 64) return hipErrorInvalidValue;   // the host sizes units for one tile per wave
     const int units = a.B * a.Hkv * a.n_split * a.n_rg;
-    // resident workgroups: the runtime's occupancy (registers and LDS) times the CUs
-    static int occupancy = 0;
-    if (occupancy == 0 &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occupancy, attn_sched_kernel<1>, AT, 0) != hipSuccess)
-        occupancy = 0;
-    const int resident = ((occupancy * cu_count()) / 8) * 8;
+    const int resident = (resident_workgroups() / 8) * 8;
     // the list packs row groups in 8 bits and an item's unit count in 12
     const bool sched = resident >= 8 && (long long)a.B * a.n_split <= SCHED_ITEMS && a.n_rg < 256 &&
                        a.Hkv * a.n_rg < 4096;

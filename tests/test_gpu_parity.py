@@ -486,3 +486,21 @@ def test_budget_select_more_nodes_than_register_cache(budget_frac):
     torch.cuda.synchronize()
     assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
     assert np.array_equal(host(keep), ko) and np.array_equal(host(kept), co) and np.array_equal(host(st), sto)
+
+
+def test_budget_select_tie_order_hand_cases():
+    """The hand-built tie cases (tests/golden/budget_ties.json): the kernel's keep sets
+    equal the ones written out by hand, bit for bit."""
+    import json
+    import os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "budget_ties.json")))["cases"]
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    for c in cases:
+        B = len(c["node_offset"]) - 1
+        s, keep, kept, st = G.budget_select(i32(c["node_offset"]), i32(c["parent"]),
+                                            torch.tensor(c["p"], dtype=torch.float32, device="cuda"),
+                                            c["budget"], c["threshold"], max_nodes=8)
+        torch.cuda.synchronize()
+        assert host(st).tolist() == [0] * B, c["name"]
+        assert host(keep).tolist() == c["expected_keep"], c["name"]
+        assert host(kept).tolist() == c["expected_kept"], c["name"]

@@ -511,3 +511,53 @@ def test_acceptance_probs_follow_pages_decay():
     wl = W.make_custom([W.chain(7)] * 400, [0] * 400, Hv=1, Hk=1, d=4)
     p = W.acceptance_probs(wl).reshape(400, 7)
     assert p[:, 0].mean() > facts["first_above"] and p[:, -1].mean() < facts["last_below"]
+
+
+# ----------------------------------------------------------------------------
+# the budget selection's tie order, by hand-built cases
+# ----------------------------------------------------------------------------
+
+def _budget_cases():
+    return json.load(open(os.path.join(GOLDEN, "budget_ties.json")))["cases"]
+
+
+def _keep_by_order(case, key):
+    """The kept set when the valid nodes are ranked by `key(survival, depth, global index)`:
+    a deliberately different ordering, to show that the hand-built cases tell orders apart."""
+    off, par, p = case["node_offset"], case["parent"], np.asarray(case["p"], np.float32)
+    nodes = []
+    for b in range(len(off) - 1):
+        lo, hi = off[b], off[b + 1]
+        s = O.survival(par[lo:hi], p[lo:hi])
+        d = O.depths(par[lo:hi])
+        nodes += [(float(s[t]), d[t], lo + t) for t in range(hi - lo)]
+    keep = [0] * len(par)
+    for s, _, gi in sorted(nodes, key=lambda x: key(*x))[:case["budget"]]:
+        if s >= np.float32(case["threshold"]):
+            keep[gi] = 1
+    return keep
+
+
+@pytest.mark.parametrize("case", _budget_cases(), ids=lambda c: c["name"])
+def test_budget_select_tie_order_hand_cases(case):
+    off = np.asarray(case["node_offset"], np.int32)
+    par = np.asarray(case["parent"], np.int32)
+    p = np.asarray(case["p"], np.float32)
+    s, keep, kept, st = O.budget_select(off, par, p, case["budget"], case["threshold"])
+    assert np.all(st == 0)
+    assert keep.tolist() == case["expected_keep"], case["why"]
+    assert kept.tolist() == case["expected_kept"]
+
+
+def test_budget_tie_cases_reject_other_orders():
+    """Every swapped tie-break loses at least one hand-built case: the cases pin the order."""
+    cases = _budget_cases()
+    assert all(_keep_by_order(c, lambda s, d, i: (-s, d, i)) == c["expected_keep"] for c in cases)
+    mutants = {
+        "index descending": lambda s, d, i: (-s, d, -i),
+        "depth descending": lambda s, d, i: (-s, -d, i),
+        "index before depth": lambda s, d, i: (-s, i, d),
+        "index only after survival, reversed": lambda s, d, i: (-s, -i),
+    }
+    for name, key in mutants.items():
+        assert any(_keep_by_order(c, key) != c["expected_keep"] for c in cases), name
