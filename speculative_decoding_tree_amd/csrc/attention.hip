@@ -159,15 +159,16 @@ __device__ __forceinline__ int nan_end(const AttnArgs &a, int rg, int R) {
 // use KG = 4 or 2 so that no wave idles.
 template <int TPW, int KG>
 __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int sp, int rg, int rot, uint16_t *Ks,
-                                          uint16_t *Vs, int lo, int N, int c0, int R, int row0, int k0, int k1,
-                                          int nctx, int nblk);
+                                          uint16_t *Vs, uint32_t *vnf_all, int lo, int N, int c0, int R, int row0,
+                                          int k0, int k1, int nctx, int nblk);
 
 // One unit: query rows [ROWS rg, ROWS (rg + 1)) of (request b, kv-head hk)
 // against context part sp (and, for part 0, the draft nodes).  Ks / Vs are
-// the workgroup's LDS block; rot only varies which wave takes which rows.
+// the workgroup's LDS block and vnf_all its per-thread record of non-finite
+// node values; rot only varies which wave takes which rows.
 template <int TPW>
 __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int sp, int rg, int rot, uint16_t *Ks,
-                                          uint16_t *Vs) {
+                                          uint16_t *Vs, uint32_t *vnf_all) {
     constexpr int ROWS = 64 * TPW;
     const int tid = threadIdx.x;
 
@@ -191,17 +192,17 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int 
     const int nblk = nctx + (sp == 0 ? 1 : 0);   // the draft nodes' own block goes with the first part
     const int tiles = (min(R - row0, ROWS) + 15) >> 4;
     if (TPW == 1 && tiles == 1)
-        attn_body<TPW, 4>(a, b, hk, sp, rg, rot, Ks, Vs, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+        attn_body<TPW, 4>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
     else if (TPW == 1 && tiles == 2)
-        attn_body<TPW, 2>(a, b, hk, sp, rg, rot, Ks, Vs, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+        attn_body<TPW, 2>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
     else
-        attn_body<TPW, 1>(a, b, hk, sp, rg, rot, Ks, Vs, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+        attn_body<TPW, 1>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
 }
 
 template <int TPW, int KG>
 __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int sp, int rg, int rot, uint16_t *Ks,
-                                          uint16_t *Vs, int lo, int N, int c0, int R, int row0, int k0, int k1,
-                                          int nctx, int nblk) {
+                                          uint16_t *Vs, uint32_t *vnf_all, int lo, int N, int c0, int R, int row0,
+                                          int k0, int k1, int nctx, int nblk) {
     constexpr int ROWS = 64 * TPW;
     static_assert(KG == 1 || TPW == 1, "key groups split one tile per wave");
     constexpr int NKT = 4 / KG;            // this wave's 16-key tiles per block
@@ -286,9 +287,32 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
         for (int mt = 0; mt < 8; ++mt) ot[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // A row's zero weights still meet every staged value row inside the value
+    // product, so a non-finite value of a node the row does not see (NaN or
+    // Inf in another branch) would reach it as 0 * Inf.  A branch sees only
+    // its ancestors (TreeWY, "Method"), so the draft nodes' block is staged
+    // with non-finite values replaced by 0 (select), and vnf_all[tid] records
+    // which of this thread's 32 staged values were (bit 8 q + 2 e + half).  If
+    // any was (rare), each output column whose visible nodes include one that
+    // carried a non-finite value in that column is set to NaN at the end.
+    // Finite values: the same products as without the check.
     load_block(0);
     for (int blk = 0; blk < nblk; ++blk) {
         if (blk > 0) lds_barrier();   // every wave is done with the previous block
+        if (blk >= nctx) {   // the draft nodes' block (the last one; workgroup-uniform)
+            uint32_t vnf = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = vst[q][e];
+                    const bool blo = (w & 0x7f80u) == 0x7f80u, bhi = (w & 0x7f800000u) == 0x7f800000u;
+                    vnf |= (blo ? 1u : 0u) << (8 * q + 2 * e);
+                    vnf |= (bhi ? 1u : 0u) << (8 * q + 2 * e + 1);
+                    vst[q][e] = w & (blo ? 0xffff0000u : 0xffffffffu) & (bhi ? 0x0000ffffu : 0xffffffffu);
+                }
+            vnf_all[tid] = vnf;
+        }
         store_block();
         lds_barrier();
         if (blk + 1 < nblk) load_block(blk + 1);
@@ -421,6 +445,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
                 }
         }
     }
+    // did any staged node value turn out non-finite? (vnf words of all threads,
+    // visible since the node block's barrier; four per lane, one ballot)
+    bool vpoison = false;
+    if (nctx < nblk) {
+        const u32x4 f = *reinterpret_cast<const u32x4 *>(&vnf_all[4 * lane]);
+        vpoison = __ballot((f[0] | f[1] | f[2] | f[3]) != 0u) != 0ull;
+    }
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
         l[tt] += __shfl_xor(l[tt], 16);
@@ -473,6 +504,26 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
     }
 
     // lane (n, grp) holds columns 16 mt + 4 grp .. +3 of its rows
+    if (vpoison) {   // rare: column c of a row turns NaN if a node it sees had a non-finite value there
+        const float qnan = __int_as_float(0x7fc00000);
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            uint32_t pm = 0;   // bit 4 mt + i: column 16 mt + 4 grp + i
+#pragma unroll 1
+            for (int x = 0; x < 32; ++x) {
+                const int col = 16 * (x >> 2) + 4 * grp + (x & 3);
+                for (uint64_t m = anc_row[tt]; m; m &= m - 1) {
+                    const int j = __builtin_ctzll(m);   // node row j was staged by thread 16 (j % 16) + col / 8
+                    if ((vnf_all[16 * (j & 15) + (col >> 3)] >> (8 * (j >> 4) + (col & 7))) & 1u) pm |= 1u << x;
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if ((pm >> (4 * mt + i)) & 1u) ot[tt][mt][i] = qnan;
+        }
+    }
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
         if (!rvalid[tt]) continue;
@@ -507,6 +558,7 @@ template <int TPW>
 __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3 : 2))) void attn_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * D];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[KB * D];
+    __shared__ __attribute__((aligned(16))) uint32_t vnf_all[AT];   // non-finite node values, per thread
     const int n_units = a.B * a.Hkv * a.n_split * a.n_rg;
     const int unit = xcd_unit(blockIdx.x, n_units);
     if (unit >= n_units) return;
@@ -514,7 +566,7 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3
     int rest = unit / a.n_rg;
     const int sp = rest % a.n_split;
     rest /= a.n_split;
-    attn_unit<TPW>(a, rest / a.Hkv, rest % a.Hkv, sp, rg, unit, Ks, Vs);
+    attn_unit<TPW>(a, rest / a.Hkv, rest % a.Hkv, sp, rg, unit, Ks, Vs, vnf_all);
 }
 
 // ---- scheduled launch: a resident grid working through a sorted unit list ----
@@ -635,6 +687,7 @@ template <int TPW>
 __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3 : 2))) void attn_sched_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * D];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[KB * D];
+    __shared__ __attribute__((aligned(16))) uint32_t vnf_all[AT];   // non-finite node values, per thread
     __shared__ AttnSched sc;
     if ((threadIdx.x >> 6) == 0) build_sched(a, sc);
     lds_barrier();
@@ -657,7 +710,7 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3
         const int it = sc.item[lo] & 0xffff, nrg = sc.item[lo] >> 16, j = k - sc.first[lo];
         const int b = it / a.n_split, sp = it - b * a.n_split;
         const int hk = nrg > 0 ? j / nrg : 0, rg = nrg > 0 ? j - hk * nrg : 0;
-        attn_unit<TPW>(a, b, hk, sp, rg, k, Ks, Vs);
+        attn_unit<TPW>(a, b, hk, sp, rg, k, Ks, Vs, vnf_all);
         lds_barrier();   // every wave is done with the LDS block (and the ticket) before the next unit
     }
 }

@@ -43,6 +43,8 @@
 // independent per column, so each wave finishes its own 32 columns alone (LDS
 // operations of one wave complete in order, so one level's writes are seen
 // by the next level).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "mfma.h"
@@ -598,7 +600,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
     // ---- forward substitution over depth levels, this wave's 32 columns ----
     // Lane (k, p) = (lane >> 4, lane & 15) takes node k of each group of four
     // nodes of the level and the column pair c = 32w + 2p.  U rows go to HBM
-    // as soon as their level is done.
+    // as soon as their level is done.  usum is a running sum of the lane's
+    // pseudo-values: it is non-finite when one of them is (or, harmlessly, when
+    // the sum overflows), which sends the wave to the output product that keeps
+    // non-finite values inside their subtree.
+    float usum = 0.f;
     {
         const int kk = lane >> 4;   // == grp
         const int maxdep = sm.maxdep;
@@ -621,6 +627,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
                     }
                     if (L > 1) *reinterpret_cast<float2 *>(&sm.ru[t][c]) = acc2;
                     st_stream2(Ubase + (size_t)t * ustride, acc2);
+                    usum += acc2.x + acc2.y;
                 }
             }
             __builtin_amdgcn_wave_barrier();
@@ -632,7 +639,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
     // transposed table; j > t, j >= N are 0 by select).  B operand: U rows j,
     // this wave's columns (rows j >= N are 0 by select).  Both are split into
     // bf16 hi + lo and combined as hi.hi + hi.lo + lo.hi (~16 mantissa bits).
-    {
+    //
+    // A non-ancestor's pseudo-value still meets its zero in P inside the
+    // product, so a non-finite entry (from a NaN or Inf in that node's g, beta
+    // or v) would reach every row of the tile as 0 * Inf.  A branch reads only
+    // its ancestors (TreeWY, "Method"), so such entries must stay in their
+    // subtree: when the wave holds one (rare: see usum), the product runs with
+    // non-finite U entries replaced by 0 (select), and afterwards every output
+    // whose inclusive ancestors carry a non-finite pseudo-value in its column
+    // is set to NaN.  Each value row of the state evolves on its own under the
+    // gated delta rule, so this is exactly where sequential decode turns
+    // non-finite.  Finite inputs take the plain product: same bits as before.
+    auto output_product = [&](auto sanitize) {
+        constexpr bool SAN = decltype(sanitize)::value;
         const int nks = (N + 31) >> 5;
 #pragma unroll
         for (int tau = 0; tau < KT; ++tau) {
@@ -660,6 +679,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
                     float2 u1 = *reinterpret_cast<const float2 *>(&sm.ru[jr + 1][c]);
                     if (j0 >= N) u0 = make_float2(0.f, 0.f);
                     if (j0 + 1 >= N) u1 = make_float2(0.f, 0.f);
+                    if constexpr (SAN) {
+                        u0.x = __builtin_isfinite(u0.x) ? u0.x : 0.f;
+                        u0.y = __builtin_isfinite(u0.y) ? u0.y : 0.f;
+                        u1.x = __builtin_isfinite(u1.x) ? u1.x : 0.f;
+                        u1.y = __builtin_isfinite(u1.y) ? u1.y : 0.f;
+                    }
                     uint32_t h0, l0, h1, l1;
                     split_bf16x2(u0.x, u1.x, h0, l0);
                     split_bf16x2(u0.y, u1.y, h1, l1);
@@ -695,6 +720,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
                 }
             }
         }
+        if constexpr (SAN) {
+            // output (r, column) turns NaN when an inclusive ancestor of r has a
+            // non-finite pseudo-value in that column (LDS still holds U)
+            const float qnan = __int_as_float(0x7fc00000);
+#pragma unroll
+            for (int tau = 0; tau < KT; ++tau)
+                if (tau < nkt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 16 * tau + 4 * grp + i;
+                        if (r >= N) continue;
+                        bool bad0 = false, bad1 = false;
+                        for (uint64_t m = sm.anc[r]; m; m &= m - 1) {
+                            const float2 uj = *reinterpret_cast<const float2 *>(&sm.ru[__builtin_ctzll(m)][c]);
+                            bad0 = bad0 || !__builtin_isfinite(uj.x);
+                            bad1 = bad1 || !__builtin_isfinite(uj.y);
+                        }
+                        if (bad0) zt[tau][0][i] = qnan;
+                        if (bad1) zt[tau][1][i] = qnan;
+                    }
+        }
         const size_t ostride = (size_t)a.Hv * D;
         float *Obase = a.out + ((size_t)lo * a.Hv + h) * D + c;
 #pragma unroll
@@ -705,7 +751,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
                     const int r = 16 * tau + 4 * grp + i;
                     if (r < N) st_stream2(Obase + (size_t)r * ostride, make_float2(zt[tau][0][i], zt[tau][1][i]));
                 }
-    }
+    };
+    if (__ballot(!__builtin_isfinite(usum)))
+        output_product(std::true_type{});
+    else
+        output_product(std::false_type{});
 }
 
 template <int MODE>

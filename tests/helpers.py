@@ -8,6 +8,14 @@ import numpy as np
 # bf16 q/k/v inputs): max over rows of ||x - ref||_inf / ||ref||_inf.
 TOL = 2e-3
 
+# Regression guard, well inside the bar: the state enters the matrix cores as
+# bf16 hi + lo parts (|H0 - hi - lo| <= 2^-16 |H0|, ~1.5e-5 relative), the
+# decay ratios are exp2 of fp32 path sums, everything accumulates in fp32, and
+# the solve is at most a few levels deep; the observed errors are 5e-7 to
+# ~1.3e-5.  An error above this envelope is a change in the arithmetic long
+# before it threatens the bar.
+ENVELOPE = 1e-4
+
 
 def dev():
     import torch

@@ -22,6 +22,8 @@ import speculative_decoding_tree_amd.gdn_tree as G
 pytestmark = pytest.mark.gpu
 
 ATTN_TOL = 1e-4
+# regression guard inside the bar: the errors these inputs show are ~5e-6 (out) and ~1.4e-6 (lse)
+ATTN_ENVELOPE = 3e-5
 
 
 def _dev():
@@ -49,20 +51,6 @@ def run_attn(wl, split=None, max_nodes=None, max_ctx=None, anc=None):
     return host(out), host(lse), host(st), d
 
 
-def oracle_attn_sampled(wl, reqs):
-    """Oracle rows of the sampled requests only, converting just their slices."""
-    f = lambda x: W.bf16_bits_to_f32(x).astype(np.float64)
-    out = np.full((wl.T, wl.Hq, 128), np.nan)
-    lse = np.full((wl.T, wl.Hq), np.nan)
-    for b in reqs:
-        lo, hi = int(wl.node_offset[b]), int(wl.node_offset[b + 1])
-        c0, c1 = int(wl.ctx_offset[b]), int(wl.ctx_offset[b + 1])
-        out[lo:hi], lse[lo:hi] = A.tree_attention_request(f(wl.q[lo:hi]), f(wl.k_ctx[c0:c1]), f(wl.v_ctx[c0:c1]),
-                                                          f(wl.k_node[lo:hi]), f(wl.v_node[lo:hi]),
-                                                          wl.parent[lo:hi], wl.scale)
-    return out, lse
-
-
 def oracle_attn(wl, requests=None, max_nodes=None, max_ctx=None):
     f = lambda x: W.bf16_bits_to_f32(x).astype(np.float64)
     return A.tree_attention_batch(f(wl.q), f(wl.k_ctx), f(wl.v_ctx), wl.ctx_offset, f(wl.k_node), f(wl.v_node),
@@ -81,8 +69,8 @@ def compare(wl, out, lse, ref_out, ref_lse, reqs):
     e = rowwise_rel_err(out[rows], ref_out[rows])
     el = float(np.abs(lse[rows] - ref_lse[rows]).max()) if rows.size else 0.0
     print(f"{wl.name}: out row-normwise rel err {e:.2e}, lse abs err {el:.2e}")
-    assert e <= ATTN_TOL
-    assert el <= ATTN_TOL
+    assert e <= ATTN_TOL and e <= ATTN_ENVELOPE
+    assert el <= ATTN_TOL and el <= ATTN_ENVELOPE
 
 
 # ---- ancestry ----------------------------------------------------------------
@@ -168,18 +156,30 @@ def test_attention_gqa_groups_and_wide_group():
         compare(wl, out, lse, ref_out, ref_lse, range(wl.B))
 
 
-@pytest.mark.parametrize("split", [None, 1024])
-def test_attention_full_size_sampled(split):
+def test_attention_full_size_every_request():
+    """The batch-256 shape the benchmark times, in both launch modes (one pass and contexts
+    split at 1024 keys): every request against the oracle, one request per task over a pool of
+    oracle processes (~200 s of single-core oracle work)."""
+    import oracle_pool as OP
     wl = W.make_attn_mixed_b256(0)
-    out, lse, st, _ = run_attn(wl, split=split)
-    assert (st == 0).all()
-    kinds = np.array(wl.kinds)
-    lens = np.diff(wl.ctx_offset)
-    reqs = sorted({int(np.flatnonzero(kinds == k)[0]) for k in W.MIXED_KINDS} |
-                  {int(np.argmax(lens)), int(np.argmin(lens)), wl.B - 1})
-    ref_out, ref_lse = oracle_attn_sampled(wl, reqs)
-    compare(wl, out, lse, ref_out, ref_lse, reqs)
-    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    results = {}
+    for i, split in enumerate((None, 1024)):
+        out, lse, st, _ = run_attn(wl, split=split)
+        assert (st == 0).all()
+        assert np.isfinite(out).all() and np.isfinite(lse).all()
+        results[f"out_{i}"], results[f"lse_{i}"] = out, lse
+    arrays = dict(q=wl.q, k_ctx=wl.k_ctx, v_ctx=wl.v_ctx, k_node=wl.k_node, v_node=wl.v_node,
+                  node_offset=wl.node_offset, ctx_offset=wl.ctx_offset, parent=wl.parent,
+                  scale=np.float64(wl.scale), **results)
+    del results
+    rows = OP.run(arrays, OP.attention_request, list(range(wl.B)))
+    assert sorted(r[0] for r in rows) == list(range(wl.B))
+    for i, name in enumerate(("one pass", "split 1024")):
+        eo = max(r[1][i][0] for r in rows if r[1])
+        el = max(r[1][i][1] for r in rows if r[1])
+        print(f"attention batch-256 {name}: all {wl.B} requests, out rel err {eo:.2e}, lse abs err {el:.2e}")
+        assert eo <= ATTN_TOL and el <= ATTN_TOL
+        assert eo <= ATTN_ENVELOPE and el <= ATTN_ENVELOPE
 
 
 def _many_small_requests(B, seed):
@@ -258,3 +258,45 @@ def test_attention_host_errors():
     with pytest.raises(G.GdnTreeError) as e:
         G.attention(*args, wl.scale, max_nodes=64, max_ctx=wl.max_ctx, split=32, workspace=ws)
     assert e.value.code == -8
+
+
+@pytest.mark.parametrize("split", [None, 100])
+def test_attention_non_finite_node_values_stay_in_their_subtree(split):
+    """TreeWY, Method: a node's row reads its own path only.  NaN and Inf in the keys and values of
+    some nodes leave every row that does not see them bit-identical; a row that sees one is
+    non-finite exactly where the oracle is, and its other columns meet the bar.  Cases: key groups
+    (small units), the plain one-tile layout, 64-node trees, and the split context."""
+    import copy
+    base = W.make_attn_small(5)
+    out0, lse0, st0, _ = run_attn(base, split=split)
+    wl = copy.deepcopy(base)
+    hit = []   # (request, node) perturbed
+    for b in range(wl.B):
+        n = int(wl.node_offset[b + 1] - wl.node_offset[b])
+        if n >= 2:
+            j = n - 1 if b % 2 else n // 2
+            t = int(wl.node_offset[b]) + j
+            wl.v_node[t, 0, 3] = 0x7F80       # +Inf, kv head 0, column 3
+            wl.v_node[t, -1, 100] = 0x7FC0    # NaN, last kv head, column 100
+            wl.k_node[t, 0, 7] = 0x7FC0       # NaN key entry: only rows that see the node score it
+            hit.append((b, j))
+    out1, lse1, st1, _ = run_attn(wl, split=split)
+    assert np.array_equal(st0, st1)
+    seen = np.zeros(wl.T, bool)
+    for b, j in hit:
+        lo = int(wl.node_offset[b])
+        anc = O.ancestry(wl.parent[lo:int(wl.node_offset[b + 1])])
+        for t, m in enumerate(anc):
+            seen[lo + t] |= bool((m >> j) & 1)
+    rows = rows_of(wl, range(wl.B))
+    unseen = rows[~seen[rows]]
+    assert np.array_equal(out0[unseen].view(np.uint32), out1[unseen].view(np.uint32))
+    assert np.array_equal(lse0[unseen].view(np.uint32), lse1[unseen].view(np.uint32))
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref_out, ref_lse, _ = oracle_attn(wl)
+    inside = rows[seen[rows]]
+    got, want = out1[inside].astype(np.float64), ref_out[inside]
+    assert np.array_equal(np.isfinite(got), np.isfinite(want))
+    fin = np.isfinite(want)
+    scale = np.abs(np.where(fin, want, 0)).max(axis=-1, keepdims=True)
+    assert (np.abs(np.where(fin, got - want, 0)) / np.maximum(scale, 1e-30)).max() <= ATTN_TOL

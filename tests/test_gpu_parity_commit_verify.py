@@ -13,7 +13,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from helpers import TOL, anc_u64, host, matwise_rel_err, rowwise_rel_err, upload
+from helpers import ENVELOPE, TOL, anc_u64, host, matwise_rel_err, rowwise_rel_err, upload
+import oracle_pool as OP
 
 import speculative_decoding_tree_amd.gdn_tree as G
 
@@ -106,11 +107,13 @@ def oracle_check(P, C, res):
                                        C.Hv, C.Hk, max_nodes=mnC)
     assert np.array_equal(res["st_f"], sto)
     assert np.array_equal(res["anc_f"], anco)
-    assert matwise_rel_err(res["S_f"], S_mid) <= TOL
+    es = matwise_rel_err(res["S_f"], S_mid)
+    assert es <= TOL and es <= ENVELOPE, es
     ok = np.concatenate([np.arange(C.node_offset[b], C.node_offset[b + 1])
                          for b in range(C.B) if sto[b] == 0] + [np.zeros(0, int)]).astype(int)
     eo, eu = rowwise_rel_err(res["out_f"][ok], Oo[ok]), rowwise_rel_err(res["U_f"][ok], Uo[ok])
     assert eo <= TOL and eu <= TOL, (eo, eu)
+    assert eo <= ENVELOPE and eu <= ENVELOPE, (eo, eu)
 
 
 @pytest.mark.parametrize("name", sorted(PAIRS))
@@ -185,27 +188,21 @@ def test_commit_verify_rejects_overlap_and_mismatched_dims():
 
 def test_commit_verify_full_mixed_batch():
     """The launch the benchmark times (256 mixed trees, 48 v-heads): fused equals the two calls bit for
-    bit, and sampled requests (the largest trees included) match the oracle's commit-then-verify."""
+    bit, and every request matches the oracle's commit-then-verify (one request per task over a
+    process pool)."""
     P, C = W.make_mixed_b256(), W.make_mixed_b256(seed=1)
     res = run_pair(P, C)
     assert_same_bits(res)
     assert (res["st_f"] == 0).all() and (res["cst_f"] == 0).all()
-    rng = np.random.default_rng(3)
-    reqs = set(rng.choice(P.B, size=5, replace=False).tolist())
-    reqs |= {int(np.argmax(np.diff(P.node_offset))), int(np.argmax(np.diff(C.node_offset)))}
-    Pq, Pk, Pv, Cq, Ck, Cv = P.q64(), P.k64(), P.v64(), C.q64(), C.k64(), C.v64()
-    worst = [0.0, 0.0, 0.0]
-    for b in sorted(reqs):
-        _, _, _, _, states = O.verify_request(P.S0, Pq, Pk, Pv, P.g, P.beta, P.node_offset, P.parent, b, P.Hv, P.Hk)
-        path = O.accepted_path(P.parents_of(b), int(P.accept_node[b]))
-        S_mid = np.stack([O.commit_unit(P.S0[b, h], states[h], path) for h in range(P.Hv)])
-        worst[0] = max(worst[0], matwise_rel_err(res["S_f"][b], S_mid))
-        _, Ob, Ub, _, _ = O.verify_request(S_mid[None], Cq, Ck, Cv, C.g, C.beta, C.node_offset, C.parent, b, C.Hv,
-                                           C.Hk, state_slot=np.zeros(C.B, np.int32))
-        lo, hi = C.node_offset[b], C.node_offset[b + 1]
-        worst[1] = max(worst[1], rowwise_rel_err(res["out_f"][lo:hi], Ob))
-        worst[2] = max(worst[2], rowwise_rel_err(res["U_f"][lo:hi], Ub))
+    arrays = OP.workload_arrays(P, "P_")
+    arrays.update(OP.workload_arrays(C, "C_"))
+    arrays.update(S_f=res["S_f"], out_f=res["out_f"], U_f=res["U_f"])
+    rows = OP.run(arrays, OP.commit_then_verify_request, [(b, P.Hv, P.Hk) for b in range(P.B)])
+    assert sorted(r[0] for r in rows) == list(range(P.B))
+    worst = [max(r[k] for r in rows) for k in (1, 2, 3)]
+    print(f"commit_verify mixed_b256: all {P.B} requests, worst rel err S'/out/U: {worst}")
     assert max(worst) <= TOL, worst
+    assert max(worst) <= ENVELOPE, worst
 
 
 def test_commit_verify_state_slot_permutation():
@@ -263,3 +260,34 @@ def test_accept_commit_verify_equals_accept_commit_then_verify(name):
     else:
         assert (res["cst_f"] == 0).all() and (res["acc"] >= 0).any()
         oracle_check(P, C, res)
+
+
+@pytest.mark.parametrize("kind", ["nan_g", "inf_v"])
+def test_commit_verify_non_finite_sibling_stays_in_subtree(kind):
+    """The one-launch step keeps a NaN or Inf of one next-tree node inside its subtree: other
+    nodes' outputs and pseudo-values, and every committed state, keep their bits."""
+    P, C = PAIRS["mixed_to_mixed_nm64"]()
+    clean = run_pair(P, C)
+    C2 = W.make_mixed_b256(seed=1, per_kind=3, Hv=6, Hk=2)
+    sub_rows = []
+    for b in range(0, C2.B, 3):
+        j = C2.nodes(b) // 2
+        t = int(C2.node_offset[b]) + j
+        if kind == "nan_g":
+            C2.g[t, 1:] = np.nan
+        else:
+            C2.v[t, :, 9] = 0x7F80
+        anc = O.ancestry(C2.parents_of(b))
+        sub_rows += [int(C2.node_offset[b]) + s for s in range(C2.nodes(b)) if (anc[s] >> j) & 1]
+    bad = run_pair(P, C2)
+    # fused and two-launch forms agree: same bits where finite, NaN at the same places
+    for a, b in (("S_r", "S_f"), ("out_r", "out_f"), ("U_r", "U_f")):
+        x, y = bad[a], bad[b]
+        assert np.array_equal(np.isnan(x), np.isnan(y)), a
+        assert np.array_equal(np.where(np.isnan(x), 0, x).view(np.uint32), np.where(np.isnan(y), 0, y).view(np.uint32)), a
+    assert np.array_equal(clean["S_f"].view(np.uint32), bad["S_f"].view(np.uint32))
+    outside = np.setdiff1d(np.arange(C.T), sub_rows)
+    for key in ("out_f", "U_f"):
+        assert np.array_equal(clean[key][outside].view(np.uint32), bad[key][outside].view(np.uint32)), key
+        inside = bad[key][sub_rows]
+        assert not np.isfinite(inside).all()

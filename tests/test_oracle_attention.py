@@ -104,6 +104,35 @@ def test_non_ancestors_do_not_matter_ancestors_do():
     np.testing.assert_array_equal(moved[2], base[2])
 
 
+def test_non_finite_values_of_other_branches_do_not_reach_a_row():
+    """TreeWY, Method: a node's row sees its own path only.  NaN or Inf in the keys
+    and values of nodes off that path leave the row's output and lse bit-identical;
+    an Inf in an ancestor's value makes exactly that value column non-finite."""
+    par = np.array([-1, 0, 0, 1, 2], np.int32)      # node 3 sees {0, 1, 3}; nodes 2, 4 are off its path
+    wl = W.make_attn([par], [5], Hq=4, Hkv=2, seed=5)
+    f = lambda x: W.bf16_bits_to_f32(x).astype(np.float64)
+    args = lambda kn, vn: (f(wl.q), f(wl.k_ctx), f(wl.v_ctx), wl.ctx_offset, kn, vn, wl.node_offset, wl.parent,
+                           wl.Hq, wl.Hkv, wl.scale)
+    base, base_lse, _ = A.tree_attention_batch(*args(f(wl.k_node), f(wl.v_node)))
+    kn, vn = f(wl.k_node), f(wl.v_node)
+    kn[2, :, 5] = np.nan
+    vn[2, :, 7] = np.inf
+    vn[4, 1, 9] = np.nan
+    with np.errstate(invalid="ignore"):
+        other, other_lse, _ = A.tree_attention_batch(*args(kn, vn))
+    for t in (1, 3):
+        np.testing.assert_array_equal(other[t], base[t])
+        np.testing.assert_array_equal(other_lse[t], base_lse[t])
+    kn, vn = f(wl.k_node), f(wl.v_node)
+    vn[1, 0, 7] = np.inf                              # ancestor of node 3, kv head 0 (query heads 0, 1)
+    with np.errstate(invalid="ignore"):
+        moved, moved_lse, _ = A.tree_attention_batch(*args(kn, vn))
+    assert not np.isfinite(moved[3, :2, 7]).any() and np.isfinite(np.delete(moved[3, :2], 7, axis=1)).all()
+    np.testing.assert_array_equal(moved[3, 2:], base[3, 2:])
+    np.testing.assert_array_equal(moved_lse, base_lse)
+    np.testing.assert_array_equal(moved[2], base[2])
+
+
 def test_requests_are_independent_under_permutation():
     wl = W.make_attn_small(2)
     perm = [3, 0, 7, 1, 6, 2, 5, 4]

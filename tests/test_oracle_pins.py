@@ -265,6 +265,43 @@ def test_sibling_invariance(seed):
                 assert not np.array_equal(O0[t], O1[t])
 
 
+@pytest.mark.parametrize("kind", ["nan_g", "nan_beta", "inf_v"])
+def test_non_finite_input_stays_in_its_subtree(kind):
+    """TreeWY, Method: a branch reads only its common ancestors, never the other
+    branch, so a NaN or Inf in one node's inputs reaches its subtree and nothing
+    else: every other node's output and pseudo-value keep their bits.  Inside the
+    subtree it reaches exactly the value rows it touches: under the gated delta
+    rule row i of the state is updated from component i of v and of u alone
+    (u_i = beta (v_i - alpha (S k)_i), S_i. <- alpha S_i. + u_i k^T), so an Inf in
+    v[c] makes column c non-finite in the subtree and leaves the other columns'
+    bits unchanged, while a NaN gate or beta spoils every column there."""
+    rng = np.random.default_rng(21)
+    n, d = 14, 6
+    par = [-1, 0, 1, 0, 3, 4, -1, 6, 2, 8, 5, 3, 11, 7]
+    H0, q, k, v, g, beta = _unit_inputs(rng, n, d)
+    O0, U0, _ = O.verify_unit(H0, q, k, v, g, beta, par)
+    for j in (1, 3, 6):
+        g2, b2, v2 = g.copy(), beta.copy(), v.copy()
+        if kind == "nan_g":
+            g2[j] = np.nan
+        elif kind == "nan_beta":
+            b2[j] = np.nan
+        else:
+            v2[j, 2] = np.inf
+        with np.errstate(invalid="ignore", over="ignore"):
+            O1, U1, _ = O.verify_unit(H0, q, k, v2, g2, b2, par)
+        inside = subtree(par, j)
+        for t in range(n):
+            if t not in inside:
+                assert np.array_equal(O0[t], O1[t]) and np.array_equal(U0[t], U1[t]), (j, t)
+            elif kind == "inf_v":
+                other = [c for c in range(d) if c != 2]
+                assert not np.isfinite(O1[t, 2]) and not np.isfinite(U1[t, 2]), (j, t)
+                assert np.array_equal(O0[t, other], O1[t, other]) and np.array_equal(U0[t, other], U1[t, other])
+            else:
+                assert not np.isfinite(O1[t]).any() and not np.isfinite(U1[t]).any(), (j, t)
+
+
 def test_relabelling_permutes_results():
     """Another parent-before-child order of the same tree permutes the outputs."""
     rng = np.random.default_rng(7)
