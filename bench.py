@@ -132,12 +132,18 @@ def _oracle_request(args):
     return len(parent)
 
 
-def cpu_baseline(wl, n_req: int, min_seconds: float = 10.0):
+def cpu_baseline(wl, n_req: int, min_seconds: float = 10.0, one_core_seconds: float = 4.0):
     """The oracle on the host cores: the first n_req requests, repeated whole
-    until at least min_seconds of work have run."""
+    until at least min_seconds of work have run, one process per core; then the
+    same work in this process alone (one core) for about one_core_seconds.
+
+    The pool takes every core this process may run on, at most 16: a host that
+    carries one GPU gives it a share of 16 cores, whatever the affinity mask
+    shows (the mask is reported beside it)."""
     import multiprocessing as mp
     import numpy as np
-    cores = min(16, len(os.sched_getaffinity(0)))
+    avail = len(os.sched_getaffinity(0))
+    cores = min(16, avail)
     q, k, v = wl.q64(), wl.k64(), wl.v64()
     jobs = []
     for b in range(min(n_req, wl.B)):
@@ -153,10 +159,18 @@ def cpu_baseline(wl, n_req: int, min_seconds: float = 10.0):
             nodes += sum(pool.map(_oracle_request, jobs, chunksize=1))
             passes += 1
         dt = time.perf_counter() - t0
+    # one core: the same requests in order, in this process
+    t1 = time.perf_counter()
+    n1, i = 0, 0
+    while i == 0 or time.perf_counter() - t1 < one_core_seconds:
+        n1 += _oracle_request(jobs[i % len(jobs)])
+        i += 1
+    dt1 = time.perf_counter() - t1
     return {"value": nodes / dt, "unit": "nodes/s", "cores": cores, "kind": "oracle",
             "sample": f"first {len(jobs)} of {wl.B} requests of the {wl.name} batch, {passes} passes "
                       f"({nodes} nodes, all {wl.Hv} heads), fp64 verify + commit, one process per core",
-            "seconds": dt}
+            "seconds": dt, "cores_in_affinity_mask": avail,
+            "one_core": {"value": n1 / dt1, "unit": "nodes/s", "requests": i, "nodes": n1, "seconds": dt1}}
 
 
 # ----------------------------------------------------------------------------
@@ -414,6 +428,77 @@ def batch_one_row(args, stream):
             "graph_step_us": t_graph, "commit_verify_step_us": t_fused, "commit_verify_graph_step_us": t_fgraph}
 
 
+def config_rows(args, stream):
+    """The other workloads the pages' shapes give (depth-3 chains at batch 64, the
+    6-node root-branch tree at batch 16 and 1, random 32-node trees at batch 256):
+    the one-launch step (gdn_tree_commit_verify, the batch playing both trees, out
+    of place) and the two-launch step (gdn_tree_verify + gdn_tree_commit_node),
+    each with nodes/s, commits/s and its fraction of the HBM peak.  Three copies of
+    every buffer rotate, as in the headline loop."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from speculative_decoding_tree_amd import gdn_tree as G
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    rows = {}
+    makers = (("chain3_b64", W.make_chain3_b64), ("rootbranch6_b16", lambda: W.make_root_branch6(B=16)),
+              ("rootbranch6_b1", lambda: W.make_root_branch6(B=1)), ("random32_b256", W.make_random32_b256))
+    n = max(20, args.steps // 2)
+    for name, make in makers:
+        wl = make()
+        mn = wl.max_nodes
+        pools = []
+        for _ in range(max(1, args.pools)):
+            p = dict(S0=torch.from_numpy(wl.S0).to(dev), q=bf(wl.q), k=bf(wl.k), v=bf(wl.v),
+                     g=torch.from_numpy(wl.g).to(dev), beta=torch.from_numpy(wl.beta).to(dev),
+                     off=torch.from_numpy(wl.node_offset).to(dev), par=torch.from_numpy(wl.parent).to(dev),
+                     acc=torch.from_numpy(wl.accept_node).to(dev))
+            p["S_out"] = torch.empty_like(p["S0"])
+            for key in ("out", "U", "out2", "U2"):
+                p[key] = torch.empty((wl.T, wl.Hv, D), dtype=torch.float32, device=dev)
+            p["anc"] = torch.empty((wl.T,), dtype=torch.int64, device=dev)
+            for key in ("st", "cst", "plen"):
+                p[key] = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+            p["path"] = torch.empty((wl.B, mn), dtype=torch.int32, device=dev)
+            pools.append(p)
+
+        def two(i):
+            p = pools[i % len(pools)]
+            G.verify(p["S0"], p["q"], p["k"], p["v"], p["g"], p["beta"], p["off"], p["par"], max_nodes=mn,
+                     out=p["out"], U=p["U"], anc_mask=p["anc"], status=p["st"], stream=stream)
+            G.commit_node(p["S0"], p["U"], p["k"], p["g"], p["off"], p["par"], p["acc"], max_nodes=mn,
+                          S_out=p["S_out"], path=p["path"], path_len=p["plen"], status=p["cst"], stream=stream)
+
+        def one(i):
+            p = pools[i % len(pools)]
+            prev = dict(U=p["U"], k=p["k"], g=p["g"], node_offset=p["off"], parent=p["par"], max_nodes=mn)
+            G.commit_verify(p["S0"], prev, p["acc"], p["q"], p["k"], p["v"], p["g"], p["beta"], p["off"], p["par"],
+                            max_nodes=mn, S_out=p["S_out"], out=p["out2"], U=p["U2"], anc_mask=p["anc"],
+                            status=p["st"], commit_status=p["cst"], path=p["path"], path_len=p["plen"],
+                            stream=stream)
+
+        t_two = _time_launches(two, n, stream)      # also leaves every pool's U for the one-launch step
+        t_one = _time_launches(one, n, stream)
+        st = np.concatenate([p["st"].cpu().numpy() for p in pools] + [p["cst"].cpu().numpy() for p in pools])
+        if not (st == 0).all():
+            raise RuntimeError(f"{name}: device status nonzero")
+        L = pools[0]["plen"].cpu().numpy()
+        vb, cb = verify_bytes(wl), commit_bytes(wl, L)
+        fb = vb + cb - wl.B * wl.Hv * D * D * 4
+        rows[name] = {
+            "B": wl.B, "Hv": wl.Hv, "Hk": wl.Hk, "T": wl.T, "max_nodes": mn, "mean_accepted_len": float(L.mean()),
+            "one_launch": {"avg_us": t_one, "nodes_per_s": wl.T / (t_one * 1e-6), "commits_per_s": wl.B / (t_one * 1e-6),
+                           "alg_bytes": fb, "alg_GBps": fb / (t_one * 1e-6) / 1e9,
+                           "hbm_frac": fb / (t_one * 1e-6) / 1e9 / HBM_PEAK_GBS},
+            "two_launch": {"avg_us": t_two, "nodes_per_s": wl.T / (t_two * 1e-6), "commits_per_s": wl.B / (t_two * 1e-6),
+                           "alg_bytes": vb + cb, "alg_GBps": (vb + cb) / (t_two * 1e-6) / 1e9,
+                           "hbm_frac": (vb + cb) / (t_two * 1e-6) / 1e9 / HBM_PEAK_GBS}}
+        del pools
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -427,6 +512,7 @@ def main():
     ap.add_argument("--no-next", action="store_true", help="skip the next-row measurements")
     ap.add_argument("--no-attention", action="store_true", help="skip the tree-bias attention measurement")
     ap.add_argument("--no-batch-one", action="store_true", help="skip the batch-one latency measurement")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' rows")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -583,7 +669,7 @@ def main():
     result = {
         "metric": METRIC, "value": nodes_per_s, "unit": "nodes/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_fused, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 hi/lo MFMA, fp32 accumulate", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "Hv": wl.Hv, "Hk": wl.Hk, "d_k": D, "d_v": D, "T": wl.T,
                    "max_nodes": mn, "trees": ("64 each of chain-3, root-branch-6, random-16, random-64"
                                               if args.workload == "mixed_b256" else "random-32, depth <= 6"),
@@ -644,6 +730,9 @@ def main():
             result["next_rows"]["tree_attention"] = attention_row(args, stream)
         if not args.no_batch_one:
             result["next_rows"]["batch_one"] = batch_one_row(args, stream)
+
+    if not args.no_configs:
+        result["configs"] = config_rows(args, stream)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)

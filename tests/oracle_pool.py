@@ -15,7 +15,9 @@ from __future__ import annotations
 import multiprocessing as mp
 import os
 import shutil
+import sys
 import tempfile
+import time
 
 import numpy as np
 
@@ -33,16 +35,41 @@ def _init(dirname, names):
         _D[n] = np.load(os.path.join(dirname, n + ".npy"), mmap_mode="r")
 
 
-def run(arrays: dict, fn, items):
-    """fn(item) for every item, in worker processes that see `arrays` (by name) as _D."""
+_THREAD_VARS = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+
+
+def run(arrays: dict, fn, items, label: str = ""):
+    """fn(item) for every item, in worker processes that see `arrays` (by name) as _D.
+
+    Each worker's BLAS runs single-threaded (the variables are set before the
+    workers start, so numpy sees them at import): one process per core is the
+    parallelism.  A progress line goes to the process's real stderr every ~20 s,
+    past any output capture, so a long comparison is visibly alive."""
+    items = list(items)
     tmp = tempfile.mkdtemp(prefix="gdn_oracle_pool_")
+    saved = {k: os.environ.get(k) for k in _THREAD_VARS}
     try:
         for name, arr in arrays.items():
             np.save(os.path.join(tmp, name + ".npy"), np.ascontiguousarray(arr))
+        for k in _THREAD_VARS:
+            os.environ[k] = "1"
         ctx = mp.get_context("spawn")
+        out, t0 = [], time.time()
+        last = t0
         with ctx.Pool(pool_size(), initializer=_init, initargs=(tmp, list(arrays))) as pool:
-            return pool.map(fn, items, chunksize=1)
+            for r in pool.imap_unordered(fn, items, chunksize=1):
+                out.append(r)
+                if time.time() - last > 20:
+                    last = time.time()
+                    print(f"[oracle pool {label}] {len(out)}/{len(items)} done in {last - t0:.0f} s",
+                          file=sys.__stderr__, flush=True)
+        return out
     finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
         shutil.rmtree(tmp, ignore_errors=True)
 
 
