@@ -74,7 +74,8 @@
 extern "C" {
 #endif
 
-#define GDN_TREE_ABI_VERSION 2   /* 2: gdn_tree_commit_verify, gdn_tree_accept_commit_verify, GDN_TREE_E_OVERLAP */
+#define GDN_TREE_ABI_VERSION 3   /* 2: gdn_tree_commit_verify, gdn_tree_accept_commit_verify, GDN_TREE_E_OVERLAP;
+                                    3: gdn_tree_attention_static, GDN_TREE_E_SCRATCH */
 #define GDN_TREE_MAX_NODES 64   /* per request: one wave64 lane and one uint64 bit per node */
 #define GDN_TREE_HEAD_DIM 128
 
@@ -89,6 +90,11 @@ extern "C" {
 #define GDN_TREE_E_ALIGN (-7)     /* a state / q / k / v / out / U / node_state pointer is not 16-byte aligned */
 #define GDN_TREE_E_WORKSPACE (-8) /* attention workspace missing, misaligned or smaller than required */
 #define GDN_TREE_E_OVERLAP (-9)   /* gdn_tree_commit_verify: out or U overlaps U_prev */
+#define GDN_TREE_E_SCRATCH (-10)  /* gdn_tree_attention_static: the call needs more than the static scratch holds,
+                                     or the scratch's device address could not be obtained */
+
+/* Bytes of the per-device static scratch of gdn_tree_attention_static. */
+#define GDN_TREE_STATIC_SCRATCH_BYTES (64u << 20)
 
 /* device-side per-request status codes (status[b]) */
 #define GDN_TREE_S_OK 0
@@ -377,6 +383,31 @@ int gdn_tree_attention(const gdn_tree_attn_dims *dims, const uint16_t *q, const 
 /* Workspace bytes gdn_tree_attention needs for dims: 256 for one pass, more
  * when split < max_ctx; 0 when B = 0 or dims are invalid.  Host only. */
 size_t gdn_tree_attention_workspace_bytes(const gdn_tree_attn_dims *dims);
+
+/*
+ * gdn_tree_attention_static -- gdn_tree_attention without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments (minus workspace and workspace_bytes), results and error
+ * behaviour as gdn_tree_attention, bit for bit.  The work-distribution
+ * counters and the partial results of a split context live in a static device
+ * array of GDN_TREE_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on
+ * every GPU it runs on until the process ends; the call allocates nothing.
+ * Its first call on a device looks up that device's copy of the array.  A
+ * call whose workspace need (gdn_tree_attention_workspace_bytes) exceeds the
+ * array returns GDN_TREE_E_SCRATCH and enqueues nothing: one pass always
+ * fits (256 bytes); a split context fits while B * Hkv * parts * row groups
+ * <= 2016 (33,280 bytes per partial record).  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (concurrent streams, or
+ * graphs replayed concurrently) race and must be serialised by the caller.
+ * The counters are cleared on the stream by each call; partial records are
+ * written before they are read, so nothing left by an earlier call is used.
+ */
+int gdn_tree_attention_static(const gdn_tree_attn_dims *dims, const uint16_t *q, const uint16_t *k_ctx,
+                              const uint16_t *v_ctx, const int32_t *ctx_offset, const uint16_t *k_node,
+                              const uint16_t *v_node, const int32_t *node_offset, const uint64_t *anc_mask,
+                              float scale, float *out, float *lse, int32_t *status, void *stream);
 
 /*
  * gdn_tree_verify_storeall -- the snapshot-per-node comparison scheme.

@@ -113,6 +113,7 @@ const char *gdn_tree_strerror(int code) {
         case GDN_TREE_E_ALIGN: return "state, q, k, v, out, U and node_state pointers must be 16-byte aligned";
         case GDN_TREE_E_WORKSPACE: return "attention workspace missing, misaligned or too small";
         case GDN_TREE_E_OVERLAP: return "out or U overlaps U_prev";
+        case GDN_TREE_E_SCRATCH: return "the call needs more than the static scratch holds (or its address is unavailable)";
         case GDN_TREE_S_BAD_OFFSETS: return "status: node_offset out of order or beyond T";
         case GDN_TREE_S_TOO_MANY: return "status: request has more than max_nodes nodes";
         case GDN_TREE_S_BAD_PARENT: return "status: parent[t] must satisfy -1 <= parent[t] < t";
@@ -452,11 +453,19 @@ size_t gdn_tree_attention_workspace_bytes(const gdn_tree_attn_dims *dims) {
     return attn_workspace(dims, n_split, n_rg);
 }
 
-int gdn_tree_attention(const gdn_tree_attn_dims *dims, const uint16_t *q, const uint16_t *k_ctx,
-                       const uint16_t *v_ctx, const int32_t *ctx_offset, const uint16_t *k_node,
-                       const uint16_t *v_node, const int32_t *node_offset, const uint64_t *anc_mask,
-                       float scale, float *out, float *lse, void *workspace, size_t workspace_bytes,
-                       int32_t *status, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and argument block shared by the two attention entry points; `need`
+// receives the workspace bytes of the launch.  Returns a GDN_TREE_* code
+// (GDN_TREE_OK with a.B == 0: nothing to do).
+int attention_args(gdn::AttnArgs &a, size_t &need, const gdn_tree_attn_dims *dims, const uint16_t *q,
+                   const uint16_t *k_ctx, const uint16_t *v_ctx, const int32_t *ctx_offset, const uint16_t *k_node,
+                   const uint16_t *v_node, const int32_t *node_offset, const uint64_t *anc_mask, float scale,
+                   float *out, float *lse, int32_t *status) {
+    a = {};
+    need = 0;
     int n_split, n_rg;
     int rc = check_attn_dims(dims, n_split, n_rg);
     if (rc != GDN_TREE_OK || dims->B == 0) return rc;
@@ -467,9 +476,7 @@ int gdn_tree_attention(const gdn_tree_attn_dims *dims, const uint16_t *q, const 
     if (dims->T > 0 && (!q || !k_node || !v_node || !anc_mask || !out)) return GDN_TREE_E_NULL;
     if (dims->C > 0 && (!k_ctx || !v_ctx)) return GDN_TREE_E_NULL;
     if (any_misaligned(q, k_ctx, v_ctx, k_node, v_node, out)) return GDN_TREE_E_ALIGN;
-    const size_t need = attn_workspace(dims, n_split, n_rg);
-    if (!workspace || misaligned(workspace) || workspace_bytes < need) return GDN_TREE_E_WORKSPACE;
-    gdn::AttnArgs a = {};
+    need = attn_workspace(dims, n_split, n_rg);
     a.B = dims->B;
     a.Hq = dims->Hq;
     a.Hkv = dims->Hkv;
@@ -493,8 +500,43 @@ int gdn_tree_attention(const gdn_tree_attn_dims *dims, const uint16_t *q, const 
     a.anc_mask = anc_mask;
     a.out = out;
     a.lse = lse;
-    a.ws = static_cast<float *>(workspace);
     a.status = status;
+    return GDN_TREE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_tree_attention(const gdn_tree_attn_dims *dims, const uint16_t *q, const uint16_t *k_ctx,
+                       const uint16_t *v_ctx, const int32_t *ctx_offset, const uint16_t *k_node,
+                       const uint16_t *v_node, const int32_t *node_offset, const uint64_t *anc_mask,
+                       float scale, float *out, float *lse, void *workspace, size_t workspace_bytes,
+                       int32_t *status, void *stream) {
+    gdn::AttnArgs a;
+    size_t need;
+    int rc = attention_args(a, need, dims, q, k_ctx, v_ctx, ctx_offset, k_node, v_node, node_offset, anc_mask, scale,
+                            out, lse, status);
+    if (rc != GDN_TREE_OK || a.B == 0) return rc;
+    if (!workspace || misaligned(workspace) || workspace_bytes < need) return GDN_TREE_E_WORKSPACE;
+    a.ws = static_cast<float *>(workspace);
+    clear_pending();
+    return finish(gdn::launch_attention(a, (hipStream_t)stream));
+}
+
+int gdn_tree_attention_static(const gdn_tree_attn_dims *dims, const uint16_t *q, const uint16_t *k_ctx,
+                              const uint16_t *v_ctx, const int32_t *ctx_offset, const uint16_t *k_node,
+                              const uint16_t *v_node, const int32_t *node_offset, const uint64_t *anc_mask,
+                              float scale, float *out, float *lse, int32_t *status, void *stream) {
+    gdn::AttnArgs a;
+    size_t need;
+    int rc = attention_args(a, need, dims, q, k_ctx, v_ctx, ctx_offset, k_node, v_node, node_offset, anc_mask, scale,
+                            out, lse, status);
+    if (rc != GDN_TREE_OK || a.B == 0) return rc;
+    if (need > GDN_TREE_STATIC_SCRATCH_BYTES) return GDN_TREE_E_SCRATCH;
+    void *ws = nullptr;
+    if (gdn::static_scratch(&ws) != hipSuccess || !ws) return GDN_TREE_E_SCRATCH;
+    a.ws = static_cast<float *>(ws);
     clear_pending();
     return finish(gdn::launch_attention(a, (hipStream_t)stream));
 }

@@ -865,6 +865,33 @@ int resident_workgroups() {
 }
 }  // namespace
 
+// ---- the workspace of the allocation-free entry point ------------------------
+// A file-scope device array: every GPU the library runs on holds its own copy
+// until the process ends.  On the host the array's name is only a stand-in, not
+// a device address, so no host code passes it to a kernel or a copy: the first
+// call on each device looks up that device's copy with hipGetSymbolAddress
+// (with the device current) and keeps the address per device.
+static __device__ __align__(256) unsigned char scratch[GDN_TREE_STATIC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<void *> g_scratch[MAX_DEVICES];
+}  // namespace
+
+hipError_t static_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
     if (a.rows_wg != 64) return hipErrorInvalidValue;   // the host sizes units for one tile per wave
     const int units = a.B * a.Hkv * a.n_split * a.n_rg;

@@ -20,6 +20,9 @@ hipError_t launch_commit_replay(const Args &a, hipStream_t stream);
 hipError_t launch_budget_select(const Args &a, int budget, float threshold, hipStream_t stream);
 hipError_t launch_ancestry(const Args &a, hipStream_t stream);
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream);
+// Device address of the calling device's copy of the static attention scratch
+// (GDN_TREE_STATIC_SCRATCH_BYTES), looked up once per device.
+hipError_t static_scratch(void **ptr);
 hipError_t launch_verify_storeall(const Args &a, hipStream_t stream);
 hipError_t launch_commit_storeall(const Args &a, hipStream_t stream);
 

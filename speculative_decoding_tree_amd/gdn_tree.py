@@ -34,6 +34,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "gdn_tree.h")
 
 HEAD_DIM = 128
 MAX_NODES = 64
+STATIC_SCRATCH_BYTES = 64 << 20   # GDN_TREE_STATIC_SCRATCH_BYTES
 
 # status codes (include/gdn_tree.h)
 (S_OK, S_BAD_OFFSETS, S_TOO_MANY, S_BAD_PARENT, S_BAD_PATH, S_BAD_ACCEPT, S_BAD_SLOT, S_BAD_CONTEXT,
@@ -76,6 +77,7 @@ _SIGS = {
     "gdn_tree_ancestry": [ctypes.POINTER(Dims)] + [_P] * 5,
     "gdn_tree_attention": [ctypes.POINTER(AttnDims)] + [_P] * 8 + [ctypes.c_float, _P, _P, _P, ctypes.c_size_t,
                                                                    _P, _P],
+    "gdn_tree_attention_static": [ctypes.POINTER(AttnDims)] + [_P] * 8 + [ctypes.c_float, _P, _P, _P, _P],
 }
 
 _lib = None
@@ -535,4 +537,32 @@ def attention(q, k_ctx, v_ctx, ctx_offset, k_node, v_node, node_offset, anc_mask
         _ptr(out, "out", _F32, (T, Hq, HEAD_DIM)), _ptr(lse, "lse", _F32, (T, Hq)),
         ws_ptr, ctypes.c_size_t(ws_bytes), _ptr(status, "status", _I32, (B,)), _stream(stream))
     _check("gdn_tree_attention", rc)
+    return out, lse, status
+
+
+def attention_static(q, k_ctx, v_ctx, ctx_offset, k_node, v_node, node_offset, anc_mask, scale: float,
+                     max_nodes: int, max_ctx: int, split: Optional[int] = None, out=None, lse=None, status=None,
+                     stream=None):
+    """gdn_tree_attention_static: gdn_tree_attention with the library's static per-device
+    scratch instead of a workspace (no allocation by the library).  Returns (out, lse, status);
+    out, lse and status are allocated here unless given (pass them to allocate nothing)."""
+    B = int(node_offset.numel()) - 1
+    T, Hq = int(q.shape[0]), int(q.shape[1])
+    C, Hkv = int(k_ctx.shape[0]), int(k_ctx.shape[1])
+    dev = q.device
+    dims = make_attn_dims(B, Hq, Hkv, T, C, max_nodes, max_ctx, split)
+    out = out if out is not None else torch.empty((T, Hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    lse = lse if lse is not None else torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    status = status if status is not None else torch.empty((B,), dtype=torch.int32, device=dev)
+    rc = lib().gdn_tree_attention_static(
+        ctypes.byref(dims),
+        _ptr(q, "q", _B16, (T, Hq, HEAD_DIM)),
+        _ptr(k_ctx, "k_ctx", _B16, (C, Hkv, HEAD_DIM)), _ptr(v_ctx, "v_ctx", _B16, (C, Hkv, HEAD_DIM)),
+        _ptr(ctx_offset, "ctx_offset", _I32, (B + 1,)),
+        _ptr(k_node, "k_node", _B16, (T, Hkv, HEAD_DIM)), _ptr(v_node, "v_node", _B16, (T, Hkv, HEAD_DIM)),
+        _ptr(node_offset, "node_offset", _I32, (B + 1,)), _ptr(anc_mask, "anc_mask", _U64, (T,)),
+        ctypes.c_float(scale),
+        _ptr(out, "out", _F32, (T, Hq, HEAD_DIM)), _ptr(lse, "lse", _F32, (T, Hq)),
+        _ptr(status, "status", _I32, (B,)), _stream(stream))
+    _check("gdn_tree_attention_static", rc)
     return out, lse, status

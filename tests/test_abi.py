@@ -15,10 +15,11 @@ def test_library_exports_every_declared_symbol():
     assert {"gdn_tree_verify", "gdn_tree_commit", "gdn_tree_accepted_path", "gdn_tree_verify_storeall",
             "gdn_tree_commit_storeall", "gdn_tree_state_bytes", "gdn_tree_strerror",
             "gdn_tree_abi_version", "gdn_tree_accept_greedy", "gdn_tree_accept_commit", "gdn_tree_commit_node", "gdn_tree_commit_replay", "gdn_tree_budget_select", "gdn_tree_commit_verify", "gdn_tree_accept_commit_verify",
-            "gdn_tree_ancestry", "gdn_tree_attention", "gdn_tree_attention_workspace_bytes"} <= set(names)
+            "gdn_tree_ancestry", "gdn_tree_attention", "gdn_tree_attention_workspace_bytes",
+            "gdn_tree_attention_static"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert G.abi_version() == 2
+    assert G.abi_version() == 3
 
 
 def test_header_constants_match_binding():
@@ -42,7 +43,7 @@ def test_attention_status_codes_agree_with_oracle_numbers():
 
 
 def test_strerror_never_null():
-    for c in range(-10, 10):
+    for c in range(-11, 10):
         assert isinstance(G.strerror(c), str) and G.strerror(c)
 
 
@@ -243,3 +244,35 @@ def test_accept_commit_verify_host_validation():
         assert acv(**{name: None}) == -1, name
     bad = G.make_dims(4, 32, 8, 20, 8, 4)
     assert L.gdn_tree_accept_commit_verify(ctypes.byref(bad), ctypes.byref(d), *([None] * 27)) == -2
+
+
+def test_attention_static_host_validation():
+    """The allocation-free attention entry point: the same host checks as gdn_tree_attention, and
+    a call whose workspace need exceeds the static scratch is refused before anything else."""
+    L = G.lib()
+    text = open(G.HEADER).read()
+    assert "#define GDN_TREE_STATIC_SCRATCH_BYTES (64u << 20)" in text and G.STATIC_SCRATCH_BYTES == 64 << 20
+    fake = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: the calls below fail on the host
+    args = lambda: [fake] * 8 + [ctypes.c_float(0.1), fake, fake, None, None]
+    # B = 0: nothing to do
+    d = G.make_attn_dims(0, 8, 2, 0, 0, 4, 0)
+    assert L.gdn_tree_attention_static(ctypes.byref(d), *([None] * 8), ctypes.c_float(0.1), None, None, None,
+                                       None) == 0
+    # bad dims, bad scale, null pointers, misalignment: the same codes as gdn_tree_attention
+    d = G.make_attn_dims(4, 8, 3, 10, 100, 8, 50)
+    assert L.gdn_tree_attention_static(ctypes.byref(d), *args()) == -2
+    d = G.make_attn_dims(4, 8, 2, 10, 100, 8, 50)
+    a = args()
+    a[8] = ctypes.c_float(0.0)
+    assert L.gdn_tree_attention_static(ctypes.byref(d), *a) == -2
+    a = args()
+    a[0] = None
+    assert L.gdn_tree_attention_static(ctypes.byref(d), *a) == -1
+    a = args()
+    a[0] = ctypes.c_void_p((1 << 20) + 4)
+    assert L.gdn_tree_attention_static(ctypes.byref(d), *a) == -7
+    # a split whose partial records exceed 64 MiB: 2048 records of 33,280 bytes
+    d = G.make_attn_dims(256, 32, 8, 512, 4096, 4, 1024, split=256)
+    assert G.attention_workspace_bytes(d) > G.STATIC_SCRATCH_BYTES
+    assert L.gdn_tree_attention_static(ctypes.byref(d), *args()) == -10
+    assert "static scratch" in G.strerror(-10)
