@@ -598,36 +598,44 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
     lds_barrier();   // R rows and every coefficient visible; from here each wave works alone
 
     // ---- forward substitution over depth levels, this wave's 32 columns ----
-    // Lane (k, p) = (lane >> 4, lane & 15) takes node k of each group of four
-    // nodes of the level and the column pair c = 32w + 2p.  U rows go to HBM
-    // as soon as their level is done.  usum is a running sum of the lane's
+    // Lane (k, p) = (lane >> 3, lane & 7) takes node k of each group of eight
+    // nodes of the level and the column quad 32w + 4p.  U rows go to HBM as
+    // soon as their level is done.  usum is a running sum of the lane's
     // pseudo-values: it is non-finite when one of them is (or, harmlessly, when
     // the sum overflows), which sends the wave to the output product that keeps
     // non-finite values inside their subtree.
     float usum = 0.f;
     {
-        const int kk = lane >> 4;   // == grp
+        const int kk = lane >> 3, c4 = 32 * w + 4 * (lane & 7);
         const int maxdep = sm.maxdep;
         const size_t ustride = (size_t)a.Hv * D;
-        float *Ubase = a.U + ((size_t)lo * a.Hv + h) * D + c;
+        float *Ubase = a.U + ((size_t)lo * a.Hv + h) * D + c4;
         for (int L = 1; L <= maxdep; ++L) {
             const int s0 = sm.lvl_start[L], cnt = sm.lvl_start[L + 1] - s0;
-            for (int g0 = 0; g0 < cnt; g0 += 4) {
+            for (int g0 = 0; g0 < cnt; g0 += 8) {
                 if (g0 + kk < cnt) {
                     const int t = sm.lvl_nodes[s0 + g0 + kk];
-                    float2 acc2 = *reinterpret_cast<const float2 *>(&sm.ru[t][c]);
+                    // ru rows are 8-byte aligned (two floats of padding): float2 pairs
+                    float2 a0 = *reinterpret_cast<const float2 *>(&sm.ru[t][c4]);
+                    float2 a1 = *reinterpret_cast<const float2 *>(&sm.ru[t][c4 + 2]);
                     uint64_t m = sm.anc[t] & ~(1ull << t);   // the L-1 strict ancestors, root first
                     for (int q = 0; q < L - 1; ++q) {
                         const int j = __builtin_ctzll(m);
                         m &= m - 1;
                         const float aj = sm.T[t][q];
-                        const float2 uj = *reinterpret_cast<const float2 *>(&sm.ru[j][c]);
-                        acc2.x = fmaf(-aj, uj.x, acc2.x);
-                        acc2.y = fmaf(-aj, uj.y, acc2.y);
+                        const float2 u0 = *reinterpret_cast<const float2 *>(&sm.ru[j][c4]);
+                        const float2 u1 = *reinterpret_cast<const float2 *>(&sm.ru[j][c4 + 2]);
+                        a0.x = fmaf(-aj, u0.x, a0.x);
+                        a0.y = fmaf(-aj, u0.y, a0.y);
+                        a1.x = fmaf(-aj, u1.x, a1.x);
+                        a1.y = fmaf(-aj, u1.y, a1.y);
                     }
-                    if (L > 1) *reinterpret_cast<float2 *>(&sm.ru[t][c]) = acc2;
-                    st_stream2(Ubase + (size_t)t * ustride, acc2);
-                    usum += acc2.x + acc2.y;
+                    if (L > 1) {
+                        *reinterpret_cast<float2 *>(&sm.ru[t][c4]) = a0;
+                        *reinterpret_cast<float2 *>(&sm.ru[t][c4 + 2]) = a1;
+                    }
+                    st_stream4(reinterpret_cast<float4 *>(Ubase + (size_t)t * ustride), make_float4(a0.x, a0.y, a1.x, a1.y));
+                    usum += (a0.x + a0.y) + (a1.x + a1.y);
                 }
             }
             __builtin_amdgcn_wave_barrier();
