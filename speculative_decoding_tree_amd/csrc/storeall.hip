@@ -21,9 +21,11 @@ constexpr int NT = 256;
 // rows rg + 8 i (i = 0..15) in registers.  The column sums (S_p k)_c and
 // (S_p q)_c are reduced over the eight row groups by shuffles; the output is
 // o = S_t q = alpha (S_p q) + u (k.q).  Each node's state is written with
-// 16-byte stores (eight lanes cover one 128-byte row segment), plain stores
-// so that a sibling's reload of its parent state finds it in cache.  A lane
-// re-reads only states it wrote itself, so program order makes them visible.
+// 16-byte plain stores (eight lanes cover one 128-byte row segment).  The
+// registers hold one state at a time, so a node whose parent's state is not
+// the one held reads it back from memory; the visiting order keeps that rare
+// (see the walk below).  A lane re-reads only states it wrote itself, so
+// program order makes them visible.
 // Rows of bf16 (256 bytes) into LDS by direct global-to-LDS loads: one wave
 // instruction moves four rows (lane l: row 4 j + l / 16, 16-byte chunk l % 16,
 // written at base + 16 l).  Rows past n read row n - 1 (their LDS rows are
@@ -43,8 +45,9 @@ __global__ __launch_bounds__(NT) void verify_storeall_kernel(Args a) {
     __shared__ __attribute__((aligned(16))) uint16_t sQ[NM][D];
     __shared__ __attribute__((aligned(16))) uint16_t sV[NM][D];
     __shared__ float sG[NM], sB[NM];
-    __shared__ int s_order[NM];   // the visiting order: depth-first, children in index order
+    __shared__ int s_order[NM];   // the visiting order: depth-first, leaf children first
     __shared__ int s_par[NM];
+    __shared__ uint64_t s_leaf;   // nodes without children
     __shared__ int s_bad;
 
     const int n_units = a.B * a.Hv;
@@ -96,21 +99,26 @@ __global__ __launch_bounds__(NT) void verify_storeall_kernel(Args a) {
         else if (w == 2) sB[lane] = gb;
     }
     if (st == GDN_TREE_S_OK && N > 0 && w == 0) {
-        // parent check, then the depth-first visiting order (one walk on
-        // children masks held one per lane); a reload of a parent's state is
-        // then needed only where the walk backs up
+        // parent check, then the visiting order (one walk on children masks
+        // held one per lane): depth-first, and among the children of a node
+        // the leaves first.  A leaf's state is formed from its parent's state
+        // without replacing it in registers, so the parent's state is read
+        // back only before its second and later children that have children
+        // of their own.
         const bool live = lane < N;
         const int p = live ? p_mine : -1;
         const bool bad = __ballot(live && (p < -1 || p >= lane)) != 0ull;
+        uint64_t leaf = 0;
         if (!bad && slot >= 0) {
             uint64_t kids = 0;
             for (int q = 0; q < N; ++q) {
                 const uint64_t m = __ballot(live && p == q);
                 if (lane == q) kids = m;
             }
+            leaf = __ballot(live && kids == 0ull);
             const uint64_t roots = __ballot(live && p == -1);
             uint64_t done = 0;
-            int cur = -1;
+            int cur = -1;   // the node whose children are being visited (-1: the roots)
             for (int k = 0; k < N; ++k) {
                 uint64_t avail;
                 for (;;) {
@@ -120,14 +128,18 @@ __global__ __launch_bounds__(NT) void verify_storeall_kernel(Args a) {
                     if (avail || cur < 0) break;
                     cur = __builtin_amdgcn_readlane(p, cur);
                 }
-                const int nxt = __builtin_ctzll(avail);
+                const uint64_t leaves = avail & leaf;
+                const int nxt = __builtin_ctzll(leaves ? leaves : avail);
                 done |= 1ull << nxt;
                 if (lane == 0) s_order[k] = nxt;
-                cur = nxt;
+                if (!((leaf >> nxt) & 1ull)) cur = nxt;   // descend; after a leaf the same node's children go on
             }
         }
         if (lane < N) s_par[lane] = p;
-        if (lane == 0) s_bad = bad;
+        if (lane == 0) {
+            s_bad = bad;
+            s_leaf = leaf;
+        }
     }
     __syncthreads();
     if (st == GDN_TREE_S_OK && N > 0 && s_bad) st = GDN_TREE_S_BAD_PARENT;
@@ -145,6 +157,7 @@ __global__ __launch_bounds__(NT) void verify_storeall_kernel(Args a) {
     // (the vector-memory counter retires loads and stores in order, so such a
     // load waits for the stores before it).
     int held = -1;   // node whose state sits in hr (-1 = S0)
+    const uint64_t leaf = s_leaf;
     for (int k = 0; k < N; ++k) {
         const int t = s_order[k];
         const int p = s_par[t];
@@ -193,13 +206,17 @@ __global__ __launch_bounds__(NT) void verify_storeall_kernel(Args a) {
                 make_float4(fmaf(alpha, sq.x, u.x * kq), fmaf(alpha, sq.y, u.y * kq), fmaf(alpha, sq.z, u.z * kq),
                             fmaf(alpha, sq.w, u.w * kq));
         float *dst = a.node_state + gi * state_elems;
+        // a leaf's state is written and the parent's stays in hr; any other
+        // node's state replaces it
+        const bool descend = !((leaf >> t) & 1ull);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            hr[i] = make_float4(fmaf(alpha, hr[i].x, kr[i] * u.x), fmaf(alpha, hr[i].y, kr[i] * u.y),
-                                fmaf(alpha, hr[i].z, kr[i] * u.z), fmaf(alpha, hr[i].w, kr[i] * u.w));
-            *reinterpret_cast<float4 *>(dst + (rg + 8 * i) * D + c) = hr[i];
+            const float4 s = make_float4(fmaf(alpha, hr[i].x, kr[i] * u.x), fmaf(alpha, hr[i].y, kr[i] * u.y),
+                                         fmaf(alpha, hr[i].z, kr[i] * u.z), fmaf(alpha, hr[i].w, kr[i] * u.w));
+            *reinterpret_cast<float4 *>(dst + (rg + 8 * i) * D + c) = s;
+            if (descend) hr[i] = s;
         }
-        held = t;
+        if (descend) held = t;
     }
 }
 
