@@ -61,7 +61,9 @@ constexpr int PCHUNK = 16;   // accepted-path rows staged per pass (commit_verif
 //                             lower triangle; read by the solve)
 //   T[j][t], j <= t         : P_tj = D_tj (q_t.k_j) for ancestors j, 0 otherwise
 //                             (upper triangle, node-indexed: the A operand of the
-//                             output product (P masked) U)
+//                             output product (P masked) U), stored as its bf16 hi
+//                             and lo parts (hi in the low half of the word), split
+//                             once here rather than in every wave that reads it
 template <int NM, bool FUSED>
 struct VerifySmem {
     // Rows padded by two floats: rows eight apart (the four lane groups of an
@@ -533,8 +535,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = r0 + i;
-                        if (jcol < N && jcol <= r)
-                            sm.T[jcol][r] = ((sm.anc[r] >> jcol) & 1ull) ? exp2_fast(g2[i] - G2_j) * gq[i] : 0.f;
+                        if (jcol < N && jcol <= r) {   // stored split: bf16 hi in the low half, lo in the high half
+                            const float pv = ((sm.anc[r] >> jcol) & 1ull) ? exp2_fast(g2[i] - G2_j) * gq[i] : 0.f;
+                            uint32_t ph, pl;
+                            split_bf16x2(pv, 0.f, ph, pl);
+                            sm.T[jcol][r] = __uint_as_float((ph & 0xffffu) | (pl << 16));
+                        }
                     }
                 }
             }
@@ -710,13 +716,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NM <= 32 ? 4
                         for (int pr = 0; pr < 4; ++pr) {
                             const int j0 = 32 * ks + 8 * grp + 2 * pr;
                             const int jr = j0 < NM ? j0 : 0;
-                            float p0 = sm.T[jr][t], p1 = sm.T[jr + 1][t];
-                            if (j0 > t || j0 >= N) p0 = 0.f;
-                            if (j0 + 1 > t || j0 + 1 >= N) p1 = 0.f;
-                            uint32_t hh, ll;
-                            split_bf16x2(p0, p1, hh, ll);
-                            pah[pr] = hh;
-                            pal[pr] = ll;
+                            // entries are stored split (hi | lo << 16); j > t holds A, j >= N nothing
+                            uint32_t w0 = __float_as_uint(sm.T[jr][t]), w1 = __float_as_uint(sm.T[jr + 1][t]);
+                            if (j0 > t || j0 >= N) w0 = 0u;
+                            if (j0 + 1 > t || j0 + 1 >= N) w1 = 0u;
+                            pah[pr] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);   // hi(j0) | hi(j0 + 1) << 16
+                            pal[pr] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);   // lo(j0) | lo(j0 + 1) << 16
                         }
 #pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
