@@ -734,14 +734,15 @@ def main():
     if not args.no_configs:
         result["configs"] = config_rows(args, stream)
 
-    # the same GPU's device-copy rate (1 GiB read + 1 GiB written per copy), the practical
-    # ceiling of a kernel that reads each state once and writes it once
+    # the same GPU's runtime device-to-device copy (1 GiB read + 1 GiB written), for
+    # context beside a kernel that reads each state once and writes it once
     ca = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     cb = torch.empty_like(ca)
     t_copy = _time_launches(lambda i: cb.copy_(ca), 10, stream)
     copy_gbps = 2 * ca.numel() * 4 / (t_copy * 1e-6) / 1e9
-    result["copy_ceiling"] = {"GBps": copy_gbps, "frac": copy_gbps / HBM_PEAK_GBS, "bytes": 2 * ca.numel() * 4,
-                              "avg_us": t_copy}
+    result["device_copy"] = {"what": "runtime device-to-device copy (hipMemcpyAsync), 1 GiB each way",
+                             "GBps": copy_gbps, "frac": copy_gbps / HBM_PEAK_GBS, "bytes": 2 * ca.numel() * 4,
+                             "avg_us": t_copy}
     del ca, cb
     torch.cuda.empty_cache()
 
