@@ -291,3 +291,51 @@ def test_commit_verify_non_finite_sibling_stays_in_subtree(kind):
         assert np.array_equal(clean[key][outside].view(np.uint32), bad[key][outside].view(np.uint32)), key
         inside = bad[key][sub_rows]
         assert not np.isfinite(inside).all()
+
+
+def test_decoding_loop_of_four_steps_in_place():
+    """A decoding loop as a server runs it: the first step verifies a tree from the committed
+    states; each later step commits the previous tree's accepted node and verifies the next tree
+    in one launch, the states updated in place in permuted slots; the last tree's accepted node
+    is committed alone.  Every step's outputs and the final states against the oracle walking
+    the same steps in fp64 (its own states carried from step to step)."""
+    steps = [W.make_mixed_b256(seed=20 + s, per_kind=2, Hv=4, Hk=2) for s in range(4)]
+    B, Hv, Hk = steps[0].B, steps[0].Hv, steps[0].Hk
+    slots = np.arange(B, dtype=np.int32)[::-1].copy()
+    d = [upload(wl) for wl in steps]
+    dev = d[0]["S0"].device
+    ss = torch.from_numpy(slots).to(dev)
+    mn = [max(1, wl.max_nodes) for wl in steps]
+    S = d[0]["S0"].clone()
+    outs = []
+    out, U, _, st = G.verify(S, d[0]["q"], d[0]["k"], d[0]["v"], d[0]["g"], d[0]["beta"], d[0]["node_offset"],
+                             d[0]["parent"], max_nodes=mn[0], state_slot=ss)
+    assert (host(st) == 0).all()
+    outs.append(host(out))
+    for s in range(1, 4):
+        prev = dict(U=U, k=d[s - 1]["k"], g=d[s - 1]["g"], node_offset=d[s - 1]["node_offset"],
+                    parent=d[s - 1]["parent"], max_nodes=mn[s - 1])
+        _, out, U, _, st, cst = G.commit_verify(S, prev, d[s - 1]["accept_node"], d[s]["q"], d[s]["k"], d[s]["v"],
+                                                d[s]["g"], d[s]["beta"], d[s]["node_offset"], d[s]["parent"],
+                                                max_nodes=mn[s], S_out=S, state_slot=ss)
+        assert (host(st) == 0).all() and (host(cst) == 0).all()
+        outs.append(host(out))
+    _, _, _, cst = G.commit_node(S, U, d[3]["k"], d[3]["g"], d[3]["node_offset"], d[3]["parent"],
+                                 d[3]["accept_node"], max_nodes=mn[3], S_out=S, state_slot=ss)
+    assert (host(cst) == 0).all()
+    S_gpu = host(S)
+
+    S_ref = steps[0].S0.astype(np.float64)
+    for s, wl in enumerate(steps):
+        Oo, _, _, sto = O.verify_batch(S_ref, wl.q64(), wl.k64(), wl.v64(), wl.g, wl.beta, wl.node_offset,
+                                       wl.parent, Hv, Hk, max_nodes=mn[s], state_slot=slots)
+        assert (sto == 0).all()
+        e = rowwise_rel_err(outs[s], Oo)
+        assert e <= TOL and e <= ENVELOPE, (s, e)
+        path, plen, pst = O.accepted_path_batch(wl.node_offset, wl.parent, wl.accept_node, max_nodes=mn[s])
+        assert (pst == 0).all()
+        S_ref, cso = O.commit_batch(S_ref, wl.q64(), wl.k64(), wl.v64(), wl.g, wl.beta, wl.node_offset, wl.parent,
+                                    path, plen, Hv, Hk, max_nodes=mn[s], state_slot=slots)
+        assert (cso == 0).all()
+    es = matwise_rel_err(S_gpu, S_ref)
+    assert es <= TOL and es <= ENVELOPE, es
