@@ -359,6 +359,29 @@ def attention_row(args, stream):
         if split is None:
             res[key]["hbm_traffic_bytes"] = measured_traffic("mixed_b256", "gdn_tree_attention")
     assert (st.cpu().numpy() == 0).all()
+
+    # batch one: the six-node root-branch tree over a 4096-token context, where one pass has
+    # only Hkv workgroups of work and splitting the context spreads it over more
+    w1 = W.make_attn([W.root_branch()], [4096], Hq=wl.Hq, Hkv=wl.Hkv, seed=3, name="attn_b1")
+    q1, kc1, vc1, kn1, vn1 = bf(w1.q), bf(w1.k_ctx), bf(w1.v_ctx), bf(w1.k_node), bf(w1.v_node)
+    co1, no1, par1 = i32(w1.ctx_offset), i32(w1.node_offset), i32(w1.parent)
+    anc1 = torch.empty((w1.T,), dtype=torch.int64, device=dev)
+    st1 = torch.empty((1,), dtype=torch.int32, device=dev)
+    G.ancestry(no1, par1, max_nodes=w1.max_nodes, anc_mask=anc1, status=st1, stream=stream)
+    out1 = torch.empty((w1.T, w1.Hq, D), dtype=torch.float32, device=dev)
+    lse1 = torch.empty((w1.T, w1.Hq), dtype=torch.float32, device=dev)
+    b1 = {"workload": "1 request, 6-node root-branch tree, 4096-token context, Hq=32, Hkv=8, d=128"}
+    for split in (None, 1024, 256):
+        ws_need = G.attention_workspace_bytes(G.make_attn_dims(1, w1.Hq, w1.Hkv, w1.T, w1.C, w1.max_nodes, w1.C,
+                                                                split))
+        ws = torch.empty((max(ws_need, 16),), dtype=torch.uint8, device=dev)
+
+        def run1(i, split=split, ws=ws):
+            G.attention(q1, kc1, vc1, co1, kn1, vn1, no1, anc1, w1.scale, max_nodes=w1.max_nodes, max_ctx=w1.C,
+                        split=split, out=out1, lse=lse1, workspace=ws, status=st1, stream=stream)
+        b1["one_pass_us" if split is None else f"split_{split}_us"] = _time_launches(run1, n, stream)
+    assert (st1.cpu().numpy() == 0).all()
+    res["batch_one"] = b1
     return res
 
 
