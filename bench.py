@@ -536,6 +536,8 @@ def main():
     ap.add_argument("--no-attention", action="store_true", help="skip the tree-bias attention measurement")
     ap.add_argument("--no-batch-one", action="store_true", help="skip the batch-one latency measurement")
     ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' rows")
+    ap.add_argument("--batch-one-only", action="store_true",
+                    help="only the batch-one latency rows (one JSON line), e.g. under a kernel trace")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
@@ -556,6 +558,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    if args.batch_one_only:
+        print(json.dumps({"batch_one": batch_one_row(args, torch.cuda.current_stream())}), flush=True)
+        return
 
     t0 = time.time()
     wl = W.make_mixed_b256() if args.workload == "mixed_b256" else W.make_random32_b256()
