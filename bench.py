@@ -457,7 +457,9 @@ def config_rows(args, stream):
     the one-launch step (gdn_tree_commit_verify, the batch playing both trees, out
     of place) and the two-launch step (gdn_tree_verify + gdn_tree_commit_node),
     each with nodes/s, commits/s and its fraction of the HBM peak.  Three copies of
-    every buffer rotate, as in the headline loop."""
+    every buffer rotate, as in the headline loop.  Each step is timed launched from
+    Python and replayed from a HIP graph (graph_*: no per-launch host cost, which
+    decides the small batches' times)."""
     import numpy as np
     import torch
     import workloads as W
@@ -503,6 +505,40 @@ def config_rows(args, stream):
 
         t_two = _time_launches(two, n, stream)      # also leaves every pool's U for the one-launch step
         t_one = _time_launches(one, n, stream)
+
+        # the same steps replayed from a HIP graph (one step per pool per replay), which takes
+        # the Python binding's per-launch cost out of the timed interval
+        def graph_of(fn):
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                for i in range(len(pools)):
+                    fn(i, None)
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for i in range(len(pools)):
+                    fn(i, None)
+            return gr
+
+        def two_s(i, s):
+            p = pools[i % len(pools)]
+            G.verify(p["S0"], p["q"], p["k"], p["v"], p["g"], p["beta"], p["off"], p["par"], max_nodes=mn,
+                     out=p["out"], U=p["U"], anc_mask=p["anc"], status=p["st"], stream=s)
+            G.commit_node(p["S0"], p["U"], p["k"], p["g"], p["off"], p["par"], p["acc"], max_nodes=mn,
+                          S_out=p["S_out"], path=p["path"], path_len=p["plen"], status=p["cst"], stream=s)
+
+        def one_s(i, s):
+            p = pools[i % len(pools)]
+            prev = dict(U=p["U"], k=p["k"], g=p["g"], node_offset=p["off"], parent=p["par"], max_nodes=mn)
+            G.commit_verify(p["S0"], prev, p["acc"], p["q"], p["k"], p["v"], p["g"], p["beta"], p["off"], p["par"],
+                            max_nodes=mn, S_out=p["S_out"], out=p["out2"], U=p["U2"], anc_mask=p["anc"],
+                            status=p["st"], commit_status=p["cst"], path=p["path"], path_len=p["plen"], stream=s)
+        g_two, g_one = graph_of(two_s), graph_of(one_s)
+        t_two_g = _time_launches(lambda i: g_two.replay(), n, stream) / len(pools)
+        t_one_g = _time_launches(lambda i: g_one.replay(), n, stream) / len(pools)
+        del g_two, g_one
         st = np.concatenate([p["st"].cpu().numpy() for p in pools] + [p["cst"].cpu().numpy() for p in pools])
         if not (st == 0).all():
             raise RuntimeError(f"{name}: device status nonzero")
@@ -513,10 +549,14 @@ def config_rows(args, stream):
             "B": wl.B, "Hv": wl.Hv, "Hk": wl.Hk, "T": wl.T, "max_nodes": mn, "mean_accepted_len": float(L.mean()),
             "one_launch": {"avg_us": t_one, "nodes_per_s": wl.T / (t_one * 1e-6), "commits_per_s": wl.B / (t_one * 1e-6),
                            "alg_bytes": fb, "alg_GBps": fb / (t_one * 1e-6) / 1e9,
-                           "hbm_frac": fb / (t_one * 1e-6) / 1e9 / HBM_PEAK_GBS},
+                           "hbm_frac": fb / (t_one * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                           "graph_avg_us": t_one_g, "graph_nodes_per_s": wl.T / (t_one_g * 1e-6),
+                           "graph_hbm_frac": fb / (t_one_g * 1e-6) / 1e9 / HBM_PEAK_GBS},
             "two_launch": {"avg_us": t_two, "nodes_per_s": wl.T / (t_two * 1e-6), "commits_per_s": wl.B / (t_two * 1e-6),
                            "alg_bytes": vb + cb, "alg_GBps": (vb + cb) / (t_two * 1e-6) / 1e9,
-                           "hbm_frac": (vb + cb) / (t_two * 1e-6) / 1e9 / HBM_PEAK_GBS}}
+                           "hbm_frac": (vb + cb) / (t_two * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                           "graph_avg_us": t_two_g, "graph_nodes_per_s": wl.T / (t_two_g * 1e-6),
+                           "graph_hbm_frac": (vb + cb) / (t_two_g * 1e-6) / 1e9 / HBM_PEAK_GBS}}
         del pools
         torch.cuda.empty_cache()
     return rows
