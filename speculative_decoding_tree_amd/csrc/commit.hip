@@ -46,26 +46,38 @@ __device__ __forceinline__ uint64_t greedy_walk(const Args &a, int b, int lo, in
 
 constexpr int NT = 256;
 constexpr int KCHUNK = 16;   // path rows staged per pass
+// Workgroups per (request, head): each takes D / CQS consecutive state rows
+// (16 KiB), since the rank-L update is separable by row (row i of H' needs row
+// i of H0 and element i of each path k).  More, smaller workgroups keep more
+// of the stream in flight per CU than one 64 KiB workgroup per unit (mixed
+// batch-256: 279-280 -> 269.5-270 us, bit-identical; two per unit 270.5-271).
+constexpr int CQS = 4;
 
 // Where the accepted path comes from: the caller (a root-first path), the
 // greedy walk over token ids, or the accepted node (its root-first ancestors).
 enum PathSource { PATH_GIVEN = 0, PATH_GREEDY = 1, PATH_FROM_NODE = 2 };
 
-// The unit's 64 KiB of H0 is requested first (it depends only on the slot);
-// wave 0 then validates parents and the path with ballots (or derives the
-// path), and turns the path gates into decay coefficients with a suffix scan
-// over shuffles, while those loads are in flight.
-template <int SRC>
+// The workgroup's share of H0 (rows rbase .. rbase + QR - 1 of the unit's
+// state) is requested first (it depends only on the slot); wave 0 then
+// validates parents and the path with ballots (or derives the path: every
+// share's workgroup does, one publishes it), and turns the path gates into
+// decay coefficients with a suffix scan over shuffles, while those loads are
+// in flight.
+template <int SRC, int QS>
 __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
-    __shared__ float s_k[KCHUNK][D];   // D_aj * k_j rows of the current chunk
+    constexpr int QR = D / QS;         // state rows of this workgroup's share
+    constexpr int RI = QR / 8;         // rows per thread
+    __shared__ float s_k[KCHUNK][QR];  // D_aj * k_j (this share's elements) of the current chunk
     __shared__ float s_coef[MAXN];
     __shared__ int s_path[MAXN];
     __shared__ int s_st, s_L;
     __shared__ float s_gam;
 
-    const int n_units = a.B * a.Hv;
-    const int unit = xcd_unit(blockIdx.x, n_units);
-    if (unit >= n_units) return;
+    const int n_sub = a.B * a.Hv * QS;
+    const int sub = xcd_unit(blockIdx.x, n_sub);
+    if (sub >= n_sub) return;
+    const int unit = sub / QS, q = sub - unit * QS;
+    const int rbase = q * QR;
     const int b = unit / a.Hv;
     const int h = unit - b * a.Hv;
     const int hk = h / (a.Hv / a.Hk);
@@ -76,11 +88,11 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
     const size_t base = ((size_t)(slot < 0 ? 0 : slot) * a.Hv + h) * D * D;
     const float4 *src = reinterpret_cast<const float4 *>(a.S0 + base);
     float4 *dst = reinterpret_cast<float4 *>(a.S_out + base);
-    const int c4 = tid & 31, r0 = tid >> 5;   // rows r0 + 8 i, columns 4 c4 .. 4 c4 + 3
-    float4 acc[16];
+    const int c4 = tid & 31, r0 = rbase + (tid >> 5);   // rows r0 + 8 i, columns 4 c4 .. 4 c4 + 3
+    float4 acc[RI];
     if (slot >= 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = ld_stream4(src + (r0 + 8 * i) * 32 + c4);
+        for (int i = 0; i < RI; ++i) acc[i] = ld_stream4(src + (r0 + 8 * i) * 32 + c4);
     }
 
     if (tid < 64) {
@@ -109,7 +121,7 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
                 pj = path_entry(pm, lane);
                 have_path = true;
             }
-            if (h == 0) {   // one head publishes the decision
+            if (h == 0 && q == 0) {   // one head publishes the decision
                 if (SRC == PATH_GREEDY && a.accept_out && lane == 0) a.accept_out[b] = accept;
                 if (a.path_out) {
                     int32_t *row = a.path_out + (size_t)b * a.max_nodes;
@@ -146,7 +158,7 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
         if (lane == 0) {
             s_st = st;
             s_L = L;
-            if (h == 0 && a.status) a.status[b] = st;
+            if (h == 0 && q == 0 && a.status) a.status[b] = st;
         }
     }
     __syncthreads();
@@ -156,31 +168,31 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
     if (st != GDN_TREE_S_OK || L == 0) {   // S_out = S0, bit-exact
         if (a.S_out != a.S0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) st_stream4(dst + (r0 + 8 * i) * 32 + c4, acc[i]);
+            for (int i = 0; i < RI; ++i) st_stream4(dst + (r0 + 8 * i) * 32 + c4, acc[i]);
         }
         return;
     }
 
     const float gam = s_gam;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = make_float4(gam * acc[i].x, gam * acc[i].y, gam * acc[i].z, gam * acc[i].w);
+    for (int i = 0; i < RI; ++i) acc[i] = make_float4(gam * acc[i].x, gam * acc[i].y, gam * acc[i].z, gam * acc[i].w);
     int lo, N;
     check_offsets(a, b, lo, N);
     for (int j0 = 0; j0 < L; j0 += KCHUNK) {
         const int nj = min(KCHUNK, L - j0);
         if (j0 > 0) __syncthreads();
-        for (int idx = tid; idx < nj * D; idx += NT) {
-            const int jj = idx >> 7, c = idx & (D - 1);
+        for (int idx = tid; idx < nj * QR; idx += NT) {
+            const int jj = idx / QR, c = idx - jj * QR;
             const int t = s_path[j0 + jj];
-            s_k[jj][c] = s_coef[j0 + jj] * bf16_to_f32(a.k[((size_t)(lo + t) * a.Hk + hk) * D + c]);
+            s_k[jj][c] = s_coef[j0 + jj] * bf16_to_f32(a.k[((size_t)(lo + t) * a.Hk + hk) * D + rbase + c]);
         }
         __syncthreads();
         for (int jj = 0; jj < nj; ++jj) {
             const int t = s_path[j0 + jj];
             const float4 u = reinterpret_cast<const float4 *>(a.U + ((size_t)(lo + t) * a.Hv + h) * D)[c4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float kc = s_k[jj][r0 + 8 * i];
+            for (int i = 0; i < RI; ++i) {
+                const float kc = s_k[jj][r0 - rbase + 8 * i];
                 acc[i].x = fmaf(kc, u.x, acc[i].x);
                 acc[i].y = fmaf(kc, u.y, acc[i].y);
                 acc[i].z = fmaf(kc, u.z, acc[i].z);
@@ -189,7 +201,7 @@ __global__ __launch_bounds__(NT) void commit_kernel(Args a) {
         }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) st_stream4(dst + (r0 + 8 * i) * 32 + c4, acc[i]);
+    for (int i = 0; i < RI; ++i) st_stream4(dst + (r0 + 8 * i) * 32 + c4, acc[i]);
 }
 
 // One wave per request, lane t = node t: parents are validated with a ballot,
@@ -372,17 +384,17 @@ __global__ __launch_bounds__(NT) void replay_kernel(Args a) {
 }  // namespace
 
 hipError_t launch_commit_node(const Args &a, hipStream_t stream) {
-    commit_kernel<PATH_FROM_NODE><<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
+    commit_kernel<PATH_FROM_NODE, CQS><<<dim3(xcd_grid(a.B * a.Hv * CQS)), dim3(NT), 0, stream>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_commit(const Args &a, hipStream_t stream) {
-    commit_kernel<PATH_GIVEN><<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
+    commit_kernel<PATH_GIVEN, CQS><<<dim3(xcd_grid(a.B * a.Hv * CQS)), dim3(NT), 0, stream>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_accept_commit(const Args &a, hipStream_t stream) {
-    commit_kernel<PATH_GREEDY><<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
+    commit_kernel<PATH_GREEDY, CQS><<<dim3(xcd_grid(a.B * a.Hv * CQS)), dim3(NT), 0, stream>>>(a);
     return hipGetLastError();
 }
 
