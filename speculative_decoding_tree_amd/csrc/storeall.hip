@@ -220,11 +220,17 @@ __global__ __launch_bounds__(NT) void verify_storeall_kernel(Args a) {
     }
 }
 
+// A plain copy of the accepted node's state, four workgroups per (request,
+// head), each copying 16 KiB (more, smaller workgroups keep more of the
+// stream in flight per CU than one 64 KiB workgroup).
+constexpr int CQS = 4;
+
 __global__ __launch_bounds__(NT) void commit_storeall_kernel(Args a) {
     __shared__ int s_bad;
-    const int n_units = a.B * a.Hv;
-    const int unit = xcd_unit(blockIdx.x, n_units);
-    if (unit >= n_units) return;
+    const int n_sub = a.B * a.Hv * CQS;
+    const int sub = xcd_unit(blockIdx.x, n_sub);
+    if (sub >= n_sub) return;
+    const int unit = sub / CQS, q = sub - unit * CQS;
     const int b = unit / a.Hv;
     const int h = unit - b * a.Hv;
     const int tid = threadIdx.x;
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(NT) void commit_storeall_kernel(Args a) {
     if (st == GDN_TREE_S_OK && slot < 0) st = GDN_TREE_S_BAD_SLOT;
     const int acc = a.accept_node[b];
     if (st == GDN_TREE_S_OK && (acc < -1 || acc >= N)) st = GDN_TREE_S_BAD_ACCEPT;
-    if (h == 0 && tid == 0 && a.status) a.status[b] = st;
+    if (h == 0 && q == 0 && tid == 0 && a.status) a.status[b] = st;
     if (slot < 0) return;
     const size_t state_elems = (size_t)D * D;
     const float *src = (st == GDN_TREE_S_OK && acc >= 0)
@@ -253,10 +259,10 @@ __global__ __launch_bounds__(NT) void commit_storeall_kernel(Args a) {
                            : a.S0 + ((size_t)slot * a.Hv + h) * state_elems;
     float *dst = a.S_out + ((size_t)slot * a.Hv + h) * state_elems;
     if (src == dst) return;
-    const float4 *s4 = reinterpret_cast<const float4 *>(src);
-    float4 *d4 = reinterpret_cast<float4 *>(dst);
+    const float4 *s4 = reinterpret_cast<const float4 *>(src) + q * (D * D / 4 / CQS);
+    float4 *d4 = reinterpret_cast<float4 *>(dst) + q * (D * D / 4 / CQS);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) d4[i * NT + tid] = s4[i * NT + tid];
+    for (int i = 0; i < D * D / 4 / CQS / NT; ++i) d4[i * NT + tid] = s4[i * NT + tid];
 }
 
 }  // namespace
@@ -273,7 +279,7 @@ hipError_t launch_verify_storeall(const Args &a, hipStream_t stream) {
 }
 
 hipError_t launch_commit_storeall(const Args &a, hipStream_t stream) {
-    commit_storeall_kernel<<<dim3(xcd_grid(a.B * a.Hv)), dim3(NT), 0, stream>>>(a);
+    commit_storeall_kernel<<<dim3(xcd_grid(a.B * a.Hv * CQS)), dim3(NT), 0, stream>>>(a);
     return hipGetLastError();
 }
 
