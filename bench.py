@@ -26,7 +26,11 @@ launch: for the headline step inside the timed region itself (one event per
 step boundary), for the two-launch step in a second pass over the same steps.
 The snapshot-per-node (storeall) pair is timed
 after the main loop for comparison, and the fp64 oracle is timed on a bounded
-sample on the host cores.
+sample on the host cores.  The rows beyond the core step (acceptance, replay,
+budget, tree attention, batch one) are under next_rows, and the other
+workloads (depth-3 chains at batch 64, root-branch trees at batch 16 and 1,
+random 32-node trees at batch 256) under configs, each launched from Python and
+replayed from a HIP graph.
 """
 from __future__ import annotations
 
