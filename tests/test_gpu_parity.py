@@ -539,7 +539,8 @@ def _check_nonfinite(wl_clean, wl_bad, clean, bad, sub_rows):
         assert np.array_equal(np.isfinite(got), np.isfinite(want)), key
         fin = np.isfinite(want)
         scale = np.abs(np.where(fin, want, 0)).max(axis=-1, keepdims=True)
-        err = np.abs(np.where(fin, got - want, 0)) / np.maximum(scale, 1e-30)
+        with np.errstate(invalid="ignore"):   # got - want is NaN where both are (those entries are masked)
+            err = np.abs(np.where(fin, got - want, 0)) / np.maximum(scale, 1e-30)
         assert err.max() <= TOL, (key, err.max())
 
 
@@ -567,6 +568,44 @@ def test_non_finite_sibling_stays_in_subtree(kind):
         path = O.accepted_path(wl.parents_of(b), int(wl.accept_node[b]))
         if j not in path:
             assert np.array_equal(clean["S1"][b].view(np.uint32), bad["S1"][b].view(np.uint32)), b
+
+
+@pytest.mark.parametrize("kind", ["nan_g", "inf_v"])
+def test_non_finite_stays_in_subtree_storeall_and_replay(kind):
+    """The snapshot-per-node verify and the replay commit walk the sequential rule, so a
+    non-finite input of one node reaches only its subtree there too: every other node's output
+    and state, and the replay commit of a path that avoids the node, keep their bits."""
+    perturbed = ((0, 3), (1, 4), (2, 1))
+    wl, wl2 = _nonfinite_workload(), _nonfinite_workload()
+    for b, j in perturbed:
+        _perturb(wl2, kind, b, j)
+    mn = _mn(wl)
+    res = {}
+    for tag, w in (("clean", wl), ("bad", wl2)):
+        d = upload(w)
+        out, NS, st = G.verify_storeall(d["S0"], d["q"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"],
+                                        d["parent"], max_nodes=mn)
+        path, plen, _ = G.accepted_path(d["node_offset"], d["parent"], d["accept_node"], max_nodes=mn)
+        S2, rst = G.commit_replay(d["S0"], d["k"], d["v"], d["g"], d["beta"], d["node_offset"], d["parent"],
+                                  path, plen, max_nodes=mn)
+        torch.cuda.synchronize()
+        res[tag] = dict(out=host(out), NS=host(NS), st=host(st), S2=host(S2), rst=host(rst))
+    assert (res["clean"]["st"] == 0).all() and (res["bad"]["st"] == 0).all() and (res["bad"]["rst"] == 0).all()
+    sub_rows = []
+    for b, j in perturbed:
+        lo = int(wl.node_offset[b])
+        anc = O.ancestry(wl.parents_of(b))
+        sub_rows += [lo + t for t in range(wl.nodes(b)) if (anc[t] >> j) & 1]
+    outside = np.setdiff1d(np.arange(wl.T), sub_rows)
+    for key in ("out", "NS"):
+        assert np.array_equal(res["clean"][key][outside].view(np.uint32), res["bad"][key][outside].view(np.uint32)), key
+        assert not np.isfinite(res["bad"][key][sub_rows]).all(), key
+    for b, j in perturbed:
+        path = O.accepted_path(wl.parents_of(b), int(wl.accept_node[b]))
+        if j not in path:
+            assert np.array_equal(res["clean"]["S2"][b].view(np.uint32), res["bad"]["S2"][b].view(np.uint32)), b
+        else:
+            assert not np.isfinite(res["bad"]["S2"][b]).all(), b
 
 
 def test_non_finite_pseudo_value_off_the_path_does_not_reach_the_commit():
