@@ -380,8 +380,10 @@ int gdn_tree_attention(const gdn_tree_attn_dims *dims, const uint16_t *q, const 
                        float scale, float *out, float *lse, void *workspace, size_t workspace_bytes,
                        int32_t *status, void *stream);
 
-/* Workspace bytes gdn_tree_attention needs for dims: 256 for one pass, more
- * when split < max_ctx; 0 when B = 0 or dims are invalid.  Host only. */
+/* Workspace bytes gdn_tree_attention needs for dims: 256 for one pass; for a
+ * split context 256 + B * Hkv * parts * row groups * rows * 130 * 4, where a
+ * row group holds rows = 128 query rows when max_nodes * Hq / Hkv > 64 and
+ * B * parts <= 1024, else 64; 0 when B = 0 or dims are invalid.  Host only. */
 size_t gdn_tree_attention_workspace_bytes(const gdn_tree_attn_dims *dims);
 
 /*
@@ -398,7 +400,10 @@ size_t gdn_tree_attention_workspace_bytes(const gdn_tree_attn_dims *dims);
  * call whose workspace need (gdn_tree_attention_workspace_bytes) exceeds the
  * array returns GDN_TREE_E_SCRATCH and enqueues nothing: one pass always
  * fits (256 bytes); a split context fits while B * Hkv * parts * row groups
- * <= 2016 (33,280 bytes per partial record).  Every call on one GPU shares
+ * partial records fit: 2016 records of 64 rows (33,280 bytes each), or 1008
+ * of 128 rows (66,560 bytes), the size taken when a request and kv head have
+ * more than 64 query rows (max_nodes * Hq / Hkv) and B * parts <= 1024.
+ * Every call on one GPU shares
  * that GPU's array: calls that overlap on one GPU (concurrent streams, or
  * graphs replayed concurrently) race and must be serialised by the caller.
  * The counters are cleared on the stream by each call; partial records are

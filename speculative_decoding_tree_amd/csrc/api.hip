@@ -51,12 +51,23 @@ bool any_misaligned(Ps... ps) {
     return (misaligned((const void *)ps) || ...);
 }
 
-// Query rows per attention workgroup.  64 (one 16-row tile per wave): with
-// the row groups of a request scheduled side by side on one XCD their shared
-// context reads meet in L2, and three such workgroups fit on a CU against two
-// of 128 rows (two tiles per wave); measured 811 -> 694 us on the batch-256
-// trees with 1k-4k contexts.
-int attn_rows_wg(const gdn_tree_attn_dims *) { return 64; }
+// Query rows per attention workgroup.  128 (two 16-row tiles per wave, two
+// workgroups per CU) when a request can have more than 64 query rows per kv
+// head and the scheduled launch takes the batch: a 64-node tree's rows then
+// need two workgroups instead of four, each K and V fragment read from LDS
+// serves 32 rows, and the context is read twice instead of four times (on
+// the batch-256 trees with 1k-4k contexts: the same time, 718-735 vs 719-725
+// us, and 3.08 instead of 3.70 GB fetched).  Otherwise 64 (one tile per wave,
+// three workgroups per CU; the waves of a one- or two-tile unit split the
+// keys instead).  Depends only on the dims, so the workspace size does too.
+int attn_rows_wg(const gdn_tree_attn_dims *d, int n_split) {
+    const long long G = d->Hq / d->Hkv;
+    const long long rows = (long long)d->max_nodes * G;
+    if (rows <= 64) return 64;
+    const long long n_rg = (rows + 127) / 128;
+    const bool sched = (long long)d->B * n_split <= gdn::ATTN_SCHED_ITEMS && n_rg < 256 && d->Hkv * n_rg < 4096;
+    return sched ? 128 : 64;
+}
 
 // Attention dims; also derives the launch shape.  Returns a GDN_TREE_* code.
 int check_attn_dims(const gdn_tree_attn_dims *d, int &n_split, int &n_rg) {
@@ -70,9 +81,9 @@ int check_attn_dims(const gdn_tree_attn_dims *d, int &n_split, int &n_rg) {
     if (d->max_nodes < 1 || d->max_nodes > GDN_TREE_MAX_NODES) return GDN_TREE_E_MAX_NODES;
     if (d->max_ctx < 0 || d->max_ctx > (1 << 30) || d->split < 1) return GDN_TREE_E_DIMS;
     const long long G = d->Hq / d->Hkv;
-    const int rows_wg = attn_rows_wg(d);
-    n_rg = (int)((d->max_nodes * G + rows_wg - 1) / rows_wg);
     n_split = d->max_ctx > d->split ? (int)(((long long)d->max_ctx + d->split - 1) / d->split) : 1;
+    const int rows_wg = attn_rows_wg(d, n_split);
+    n_rg = (int)((d->max_nodes * G + rows_wg - 1) / rows_wg);
     const long long units = (long long)d->B * d->Hkv * n_split * n_rg;
     if (units > (long long)INT_MAX - 8) return GDN_TREE_E_SIZE;
     const long long row = (long long)GDN_TREE_HEAD_DIM * 4;
@@ -85,8 +96,8 @@ int check_attn_dims(const gdn_tree_attn_dims *d, int &n_split, int &n_rg) {
 size_t attn_workspace(const gdn_tree_attn_dims *d, int n_split, int n_rg) {
     const size_t header = gdn::ATTN_WS_HEADER_BYTES;
     if (n_split <= 1) return header;
-    return header + (size_t)d->B * d->Hkv * n_split * n_rg * (size_t)attn_rows_wg(d) * (GDN_TREE_HEAD_DIM + 2) *
-                        sizeof(float);
+    return header + (size_t)d->B * d->Hkv * n_split * n_rg * (size_t)attn_rows_wg(d, n_split) *
+                        (GDN_TREE_HEAD_DIM + 2) * sizeof(float);
 }
 
 int finish(hipError_t e) { return e == hipSuccess ? GDN_TREE_OK : GDN_TREE_E_LAUNCH; }
@@ -488,7 +499,7 @@ int attention_args(gdn::AttnArgs &a, size_t &need, const gdn_tree_attn_dims *dim
     a.split = dims->split;
     a.n_split = n_split;
     a.n_rg = n_rg;
-    a.rows_wg = attn_rows_wg(dims);
+    a.rows_wg = attn_rows_wg(dims, n_split);
     a.scale_log2 = scale * 1.4426950408889634f;
     a.q = q;
     a.k_ctx = k_ctx;

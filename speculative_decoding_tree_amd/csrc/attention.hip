@@ -191,12 +191,16 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int 
     const int nctx = k1 > k0 ? (k1 - k0 + KB - 1) / KB : 0;
     const int nblk = nctx + (sp == 0 ? 1 : 0);   // the draft nodes' own block goes with the first part
     const int tiles = (min(R - row0, ROWS) + 15) >> 4;
-    if (TPW == 1 && tiles == 1)
-        attn_body<TPW, 4>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
-    else if (TPW == 1 && tiles == 2)
-        attn_body<TPW, 2>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
-    else
+    if constexpr (TPW == 1) {
+        if (tiles == 1)
+            attn_body<TPW, 4>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+        else if (tiles == 2)
+            attn_body<TPW, 2>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+        else
+            attn_body<TPW, 1>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+    } else {
         attn_body<TPW, 1>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+    }
 }
 
 template <int TPW, int KG>
@@ -240,6 +244,30 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
         }
     }
     const bool active = tact[0];
+    // Two tiles per wave leave no registers to spare: there the rows' ancestry
+    // masks and output indices are derived again where they are used (the
+    // draft nodes' block and the end) rather than held across the blocks.
+    auto row_index = [&](int tt, int &tr, int &gr) {
+        if constexpr (TPW == 1) {
+            tr = t[tt];
+            gr = g[tt];
+        } else {
+            int id = threadIdx.x;
+            asm volatile("" : "+v"(id));
+            const int r = row0 + 16 * (TPW * wr + tt) + (id & 15);
+            tr = rvalid[tt] ? r / G : 0;
+            gr = rvalid[tt] ? r - tr * G : 0;
+        }
+    };
+    auto ancestry = [&](int tt) -> uint64_t {
+        if constexpr (TPW == 1) {
+            return anc_row[tt];
+        } else {
+            int tr, gr;
+            row_index(tt, tr, gr);
+            return rvalid[tt] ? a.anc_mask[lo + tr] : 0ull;
+        }
+    };
 
     // ---- staging: 16 lanes per row and 16-byte chunk c = tid % 16, so each
     //      load instruction reads whole rows; thread tid moves rows 16q + tid / 16
@@ -356,7 +384,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) x[kt][i] = sc[tt][kt][i];
             if (nodeb || rem < KB) {   // the last context block and the nodes' block: hide keys row n may not see
-                const uint64_t vis = nodeb ? anc_row[tt] : ((1ull << rem) - 1ull);
+                const uint64_t vis = nodeb ? ancestry(tt) : ((1ull << rem) - 1ull);
                 // bit 16 kt + i: key 16 (kt_lo + kt) + 4 grp + i
                 const uint64_t vl = vis >> (4 * grp + 16 * kt_lo);
 #pragma unroll
@@ -512,7 +540,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
 #pragma unroll 1
             for (int x = 0; x < 32; ++x) {
                 const int col = 16 * (x >> 2) + 4 * grp + (x & 3);
-                for (uint64_t m = anc_row[tt]; m; m &= m - 1) {
+                for (uint64_t m = ancestry(tt); m; m &= m - 1) {
                     const int j = __builtin_ctzll(m);   // node row j was staged by thread 16 (j % 16) + col / 8
                     if ((vnf_all[16 * (j & 15) + (col >> 3)] >> (8 * (j >> 4) + (col & 7))) & 1u) pm |= 1u << x;
                 }
@@ -528,7 +556,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
     for (int tt = 0; tt < TPW; ++tt) {
         if (!rvalid[tt]) continue;
         if (a.n_split == 1) {
-            const size_t orow = (size_t)(lo + t[tt]) * a.Hq + hk * G + g[tt];
+            int tr, gr;
+            row_index(tt, tr, gr);
+            const size_t orow = (size_t)(lo + tr) * a.Hq + hk * G + gr;
             const float inv = 1.f / l[tt];
             float *op = a.out + orow * D + 4 * grp;
 #pragma unroll
@@ -582,7 +612,7 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3
 // free: the deal balances the sub-lists, the counter absorbs the workgroups'
 // differing speeds, and neighbouring positions (the row groups of one request
 // and kv-head) run on one XCD at the same time and share its L2.
-constexpr int SCHED_ITEMS = 1024;    // (request, context part) items the list can hold
+constexpr int SCHED_ITEMS = ATTN_SCHED_ITEMS;   // (request, context part) items the list can hold
 constexpr int SCHED_BUCKETS = 64;    // length classes of the counting sort
 
 struct AttnSched {
@@ -834,7 +864,7 @@ constexpr int MAX_DEVICES = 64;
 // Threads that race to fill an entry compute the same value; the atomics keep
 // those stores and loads well defined.
 std::atomic<int> g_cus[MAX_DEVICES];
-std::atomic<int> g_occupancy[MAX_DEVICES];
+std::atomic<int> g_occupancy[MAX_DEVICES], g_occupancy2[MAX_DEVICES];
 
 int cached_fact(std::atomic<int> *table, int dev, int (*query)(int)) {
     if (dev < 0 || dev >= MAX_DEVICES) return query(dev);
@@ -851,17 +881,20 @@ int query_cus(int dev) {
     return hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? cus : 0;
 }
 
+template <int TPW>
 int query_occupancy(int) {
     int occ = 0;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attn_sched_kernel<1>, AT, 0) == hipSuccess ? occ : 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attn_sched_kernel<TPW>, AT, 0) == hipSuccess ? occ : 0;
 }
 
-// Resident workgroups of the scheduled launch on the current device: the
-// runtime's occupancy (registers and LDS) times the compute units.
+// Resident workgroups of the scheduled launch (TPW tiles per wave) on the
+// current device: the runtime's occupancy (registers and LDS) times the CUs.
+template <int TPW>
 int resident_workgroups() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    return cached_fact(g_occupancy, dev, query_occupancy) * cached_fact(g_cus, dev, query_cus);
+    return cached_fact(TPW == 1 ? g_occupancy : g_occupancy2, dev, query_occupancy<TPW>) *
+           cached_fact(g_cus, dev, query_cus);
 }
 }  // namespace
 
@@ -893,18 +926,26 @@ hipError_t static_scratch(void **ptr) {
 }
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
-    if (a.rows_wg != 64) return hipErrorInvalidValue;   // the host sizes units for one tile per wave
     const int units = a.B * a.Hkv * a.n_split * a.n_rg;
-    const int resident = (resident_workgroups() / 8) * 8;
-    // the list packs row groups in 8 bits and an item's unit count in 12
-    const bool sched = resident >= 8 && (long long)a.B * a.n_split <= SCHED_ITEMS && a.n_rg < 256 &&
-                       a.Hkv * a.n_rg < 4096;
-    if (sched) {
+    if (a.rows_wg == 128) {
+        // the host chose 128-row units only where the scheduled launch takes the batch
+        const int resident = (resident_workgroups<2>() / 8) * 8;
+        if (resident < 8 || (long long)a.B * a.n_split > SCHED_ITEMS || a.n_rg >= 256 || a.Hkv * a.n_rg >= 4096)
+            return hipErrorInvalidValue;
         attn_reset_kernel<<<dim3(1), dim3(64), 0, stream>>>(a.ws);
-        const int grid = min(resident, xcd_grid(units));
-        attn_sched_kernel<1><<<dim3(grid), dim3(AT), 0, stream>>>(a);
+        attn_sched_kernel<2><<<dim3(min(resident, xcd_grid(units))), dim3(AT), 0, stream>>>(a);
     } else {
-        attn_kernel<1><<<dim3(xcd_grid(units)), dim3(AT), 0, stream>>>(a);
+        if (a.rows_wg != 64) return hipErrorInvalidValue;
+        const int resident = (resident_workgroups<1>() / 8) * 8;
+        // the list packs row groups in 8 bits and an item's unit count in 12
+        const bool sched = resident >= 8 && (long long)a.B * a.n_split <= SCHED_ITEMS && a.n_rg < 256 &&
+                           a.Hkv * a.n_rg < 4096;
+        if (sched) {
+            attn_reset_kernel<<<dim3(1), dim3(64), 0, stream>>>(a.ws);
+            attn_sched_kernel<1><<<dim3(min(resident, xcd_grid(units))), dim3(AT), 0, stream>>>(a);
+        } else {
+            attn_kernel<1><<<dim3(xcd_grid(units)), dim3(AT), 0, stream>>>(a);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;

@@ -13,6 +13,9 @@ constexpr int MAXN = GDN_TREE_MAX_NODES;
 // Attention workspace: scheduling counters first, then the partial records of
 // a split context.
 constexpr int ATTN_WS_HEADER_BYTES = 256;
+// The scheduled attention launch builds its unit list in LDS: at most this
+// many (request, context part) items.
+constexpr int ATTN_SCHED_ITEMS = 1024;
 
 // Plain-old-data argument block shared by every launcher.
 struct Args {

@@ -162,6 +162,14 @@ def test_attention_host_validation_pointers_scale_workspace():
     assert L.gdn_tree_attention(ctypes.byref(d), *good, ctypes.c_float(0.1), *unaligned) == -8
     small = [ok, ok, ok, ctypes.c_size_t(need - 4), None, None]
     assert L.gdn_tree_attention(ctypes.byref(split), *good, ctypes.c_float(0.1), *small) == -8
+    # more than 64 rows per (request, kv head): 128-row units (two tiles per wave)
+    # while the batch's (request, part) items fit the work list, 64-row units past it
+    wide = G.make_attn_dims(4, 32, 8, 64 * 4, 100, 40, 50, split=16)   # 40 nodes x 4 heads = 160 rows
+    assert G.attention_workspace_bytes(wide) == 256 + 4 * 8 * 4 * 2 * 128 * 130 * 4
+    many = G.make_attn_dims(1025, 32, 8, 40 * 1025, 100, 40, 50)      # 1025 one-part items
+    assert G.attention_workspace_bytes(many) == 256
+    many_split = G.make_attn_dims(300, 32, 8, 40 * 300, 100, 40, 50, split=16)   # 1200 items
+    assert G.attention_workspace_bytes(many_split) == 256 + 300 * 8 * 4 * 3 * 64 * 130 * 4
     assert L.gdn_tree_ancestry(None, None, None, None, None, None) == -1
 
 
