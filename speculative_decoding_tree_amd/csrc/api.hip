@@ -52,14 +52,16 @@ bool any_misaligned(Ps... ps) {
 }
 
 // Query rows per attention workgroup.  128 (two 16-row tiles per wave, two
-// workgroups per CU) when a request can have more than 64 query rows per kv
-// head and the scheduled launch takes the batch: a 64-node tree's rows then
-// need two workgroups instead of four, each K and V fragment read from LDS
-// serves 32 rows, and the context is read twice instead of four times (on
-// the batch-256 trees with 1k-4k contexts: the same time, 718-735 vs 719-725
-// us, and 3.08 instead of 3.70 GB fetched).  Otherwise 64 (one tile per wave,
-// three workgroups per CU; the waves of a one- or two-tile unit split the
-// keys instead).  Depends only on the dims, so the workspace size does too.
+// workgroups per CU, blocks staged by direct loads into two LDS buffers) when
+// a request can have more than 64 query rows per kv head and the scheduled
+// launch takes the batch: a 64-node tree's rows then need two workgroups
+// instead of four, each K and V fragment read from LDS serves 32 rows, and
+// the context is read twice instead of four times; units of at most 64 rows
+// still run one tile per wave.  On the batch-256 trees with 1k-4k contexts:
+// 684-693 against 708-715 us for 64-row units on one GPU, and ~3.1 instead of
+// 3.70 GB fetched.  Otherwise 64 (one tile per wave, three workgroups per CU;
+// the waves of a one- or two-tile unit split the keys instead).  Depends only
+// on the dims, so the workspace size does too.
 int attn_rows_wg(const gdn_tree_attn_dims *d, int n_split) {
     const long long G = d->Hq / d->Hkv;
     const long long rows = (long long)d->max_nodes * G;

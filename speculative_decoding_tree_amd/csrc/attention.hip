@@ -90,8 +90,11 @@ __device__ __forceinline__ int v_at(int row, int c) { return row * D + 8 * (c ^ 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane 4a + b receives
-// element b of the 8 bytes addressed by lanes a, 4 + a, 8 + a, 12 + a.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *p) {
+// element b of the 8 bytes addressed by lanes a, 4 + a, 8 + a, 12 + a.  p is
+// restrict (nothing else writes what it reads while the read runs): with that
+// the compiler does not hold the read for direct LDS loads in flight into
+// another buffer, which the callers wait for themselves.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *__restrict__ p) {
     const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) v4i16 *)(p));
     return __builtin_bit_cast(u32x2, r);
@@ -156,19 +159,22 @@ __device__ __forceinline__ int nan_end(const AttnArgs &a, int rg, int R) {
 // (tile, group) taking keys [KB g / KG, KB (g + 1) / KG) of every block; the
 // groups' running (max, sum, O) are merged at the end through LDS.  KG = 1 is
 // the plain layout (one tile per wave, every key); units of one or two tiles
-// use KG = 4 or 2 so that no wave idles.
-template <int TPW, int KG>
+// use KG = 4 or 2 so that no wave idles.  RROWS is the launch's unit size (64
+// or 128 rows): the layout of its partial records, and with 128 the staging
+// by direct loads into two LDS buffers.
+template <int TPW, int KG, int RROWS>
 __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int sp, int rg, int rot, uint16_t *Ks,
-                                          uint16_t *Vs, uint32_t *vnf_all, int lo, int N, int c0, int R, int row0,
-                                          int k0, int k1, int nctx, int nblk);
+                                          uint16_t *Vs, uint16_t *Ks2, uint16_t *Vs2, uint32_t *vnf_all, int lo,
+                                          int N, int c0, int R, int row0, int k0, int k1, int nctx, int nblk);
 
 // One unit: query rows [ROWS rg, ROWS (rg + 1)) of (request b, kv-head hk)
 // against context part sp (and, for part 0, the draft nodes).  Ks / Vs are
-// the workgroup's LDS block and vnf_all its per-thread record of non-finite
-// node values; rot only varies which wave takes which rows.
+// the workgroup's LDS block (Ks2 / Vs2 the second one of 128-row units) and
+// vnf_all its per-thread record of non-finite node values; rot only varies
+// which wave takes which rows.
 template <int TPW>
 __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int sp, int rg, int rot, uint16_t *Ks,
-                                          uint16_t *Vs, uint32_t *vnf_all) {
+                                          uint16_t *Vs, uint16_t *Ks2, uint16_t *Vs2, uint32_t *vnf_all) {
     constexpr int ROWS = 64 * TPW;
     const int tid = threadIdx.x;
 
@@ -190,24 +196,26 @@ __device__ __forceinline__ void attn_unit(const AttnArgs &a, int b, int hk, int 
     const int k1 = min(Lc, k0 + a.split);
     const int nctx = k1 > k0 ? (k1 - k0 + KB - 1) / KB : 0;
     const int nblk = nctx + (sp == 0 ? 1 : 0);   // the draft nodes' own block goes with the first part
+    // A unit with at most 64 rows (every unit of a 64-row launch, and in a
+    // 128-row launch small requests and a request's last row group) runs one
+    // tile per wave, its waves sharing a tile through key groups when it has
+    // one or two; its partial record keeps the launch's row count.
     const int tiles = (min(R - row0, ROWS) + 15) >> 4;
-    if constexpr (TPW == 1) {
-        if (tiles == 1)
-            attn_body<TPW, 4>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
-        else if (tiles == 2)
-            attn_body<TPW, 2>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
-        else
-            attn_body<TPW, 1>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
-    } else {
-        attn_body<TPW, 1>(a, b, hk, sp, rg, rot, Ks, Vs, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
-    }
+    if (tiles == 1)
+        attn_body<1, 4, ROWS>(a, b, hk, sp, rg, rot, Ks, Vs, Ks2, Vs2, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+    else if (tiles == 2)
+        attn_body<1, 2, ROWS>(a, b, hk, sp, rg, rot, Ks, Vs, Ks2, Vs2, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+    else if (TPW == 1 || tiles <= 4)
+        attn_body<1, 1, ROWS>(a, b, hk, sp, rg, rot, Ks, Vs, Ks2, Vs2, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
+    else if constexpr (TPW > 1)
+        attn_body<TPW, 1, ROWS>(a, b, hk, sp, rg, rot, Ks, Vs, Ks2, Vs2, vnf_all, lo, N, c0, R, row0, k0, k1, nctx, nblk);
 }
 
-template <int TPW, int KG>
+template <int TPW, int KG, int RROWS>
 __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int sp, int rg, int rot, uint16_t *Ks,
-                                          uint16_t *Vs, uint32_t *vnf_all, int lo, int N, int c0, int R, int row0,
-                                          int k0, int k1, int nctx, int nblk) {
-    constexpr int ROWS = 64 * TPW;
+                                          uint16_t *Vs, uint16_t *Ks2, uint16_t *Vs2, uint32_t *vnf_all, int lo,
+                                          int N, int c0, int R, int row0, int k0, int k1, int nctx, int nblk) {
+    static_assert(RROWS >= 64 * TPW, "a partial record holds the unit's rows");
     static_assert(KG == 1 || TPW == 1, "key groups split one tile per wave");
     constexpr int NKT = 4 / KG;            // this wave's 16-key tiles per block
     constexpr int NKS = NKT >= 2 ? NKT / 2 : 1;   // its 32-key value steps
@@ -280,7 +288,34 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
     const uint16_t *vctx = a.v_ctx + ((size_t)c0 * a.Hkv + hk) * D;
     const uint16_t *knode = a.k_node + ((size_t)lo * a.Hkv + hk) * D;
     const uint16_t *vnode = a.v_node + ((size_t)lo * a.Hkv + hk) * D;
+    // The 128-row launch (two workgroups per CU) has LDS for two blocks: it
+    // stages by direct global-to-LDS loads into the other buffer while a block
+    // is computed, which frees the staging registers.  One wave instruction
+    // fills four rows (lane l: row 4 j + l / 16, LDS chunk l % 16, written at
+    // the row's base + 16 l); the lane loads the global chunk that the swizzle
+    // puts there.  The 64-row launches stage through registers.
+    constexpr bool DMA = RROWS == 128;
     u32x4 kst[4], vst[4];
+    auto issue_block = [&](int blk, uint16_t *Kd, uint16_t *Vd) {
+        const bool nodeb = blk >= nctx;
+        const int last = nodeb ? N - 1 : k1 - 1;
+        const int first = nodeb ? 0 : k0 + KB * blk;
+        const uint16_t *kb = nodeb ? knode : kctx;
+        const uint16_t *vb = nodeb ? vnode : vctx;
+        const int lane16 = tid & 15;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = w + 4 * i;          // rows 4 j .. 4 j + 3
+            const int r = 4 * j + ((tid & 63) >> 4);
+            const uint32_t roff = (uint32_t)min(first + r, last) * kvrow;
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const u32x4 *>(kb + roff) + (lane16 ^ (r & 15)),
+                (__attribute__((address_space(3))) void *)&Kd[4 * j * D], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const u32x4 *>(vb + roff) + (lane16 ^ ((r & 7) << 1)),
+                (__attribute__((address_space(3))) void *)&Vd[4 * j * D], 16, 0, 0);
+        }
+    };
     auto load_block = [&](int blk) {
         const bool nodeb = blk >= nctx;
         // key rows past the end read the last real row; their scores are masked
@@ -324,26 +359,56 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
     // any was (rare), each output column whose visible nodes include one that
     // carried a non-finite value in that column is set to NaN at the end.
     // Finite values: the same products as without the check.
-    load_block(0);
-    for (int blk = 0; blk < nblk; ++blk) {
-        if (blk > 0) lds_barrier();   // every wave is done with the previous block
-        if (blk >= nctx) {   // the draft nodes' block (the last one; workgroup-uniform)
-            uint32_t vnf = 0;
+    // zero the non-finite halves of v (chunk q of this thread's rows) and
+    // record them in vnf
+    auto scrub = [&](u32x4 &v, int q, uint32_t &vnf) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t w = vst[q][e];
-                    const bool blo = (w & 0x7f80u) == 0x7f80u, bhi = (w & 0x7f800000u) == 0x7f800000u;
-                    vnf |= (blo ? 1u : 0u) << (8 * q + 2 * e);
-                    vnf |= (bhi ? 1u : 0u) << (8 * q + 2 * e + 1);
-                    vst[q][e] = w & (blo ? 0xffff0000u : 0xffffffffu) & (bhi ? 0x0000ffffu : 0xffffffffu);
-                }
-            vnf_all[tid] = vnf;
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t x = v[e];
+            const bool blo = (x & 0x7f80u) == 0x7f80u, bhi = (x & 0x7f800000u) == 0x7f800000u;
+            vnf |= (blo ? 1u : 0u) << (8 * q + 2 * e);
+            vnf |= (bhi ? 1u : 0u) << (8 * q + 2 * e + 1);
+            v[e] = x & (blo ? 0xffff0000u : 0xffffffffu) & (bhi ? 0x0000ffffu : 0xffffffffu);
         }
-        store_block();
-        lds_barrier();
-        if (blk + 1 < nblk) load_block(blk + 1);
+    };
+    if constexpr (DMA) issue_block(0, Ks, Vs);
+    else load_block(0);
+    for (int blk = 0; blk < nblk; ++blk) {
+        // With direct loads the two buffers are separate LDS arrays chosen by
+        // the block's parity (even blocks in Ks / Vs, odd ones in Ks2 / Vs2),
+        // so that the compiler can tell this block's reads from the next
+        // block's loads and does not wait for those loads before them (the
+        // wait at the top of the next block covers them).
+        const bool odd = DMA && (blk & 1);
+        uint16_t *Kb = odd ? Ks2 : Ks, *Vb = odd ? Vs2 : Vs;
+        if constexpr (DMA) {
+            __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads of the block have landed
+            lds_barrier();                   // everyone's have, and every wave is done with the other buffer
+            if (blk >= nctx) {   // the draft nodes' block (the last one; workgroup-uniform): scrub in LDS
+                uint32_t vnf = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    u32x4 *p = reinterpret_cast<u32x4 *>(&Vb[v_at(16 * q + srow, cch)]);
+                    u32x4 v = *p;
+                    scrub(v, q, vnf);
+                    *p = v;
+                }
+                vnf_all[tid] = vnf;
+                lds_barrier();
+            }
+            if (blk + 1 < nblk) issue_block(blk + 1, odd ? Ks : Ks2, odd ? Vs : Vs2);
+        } else {
+            if (blk > 0) lds_barrier();   // every wave is done with the previous block
+            if (blk >= nctx) {   // the draft nodes' block (the last one; workgroup-uniform)
+                uint32_t vnf = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) scrub(vst[q], q, vnf);
+                vnf_all[tid] = vnf;
+            }
+            store_block();
+            lds_barrier();
+            if (blk + 1 < nblk) load_block(blk + 1);
+        }
         if (!active) continue;
         const bool nodeb = blk >= nctx;
         const int rem = k1 - (k0 + KB * blk);   // context keys left from this block on
@@ -361,7 +426,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
         constexpr int KPF = 2;
         u32x4 kf[KPF];
         auto kload = [&](int j) {   // row 16 (kt_lo + kt) + n, chunk 4 s + grp
-            kf[j % KPF] = *reinterpret_cast<const u32x4 *>(&Ks[k_at(16 * (kt_lo + (j >> 2)) + n, 4 * (j & 3) + grp)]);
+            kf[j % KPF] = *reinterpret_cast<const u32x4 *>(&Kb[k_at(16 * (kt_lo + (j >> 2)) + n, 4 * (j & 3) + grp)]);
         };
 #pragma unroll
         for (int j = 0; j < KPF; ++j) kload(j);
@@ -455,8 +520,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
             const int ks = (kt_lo >> 1) + (j >> 3), mt = j & 7;
             const int c = 2 * mt + ((n & 3) >> 1);
             const int r0 = 32 * ks + 4 * grp + (n >> 2);
-            const u32x2 va = lds_read_tr16(&Vs[v_at(r0, c) + vsub]);
-            const u32x2 vb = lds_read_tr16(&Vs[v_at(r0 + 16, c) + vsub]);
+            const u32x2 va = lds_read_tr16(&Vb[v_at(r0, c) + vsub]);
+            const u32x2 vb = lds_read_tr16(&Vb[v_at(r0 + 16, c) + vsub]);
             vf[j % PF] = u32x4{va.x, va.y, vb.x, vb.y};
         };
 #pragma unroll
@@ -568,15 +633,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
             if (grp == 0 && a.lse) a.lse[orow] = (m[tt] + log2f(l[tt])) * LN2;
         } else {
             float *rec = a.ws + ATTN_WS_HEADER_BYTES / 4 +
-                         ((((size_t)b * a.Hkv + hk) * a.n_split + sp) * a.n_rg + rg) * part_floats(ROWS);
+                         ((((size_t)b * a.Hkv + hk) * a.n_split + sp) * a.n_rg + rg) * part_floats(RROWS);
             const int rl = 16 * (TPW * wr + tt) + n;
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
                 *reinterpret_cast<float4 *>(rec + rl * D + 16 * mt + 4 * grp) =
                     make_float4(ot[tt][mt][0], ot[tt][mt][1], ot[tt][mt][2], ot[tt][mt][3]);
             if (grp == 0) {
-                rec[ROWS * D + rl] = m[tt];
-                rec[ROWS * D + ROWS + rl] = l[tt];
+                rec[RROWS * D + rl] = m[tt];
+                rec[RROWS * D + RROWS + rl] = l[tt];
             }
         }
     }
@@ -596,7 +661,7 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3
     int rest = unit / a.n_rg;
     const int sp = rest % a.n_split;
     rest /= a.n_split;
-    attn_unit<TPW>(a, rest / a.Hkv, rest % a.Hkv, sp, rg, unit, Ks, Vs, vnf_all);
+    attn_unit<TPW>(a, rest / a.Hkv, rest % a.Hkv, sp, rg, unit, Ks, Vs, Ks, Vs, vnf_all);
 }
 
 // ---- scheduled launch: a resident grid working through a sorted unit list ----
@@ -717,6 +782,9 @@ template <int TPW>
 __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3 : 2))) void attn_sched_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * D];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[KB * D];
+    // 128-row units stage two blocks (direct loads into one while the other is computed)
+    __shared__ __attribute__((aligned(16))) uint16_t Ks2[TPW == 2 ? KB * D : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs2[TPW == 2 ? KB * D : 8];
     __shared__ __attribute__((aligned(16))) uint32_t vnf_all[AT];   // non-finite node values, per thread
     __shared__ AttnSched sc;
     if ((threadIdx.x >> 6) == 0) build_sched(a, sc);
@@ -740,7 +808,7 @@ __global__ __launch_bounds__(AT) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 3
         const int it = sc.item[lo] & 0xffff, nrg = sc.item[lo] >> 16, j = k - sc.first[lo];
         const int b = it / a.n_split, sp = it - b * a.n_split;
         const int hk = nrg > 0 ? j / nrg : 0, rg = nrg > 0 ? j - hk * nrg : 0;
-        attn_unit<TPW>(a, b, hk, sp, rg, k, Ks, Vs, vnf_all);
+        attn_unit<TPW>(a, b, hk, sp, rg, k, Ks, Vs, Ks2, Vs2, vnf_all);
         lds_barrier();   // every wave is done with the LDS block (and the ticket) before the next unit
     }
 }
