@@ -213,6 +213,26 @@ def test_attention_scheduled_and_per_unit_launches_agree():
     compare(wl, o2, l2, ref_out, ref_lse, range(wl.B))
 
 
+@pytest.mark.parametrize("split", [None, 64])
+def test_attention_128_row_units_match_64_row_units(split):
+    # trees of at most 16 nodes at 4 query heads per kv head: max_nodes = 16 gives
+    # 64-row units staged through registers; max_nodes = 64 gives 128-row units
+    # staged by direct loads into two LDS buffers, whose units of <= 64 rows run
+    # the same one-tile products, so the outputs must agree bit for bit
+    rng = np.random.default_rng(41)
+    parents = [W.chain(3), W.root_branch(), W.random_tree(rng, 16), np.array([-1, -1, 0], np.int32),
+               W.random_tree(rng, 9), W.chain(16), np.zeros(0, np.int32), W.random_tree(rng, 12)]
+    wl = W.make_attn(parents, [0, 1, 63, 64, 65, 200, 7, 517], Hq=8, Hkv=2, seed=41, name="attn_rows")
+    o64, l64, s64, _ = run_attn(wl, split=split, max_nodes=16)
+    o128, l128, s128, _ = run_attn(wl, split=split, max_nodes=64)
+    ref_out, ref_lse, ref_st = oracle_attn(wl, max_nodes=16)
+    assert np.array_equal(s64, ref_st) and np.array_equal(s128, ref_st)
+    rows = rows_of(wl, range(wl.B))
+    assert np.array_equal(o64[rows].view(np.uint32), o128[rows].view(np.uint32))
+    assert np.array_equal(l64[rows].view(np.uint32), l128[rows].view(np.uint32))
+    compare(wl, o128, l128, ref_out, ref_lse, range(wl.B))
+
+
 def test_attention_deterministic():
     wl = W.make_attn_small(5)
     o1, l1, _, d = run_attn(wl, split=64)
