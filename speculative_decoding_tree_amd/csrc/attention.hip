@@ -229,6 +229,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
     const int wr = KG > 1 ? w / KG : (w - rot) & 3;
     const int kg = KG > 1 ? w % KG : 0;   // key group
     const int kt_lo = kg * NKT;            // first 16-key tile of the block this wave takes
+    // A wave computes its second tile even when the tile has no valid row (a
+    // unit's last wave): its rows are never written, and the products stay
+    // free of branches, which lets the compiler interleave them.
     int t[TPW], g[TPW];
     bool rvalid[TPW], tact[TPW];   // tact: the tile has a valid row (wave-uniform)
     uint64_t anc_row[TPW];
@@ -296,24 +299,31 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
     // puts there.  The 64-row launches stage through registers.
     constexpr bool DMA = RROWS == 128;
     u32x4 kst[4], vst[4];
+    // Wave w fills rows 4 j .. 4 j + 3, j = w + 4 i (i = 0..3); lane l takes row
+    // r = 16 i + r0, r0 = 4 w + l % 64 / 16.  r % 16 = r0 % 16 for every i, so
+    // the swizzled chunk (byte offset ck for K, cv for V) is fixed per lane.
+    const int r0 = 4 * w + ((tid & 63) >> 4);
+    const uint32_t ck = 16u * (uint32_t)((tid & 15) ^ (r0 & 15));
+    const uint32_t cv = 16u * (uint32_t)((tid & 15) ^ ((r0 & 7) << 1));
+    const uint32_t rowb = 2u * kvrow;   // bytes between consecutive rows of one kv head
     auto issue_block = [&](int blk, uint16_t *Kd, uint16_t *Vd) {
         const bool nodeb = blk >= nctx;
         const int last = nodeb ? N - 1 : k1 - 1;
         const int first = nodeb ? 0 : k0 + KB * blk;
-        const uint16_t *kb = nodeb ? knode : kctx;
-        const uint16_t *vb = nodeb ? vnode : vctx;
-        const int lane16 = tid & 15;
+        const char *kb = reinterpret_cast<const char *>(nodeb ? knode : kctx);
+        const char *vb = reinterpret_cast<const char *>(nodeb ? vnode : vctx);
+        const bool whole = first + KB - 1 <= last;   // no row past the end (workgroup-uniform)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int j = w + 4 * i;          // rows 4 j .. 4 j + 3
-            const int r = 4 * j + ((tid & 63) >> 4);
-            const uint32_t roff = (uint32_t)min(first + r, last) * kvrow;
-            __builtin_amdgcn_global_load_lds(
-                reinterpret_cast<const u32x4 *>(kb + roff) + (lane16 ^ (r & 15)),
-                (__attribute__((address_space(3))) void *)&Kd[4 * j * D], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(
-                reinterpret_cast<const u32x4 *>(vb + roff) + (lane16 ^ ((r & 7) << 1)),
-                (__attribute__((address_space(3))) void *)&Vd[4 * j * D], 16, 0, 0);
+            const int j = w + 4 * i;
+            // 32-bit byte offsets from a uniform base (a request's rows stay below
+            // 2^30 elements per array, checked on the host)
+            const uint32_t ro = whole ? (uint32_t)(first + r0) * rowb + (uint32_t)(16 * i) * rowb
+                                      : (uint32_t)min(first + 16 * i + r0, last) * rowb;
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4 *>(kb + (ro + ck)),
+                                             (__attribute__((address_space(3))) void *)&Kd[4 * j * D], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4 *>(vb + (ro + cv)),
+                                             (__attribute__((address_space(3))) void *)&Vd[4 * j * D], 16, 0, 0);
         }
     };
     auto load_block = [&](int blk) {
@@ -436,7 +446,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
             if (j + KPF < 4 * NKT) kload(j + KPF);
 #pragma unroll
             for (int tt = 0; tt < TPW; ++tt)
-                if (tt == 0 || tact[tt]) sc[tt][j >> 2] = mfma(k, qf[tt][j & 3], sc[tt][j >> 2]);
+                sc[tt][j >> 2] = mfma(k, qf[tt][j & 3], sc[tt][j >> 2]);
         }
 
         // softmax per tile; P in bf16 hi + lo as the B operand of the value product
@@ -531,11 +541,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
             const u32x4 v = vf[j % PF];
             if (j + PF < 8 * NKS) vload(j + PF);
 #pragma unroll
-            for (int tt = 0; tt < TPW; ++tt)
-                if (tt == 0 || tact[tt]) {
-                    ot[tt][j & 7] = mfma(v, phi[tt][j >> 3], ot[tt][j & 7]);
-                    ot[tt][j & 7] = mfma(v, plo[tt][j >> 3], ot[tt][j & 7]);
-                }
+            for (int tt = 0; tt < TPW; ++tt) {
+                ot[tt][j & 7] = mfma(v, phi[tt][j >> 3], ot[tt][j & 7]);
+                ot[tt][j & 7] = mfma(v, plo[tt][j >> 3], ot[tt][j & 7]);
+            }
         }
     }
     // did any staged node value turn out non-finite? (vnf words of all threads,
