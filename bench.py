@@ -375,7 +375,7 @@ def attention_row(args, stream):
     out1 = torch.empty((w1.T, w1.Hq, D), dtype=torch.float32, device=dev)
     lse1 = torch.empty((w1.T, w1.Hq), dtype=torch.float32, device=dev)
     b1 = {"workload": "1 request, 6-node root-branch tree, 4096-token context, Hq=32, Hkv=8, d=128"}
-    for split in (None, 1024, 256):
+    for split in (None, 1024, 256, 0):
         ws_need = G.attention_workspace_bytes(G.make_attn_dims(1, w1.Hq, w1.Hkv, w1.T, w1.C, w1.max_nodes, w1.C,
                                                                 split))
         ws = torch.empty((max(ws_need, 16),), dtype=torch.uint8, device=dev)
@@ -383,7 +383,8 @@ def attention_row(args, stream):
         def run1(i, split=split, ws=ws):
             G.attention(q1, kc1, vc1, co1, kn1, vn1, no1, anc1, w1.scale, max_nodes=w1.max_nodes, max_ctx=w1.C,
                         split=split, out=out1, lse=lse1, workspace=ws, status=st1, stream=stream)
-        b1["one_pass_us" if split is None else f"split_{split}_us"] = _time_launches(run1, n, stream)
+        key = "one_pass_us" if split is None else ("split_chosen_us" if split == 0 else f"split_{split}_us")
+        b1[key] = _time_launches(run1, n, stream)
     assert (st1.cpu().numpy() == 0).all()
     res["batch_one"] = b1
     return res

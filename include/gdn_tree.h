@@ -341,7 +341,11 @@ typedef struct gdn_tree_attn_dims {
     int32_t C;         /* total committed-context rows = ctx_offset[B] (>= 0) */
     int32_t max_nodes; /* per-request node cap (1..64) */
     int32_t max_ctx;   /* per-request context cap (0 .. 2^30) */
-    int32_t split;     /* context keys per workgroup (>= 1); split >= max_ctx = one pass, no merge */
+    int32_t split;     /* context keys per workgroup; split >= max_ctx = one pass, no merge;
+                          0 = chosen by the library from these dims: one pass when B * Hkv * row groups
+                          of 64 reaches 1024 or max_ctx <= 512, else parts of a multiple of 64 keys
+                          (>= 256) enough to bring the units to 1024 (16 parts of 256 keys for one
+                          request with a 4096-token context and 8 kv heads) */
 } gdn_tree_attn_dims;
 
 /*

@@ -123,7 +123,7 @@ ATTN_NULLS = [None] * 8 + [ctypes.c_float(0.1), None, None, None, ctypes.c_size_
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("Hq", 0, -2), ("Hkv", 3, -2), ("T", -1, -2), ("C", -1, -2), ("B", -1, -2), ("split", 0, -2),
+    ("Hq", 0, -2), ("Hkv", 3, -2), ("T", -1, -2), ("C", -1, -2), ("B", -1, -2), ("split", -1, -2),
     ("max_ctx", -1, -2), ("max_ctx", (1 << 30) + 1, -2), ("head_dim", 64, -3), ("max_nodes", 0, -4),
     ("max_nodes", 65, -4),
 ])
@@ -170,6 +170,22 @@ def test_attention_host_validation_pointers_scale_workspace():
     assert G.attention_workspace_bytes(many) == 256
     many_split = G.make_attn_dims(300, 32, 8, 40 * 300, 100, 40, 50, split=16)   # 1200 items
     assert G.attention_workspace_bytes(many_split) == 256 + 300 * 8 * 4 * 3 * 64 * 130 * 4
+
+
+def test_attention_split_chosen_by_the_library():
+    ws = lambda *a, **k: G.attention_workspace_bytes(G.make_attn_dims(*a, **k))
+    # one request, 8 kv heads, a 4096-token context: 16 parts of 256 keys
+    assert ws(1, 32, 8, 6, 4096, 6, 4096, split=0) == ws(1, 32, 8, 6, 4096, 6, 4096, split=256)
+    assert ws(1, 32, 8, 6, 4096, 6, 4096, split=256) == 256 + 1 * 8 * 16 * 1 * 64 * 130 * 4
+    # 16 requests: 128 one-pass units, 8 parts of 512 keys
+    assert ws(16, 32, 8, 96, 65536, 6, 4096, split=0) == ws(16, 32, 8, 96, 65536, 6, 4096, split=512)
+    # a batch that fills the chip, or short contexts: one pass (counters only)
+    assert ws(256, 32, 8, 5696, 1 << 20, 64, 4096, split=0) == 256
+    assert ws(2, 32, 8, 12, 1000, 6, 500, split=0) == 256
+    # an odd context length: parts rounded up to a multiple of 64 keys (ceil(1000 / 4) -> 256)
+    assert ws(1, 32, 8, 6, 1000, 6, 1000, split=0) == ws(1, 32, 8, 6, 1000, 6, 1000, split=256)
+    L = G.lib()
+    assert L.gdn_tree_attention_workspace_bytes(ctypes.byref(G.make_attn_dims(1, 32, 8, 6, 100, 6, 100, split=-1))) == 0
     assert L.gdn_tree_ancestry(None, None, None, None, None, None) == -1
 
 

@@ -233,6 +233,23 @@ def test_attention_128_row_units_match_64_row_units(split):
     compare(wl, o128, l128, ref_out, ref_lse, range(wl.B))
 
 
+def test_attention_split_chosen_by_the_library():
+    # one request, 8 kv heads, a 4096-token context: split = 0 takes 16 parts of 256 keys
+    wl = W.make_attn([W.root_branch()], [4096], Hq=32, Hkv=8, seed=5, name="attn_b1")
+    o0, l0, s0, _ = run_attn(wl, split=0)
+    o1, l1, s1, _ = run_attn(wl, split=256)
+    assert np.array_equal(o0.view(np.uint32), o1.view(np.uint32)) and np.array_equal(l0.view(np.uint32), l1.view(np.uint32))
+    ref_out, ref_lse, ref_st = oracle_attn(wl)
+    assert np.array_equal(s0, ref_st)
+    compare(wl, o0, l0, ref_out, ref_lse, range(wl.B))
+    # contexts of at most 512 keys: one pass
+    wl = W.make_attn_small(6)
+    o0, l0, s0, _ = run_attn(wl, split=0)
+    o1, l1, s1, _ = run_attn(wl)
+    rows = rows_of(wl, range(wl.B))
+    assert np.array_equal(o0[rows].view(np.uint32), o1[rows].view(np.uint32)) and np.array_equal(s0, s1)
+
+
 def test_attention_deterministic():
     wl = W.make_attn_small(5)
     o1, l1, _, d = run_attn(wl, split=64)
