@@ -285,7 +285,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
     //      of K and of V, q = 0..3. ----
     const int cch = tid & 15, srow = tid >> 4;
     // per-request bases are workgroup-uniform; lanes add 32-bit element offsets
-    // (a request's context is below 2^30 elements per array, checked on the host)
+    // (a request's context is below 2^31 elements per array, checked on the host)
     const uint32_t kvrow = (uint32_t)a.Hkv * D;
     const uint16_t *kctx = a.k_ctx + ((size_t)c0 * a.Hkv + hk) * D;
     const uint16_t *vctx = a.v_ctx + ((size_t)c0 * a.Hkv + hk) * D;
@@ -317,7 +317,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs &a, int b, int hk, int 
         for (int i = 0; i < 4; ++i) {
             const int j = w + 4 * i;
             // 32-bit byte offsets from a uniform base (a request's rows stay below
-            // 2^30 elements per array, checked on the host)
+            // 2^31 elements, so 2^32 bytes, per array: checked on the host)
             const uint32_t ro = whole ? (uint32_t)(first + r0) * rowb + (uint32_t)(16 * i) * rowb
                                       : (uint32_t)min(first + 16 * i + r0, last) * rowb;
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4 *>(kb + (ro + ck)),
