@@ -9,10 +9,11 @@
 // root-to-node path attends to.
 //
 // gfx950 layout.  A workgroup (4 wave64) owns 64 query rows of one
-// (request, kv-head): row r = (node r / G, query head hk G + r % G), so the
-// G query heads of a node sit in neighbouring rows and every row of the
-// workgroup shares the same keys.  Each group of 16 rows is owned by one
-// wave.  Keys go through LDS 64 at a time, K and V rows as they are in
+// (request, kv-head), or 128 (two 16-row tiles per wave) when a request can
+// have more than 64 rows per kv head: row r = (node r / G, query head
+// hk G + r % G), so the G query heads of a node sit in neighbouring rows and
+// every row of the workgroup shares the same keys.  Each group of 16 rows is
+// owned by one wave.  Keys go through LDS 64 at a time, K and V rows as they are in
 // memory, their 16-byte chunks permuted per row (XOR) so that fragment reads
 // hit distinct banks.  Per block and wave:
 //   S^T = K Q^T          (v_mfma_f32_16x16x32_bf16; A = K rows from LDS,
@@ -26,8 +27,9 @@
 // with P split into bf16 hi + lo (two MFMAs, ~16 mantissa bits), so no
 // register moves between lanes.  Blocks wholly inside the context skip the
 // mask; a row's running max only moves when a block raises it by more than
-// 2^8, so most blocks need no cross-lane reduction.  Global loads of the next
-// block are issued before the current block is computed.
+// 2^8, so most blocks need no cross-lane reduction.  Loads of the next block
+// are issued before the current block is computed (into registers with
+// 64-row units, straight into a second LDS buffer with 128-row units).
 //
 // When a request's context is split over several workgroups, each writes an
 // unnormalised partial (O, running max, sum) to the workspace and a second
