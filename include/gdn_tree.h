@@ -343,9 +343,10 @@ typedef struct gdn_tree_attn_dims {
     int32_t max_ctx;   /* per-request context cap (0 .. 2^30) */
     int32_t split;     /* context keys per workgroup; split >= max_ctx = one pass, no merge;
                           0 = chosen by the library from these dims: one pass when B * Hkv * row groups
-                          of 64 reaches 1024 or max_ctx <= 512, else parts of a multiple of 64 keys
-                          (>= 256) enough to bring the units to 1024 (16 parts of 256 keys for one
-                          request with a 4096-token context and 8 kv heads) */
+                          of 64 reaches 512, else min(ceil(512 / those units), 32, ceil(max_ctx / 64))
+                          parts, each ceil(max_ctx / parts) rounded up to a multiple of 64 keys (one
+                          pass if that is a single part); one request with a 4096-token context and
+                          8 kv heads: 32 parts of 128 keys */
 } gdn_tree_attn_dims;
 
 /*

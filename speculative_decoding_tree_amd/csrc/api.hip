@@ -74,22 +74,25 @@ int attn_rows_wg(const gdn_tree_attn_dims *d, int n_split) {
 
 // split = 0: the context part size, chosen from the dims alone.  One pass
 // when the batch's one-pass units (64-row count) already number
-// ATTN_AUTO_UNITS (enough to fill the chip several times over) or the
-// contexts are short; otherwise parts of a multiple of 64 keys, at least 256,
-// as many as bring the units to ATTN_AUTO_UNITS.  At batch one with a
-// 4096-token context that is 16 parts of 256 keys: 58.4-59.0 us against
-// 506-512 us in one pass.
-constexpr long long ATTN_AUTO_UNITS = 1024;
+// ATTN_AUTO_UNITS; otherwise as many parts as bring the units to that count,
+// at most ATTN_AUTO_PARTS (the merge reads every part of a row) and at least
+// 64 keys each, rounded up to a multiple of 64 keys.  Measured on one GPU
+// (one root-branch tree per request, 8 kv heads): one request with a 4096-key
+// context takes 32 parts of 128 keys, 52.0 us (256-key parts 58.6, 64-key
+// parts 73.5, one pass 507.8); with 16384 keys 32 parts of 512, 65.2 us (256:
+// 81.0); four requests 16 parts of 256, 46.2 us; sixteen requests 4 parts of
+// 1024, 64.1 us (512: 74.8).  Each was the fastest of the sizes tried.
+constexpr long long ATTN_AUTO_UNITS = 512, ATTN_AUTO_PARTS = 32;
 int attn_split(const gdn_tree_attn_dims *d) {
     if (d->split > 0) return d->split;
     const int one = d->max_ctx > 1 ? d->max_ctx : 1;
     const long long rows = (long long)d->max_nodes * (d->Hq / d->Hkv);
     const long long units1 = (long long)d->B * d->Hkv * ((rows + 63) / 64);
-    if (units1 >= ATTN_AUTO_UNITS || d->max_ctx <= 512) return one;
-    long long parts = (ATTN_AUTO_UNITS + units1 - 1) / units1;
-    parts = std::min(parts, ((long long)d->max_ctx + 255) / 256);
-    const long long keys = ((d->max_ctx + parts - 1) / parts + 63) / 64 * 64;
-    return (int)std::max(keys, 256ll);
+    if (units1 >= ATTN_AUTO_UNITS) return one;
+    const long long parts = std::min({(ATTN_AUTO_UNITS + units1 - 1) / units1, ATTN_AUTO_PARTS,
+                                      ((long long)d->max_ctx + 63) / 64});
+    if (parts <= 1) return one;
+    return (int)(((d->max_ctx + parts - 1) / parts + 63) / 64 * 64);
 }
 
 // Attention dims; also derives the launch shape (the context part size too).

@@ -174,16 +174,19 @@ def test_attention_host_validation_pointers_scale_workspace():
 
 def test_attention_split_chosen_by_the_library():
     ws = lambda *a, **k: G.attention_workspace_bytes(G.make_attn_dims(*a, **k))
-    # one request, 8 kv heads, a 4096-token context: 16 parts of 256 keys
-    assert ws(1, 32, 8, 6, 4096, 6, 4096, split=0) == ws(1, 32, 8, 6, 4096, 6, 4096, split=256)
-    assert ws(1, 32, 8, 6, 4096, 6, 4096, split=256) == 256 + 1 * 8 * 16 * 1 * 64 * 130 * 4
-    # 16 requests: 128 one-pass units, 8 parts of 512 keys
-    assert ws(16, 32, 8, 96, 65536, 6, 4096, split=0) == ws(16, 32, 8, 96, 65536, 6, 4096, split=512)
-    # a batch that fills the chip, or short contexts: one pass (counters only)
+    # one request, 8 kv heads (8 one-pass units), a 4096-token context: 32 parts of 128 keys
+    assert ws(1, 32, 8, 6, 4096, 6, 4096, split=0) == ws(1, 32, 8, 6, 4096, 6, 4096, split=128)
+    assert ws(1, 32, 8, 6, 4096, 6, 4096, split=128) == 256 + 1 * 8 * 32 * 1 * 64 * 130 * 4
+    # 16384 tokens: still 32 parts, of 512 keys
+    assert ws(1, 32, 8, 6, 16384, 6, 16384, split=0) == ws(1, 32, 8, 6, 16384, 6, 16384, split=512)
+    # 4 requests (32 units): 16 parts of 256 keys; 16 requests (128 units): 4 parts of 1024 keys
+    assert ws(4, 32, 8, 24, 16384, 6, 4096, split=0) == ws(4, 32, 8, 24, 16384, 6, 4096, split=256)
+    assert ws(16, 32, 8, 96, 65536, 6, 4096, split=0) == ws(16, 32, 8, 96, 65536, 6, 4096, split=1024)
+    # a batch that fills the chip, or a context of at most 64 keys: one pass (counters only)
     assert ws(256, 32, 8, 5696, 1 << 20, 64, 4096, split=0) == 256
-    assert ws(2, 32, 8, 12, 1000, 6, 500, split=0) == 256
-    # an odd context length: parts rounded up to a multiple of 64 keys (ceil(1000 / 4) -> 256)
-    assert ws(1, 32, 8, 6, 1000, 6, 1000, split=0) == ws(1, 32, 8, 6, 1000, 6, 1000, split=256)
+    assert ws(2, 32, 8, 12, 100, 6, 64, split=0) == 256
+    # an odd length: ceil(1000 / 16) = 63 keys, rounded up to 64 (16 parts)
+    assert ws(1, 32, 8, 6, 1000, 6, 1000, split=0) == ws(1, 32, 8, 6, 1000, 6, 1000, split=64)
     L = G.lib()
     assert L.gdn_tree_attention_workspace_bytes(ctypes.byref(G.make_attn_dims(1, 32, 8, 6, 100, 6, 100, split=-1))) == 0
     assert L.gdn_tree_ancestry(None, None, None, None, None, None) == -1

@@ -234,18 +234,19 @@ def test_attention_128_row_units_match_64_row_units(split):
 
 
 def test_attention_split_chosen_by_the_library():
-    # one request, 8 kv heads, a 4096-token context: split = 0 takes 16 parts of 256 keys
+    # one request, 8 kv heads, a 4096-token context: split = 0 takes 32 parts of 128 keys
     wl = W.make_attn([W.root_branch()], [4096], Hq=32, Hkv=8, seed=5, name="attn_b1")
     o0, l0, s0, _ = run_attn(wl, split=0)
-    o1, l1, s1, _ = run_attn(wl, split=256)
+    o1, l1, s1, _ = run_attn(wl, split=128)
     assert np.array_equal(o0.view(np.uint32), o1.view(np.uint32)) and np.array_equal(l0.view(np.uint32), l1.view(np.uint32))
     ref_out, ref_lse, ref_st = oracle_attn(wl)
     assert np.array_equal(s0, ref_st)
     compare(wl, o0, l0, ref_out, ref_lse, range(wl.B))
-    # contexts of at most 512 keys: one pass
+    # the edge mix (8 requests, 2 kv heads, 4 row groups of 64: 64 units, contexts up to 200
+    # keys): min(8, 32, 4) = 4 parts of 64 keys
     wl = W.make_attn_small(6)
     o0, l0, s0, _ = run_attn(wl, split=0)
-    o1, l1, s1, _ = run_attn(wl)
+    o1, l1, s1, _ = run_attn(wl, split=64)
     rows = rows_of(wl, range(wl.B))
     assert np.array_equal(o0[rows].view(np.uint32), o1[rows].view(np.uint32)) and np.array_equal(s0, s1)
 
