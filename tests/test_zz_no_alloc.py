@@ -49,7 +49,7 @@ def _smaller(wl, reqs):
     return W.make_attn(parents, ctx, Hq=wl.Hq, Hkv=wl.Hkv, seed=77, name="attn_smaller")
 
 
-@pytest.mark.parametrize("split", [None, 64])
+@pytest.mark.parametrize("split", [None, 64, 0])
 def test_attention_static_equals_workspace_entry_point(split):
     big = W.make_attn_small(4)
     small = _smaller(big, [5, 1, 2])
